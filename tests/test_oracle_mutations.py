@@ -1,0 +1,136 @@
+"""Plant plausible mistakes in the CPU oracle and check that the pins catch each one.
+
+Every mutation is a small edit of one oracle step (a sign, an index, a dropped term, a transposed
+operand, a wrong order of two steps). The pins in test_oracle_pins.py must fail for every one of them;
+otherwise a pin is missing. CPU only; the mutations live only inside this test.
+"""
+import numpy as np
+import pytest
+
+from oracle import gptq_oracle as O
+import tests.test_oracle_pins as P
+
+
+def _loop_factory(kind):
+    def loop(W0, U, bits, group=0):
+        qmax = O.qmax_for(bits)
+        W = np.array(W0, dtype=np.float64, copy=True)
+        out, d = W.shape
+        n_groups = -(-d // group) if group else 1
+        codes = np.zeros((out, d), dtype=np.int64)
+        scales = np.zeros((out, n_groups))
+        errs = np.zeros((out, d))
+        scale = O.row_scales(W, qmax)
+        orig = W.copy()
+        if not group:
+            scales[:, 0] = scale
+        for j in range(d):
+            if group and j % group == 0:
+                src = orig if kind == "group_from_original" else W
+                scale = O.row_scales(src[:, j:j + group], qmax)
+                scales[:, j // group] = scale
+            w = W[:, j]
+            c = np.clip(np.round(w / scale), -qmax, qmax)
+            if kind == "floor_not_round":
+                c = np.clip(np.floor(w / scale), -qmax, qmax)
+            q = c * scale
+            e = (w - q) / U[j, j]
+            if kind == "no_divide":
+                e = w - q
+            if kind == "unclipped_error":
+                e = (w - np.round(w / scale) * scale) / U[j, j]
+            codes[:, j] = c.astype(np.int64)
+            errs[:, j] = e
+            if j + 1 < d:
+                if kind == "sign":
+                    W[:, j + 1:] += np.outer(e, U[j, j + 1:])
+                elif kind == "transposed_u":
+                    W[:, j + 1:] -= np.outer(e, U[j + 1:, j])
+                elif kind == "off_by_one":
+                    W[:, j + 1:] -= np.outer(e, U[j, j:-1])
+                else:
+                    W[:, j + 1:] -= np.outer(e, U[j, j + 1:])
+        loss = np.einsum("rj,rj->r", errs, errs)
+        return codes, scales, errs, loss
+    return loop
+
+
+def _prepare_factory(kind):
+    def prepare(S, colsq, n, damp, act_order):
+        d = S.shape[0]
+        H = (2.0 / n) * S if kind != "no_two" else (1.0 / n) * S
+        H = 0.5 * (H + H.T)
+        dead = colsq == 0.0
+        idx = np.flatnonzero(dead)
+        if kind == "damp_before_dead":
+            lam = damp * np.mean(np.diag(H))
+            H[idx, idx] = 1.0
+        else:
+            H[idx, idx] = 1.0
+            lam = damp * np.mean(np.diag(H))
+        if kind == "absolute_damp":
+            lam = damp
+        H[np.arange(d), np.arange(d)] += lam
+        if act_order:
+            perm = np.argsort(colsq, kind="stable") if kind == "ascending" else O.activation_order(colsq)
+        else:
+            perm = np.arange(d)
+        H_p = H[np.ix_(perm, perm)]
+        return H_p, perm, dead, lam
+    return prepare
+
+
+def _factor_factory(kind):
+    def factor(H_p):
+        if kind == "lower":
+            return np.linalg.cholesky(np.linalg.inv(H_p))
+        if kind == "chol_of_h":
+            return np.linalg.cholesky(H_p).T
+        if kind == "inverse_of_chol":
+            return np.linalg.inv(np.linalg.cholesky(H_p)).T
+        raise ValueError(kind)
+    return factor
+
+
+PINS = [
+    (P.test_golden_two_column_hand, ()),
+    (P.test_hessian_brute_force_and_chunking, ()),
+    (P.test_damping_and_dead_hand_values, ()),
+    (P.test_all_dead_inputs, ()),
+    (P.test_u_factor_properties_and_reverse_closed_form, (7,)),
+    (P.test_u_rows_are_eliminated_inverse_rows, ()),
+    (P.test_cholesky_form_equals_obs_elimination, (3,)),
+    (P.test_cholesky_form_equals_obs_elimination, (5,)),
+    (P.test_loop_matches_exact_rational_obs, (0,)),
+    (P.test_loop_matches_exact_rational_obs, (4,)),
+    (P.test_each_step_is_the_constrained_least_squares_solve, ()),
+    (P.test_group_scales_from_updated_weights_exact, (0,)),
+    (P.test_group_scales_from_updated_weights_exact, (1,)),
+    (P.test_loss_identity, (4, True)),
+    (P.test_clipping_propagates_clipped_error, ()),
+    (P.test_group_sizes_special_cases, ()),
+    (P.test_act_order_equals_explicitly_permuted_problem, ()),
+    (P.test_output_error_well_below_rtn, ("teacher", 3, False)),
+]
+
+MUTATIONS = [
+    ("compensation_loop", _loop_factory, k) for k in
+    ["sign", "transposed_u", "off_by_one", "no_divide", "unclipped_error", "floor_not_round",
+     "group_from_original"]
+] + [
+    ("prepare", _prepare_factory, k) for k in ["no_two", "damp_before_dead", "absolute_damp", "ascending"]
+] + [
+    ("upper_factor_of_inverse", _factor_factory, k) for k in ["lower", "chol_of_h", "inverse_of_chol"]
+]
+
+
+@pytest.mark.parametrize("name,factory,kind", MUTATIONS, ids=[f"{m[0]}-{m[2]}" for m in MUTATIONS])
+def test_pins_catch_planted_mistake(monkeypatch, name, factory, kind):
+    monkeypatch.setattr(O, name, factory(kind))
+    caught = []
+    for fn, args in PINS:
+        try:
+            fn(*args)
+        except (AssertionError, np.linalg.LinAlgError, FloatingPointError, ValueError, IndexError):
+            caught.append(fn.__name__)
+    assert caught, f"no pin caught mutation {name}:{kind}"
