@@ -1,0 +1,154 @@
+/*
+ * gptq_mi355x.h - C ABI of libgptq_mi355x.so: GPTQ per-layer weight quantization on one MI355X (gfx950).
+ *
+ * The layer problem (GPTQ guide, herodthegreater.github.io/pigeon/guide/gptq/, "How it works"; and the
+ * lesson "GPTQ's error-compensation loop", herodthegreater.github.io/pigeon/school/gptq_loop/):
+ * weights W (out x in), calibration inputs X (n x in), a symmetric b-bit grid with qmax = 2^(b-1) - 1,
+ * optional groups of `group` input columns with their own scales, damping `damp`, optional act_order.
+ * The path is three calls, each stream-ordered on the caller's HIP stream:
+ *
+ *   1. gptq_hessian_accumulate  S += X^T X, colsq += column sums of squares, n_total += rows
+ *   2. gptq_prepare_chol        H = 2 S / n_total, dead inputs, damping, act_order permutation,
+ *                               U = upper Cholesky factor of H^-1 (H^-1 = U^T U)
+ *   3. gptq_quantize_layer      the column-by-column error-compensation loop -> integer codes,
+ *                               scales and (optionally) g_idx and the per-row loss
+ *
+ * Conventions shared by every call
+ *  - All matrices are row-major. Every pointer to matrix/vector data is a DEVICE pointer unless stated
+ *    otherwise; `n_total` is the only host pointer.
+ *  - The caller owns every buffer, workspace included. The library allocates no device memory, frees
+ *    nothing and keeps no pointer after a call returns. Workspaces are sized by the *_workspace_bytes
+ *    queries and need no initialisation. Their contents after a call are unspecified.
+ *  - `stream` is a hipStream_t (NULL = the null stream). Calls 1 and 3 are fully asynchronous; call 2
+ *    synchronises `stream` once to read a 4-byte status word written by its kernels.
+ *  - Every call returns a gptq_status. On an argument error nothing is launched and no output is
+ *    written. Calls on different streams with disjoint buffers are independent; the library has no
+ *    global mutable state.
+ *  - W and X are read only. The library works on its own fp64 copy of W in the workspace.
+ */
+#ifndef GPTQ_MI355X_H
+#define GPTQ_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GPTQ_OK = 0,
+  GPTQ_ERR_INVALID_ARG = -1, /* bad size, pointer, dtype, bits, damp or leading dimension */
+  GPTQ_ERR_UNSUPPORTED = -2, /* valid request this library does not implement (group size, see below) */
+  GPTQ_ERR_NOT_SPD = -3,     /* the damped Hessian has no Cholesky factor (a pivot <= 0) */
+  GPTQ_ERR_NONFINITE = -4,   /* NaN or Inf met in S, colsq or during the factorization */
+  GPTQ_ERR_WORKSPACE = -5,   /* ws is NULL or ws_bytes is below the size query's value */
+  GPTQ_ERR_HIP = -6          /* a HIP runtime call or kernel launch failed */
+} gptq_status;
+
+typedef enum { GPTQ_F32 = 0, GPTQ_BF16 = 1 } gptq_dtype;
+
+/* Factorization route for gptq_prepare_chol (`flags`).
+ *  GPTQ_FACTOR_INVERSE_RECHOL (0): L = chol(H); L^-1; H^-1 = L^-T L^-1; U = (chol(H^-1))^T, the order the
+ *    guide's _hessian_inverse_chol takes ("The code, line by line").
+ *  GPTQ_FACTOR_REVERSED (1): U = J chol(J H J)^-1 J with J the index reversal; the same unique U (upper,
+ *    positive diagonal, U^T U = H^-1) with half the flops, because H = V V^T with V = U^-1 upper. */
+#define GPTQ_FACTOR_INVERSE_RECHOL 0u
+#define GPTQ_FACTOR_REVERSED 1u
+
+/* ---------------------------------------------------------------------------------------------------
+ * 1. Hessian accumulation. GPTQ guide, "The idea": H = 2 X^T X / n is the curvature of the layer's
+ *    squared output error over n calibration inputs; the handbook page ("GPTQ > Implementation with
+ *    AutoGPTQ", compute_hessian) flattens (samples, seq, hidden) inputs to (tokens, hidden), so a caller
+ *    passes tokens as rows and may stream them in chunks with repeated calls.
+ *
+ *  X        n_rows x in, leading dimension ld_x >= in (elements), dtype x_dtype (GPTQ_F32 or GPTQ_BF16).
+ *           Rows may start at any element offset; 16-byte aligned rows (ld_x*elem % 16 == 0 and X 16-byte
+ *           aligned) take the fast load path.
+ *  S        in x in fp64. Only the lower triangle (i >= j) is read and written: S[i][j] += sum_k
+ *           X[k][i] X[k][j]. The caller zero-initialises S before the first chunk. The products of bf16
+ *           or fp32 inputs are formed on the matrix cores and summed in fp32 within a slice of rows;
+ *           slices are summed in fp64 in a fixed order, so results are bitwise reproducible.
+ *  colsq    fp64[in]: colsq[i] += sum_k X[k][i]^2, summed in fp64 (the act_order key and the exact
+ *           dead-input test need it exact up to fp64 rounding). Caller zero-initialises.
+ *  n_total  HOST pointer; incremented by n_rows when the call is accepted.
+ *  ws       workspace of at least gptq_hessian_workspace_bytes(n_rows, in, x_dtype) bytes.
+ *  Errors   INVALID_ARG (n_rows < 1, in < 1, ld_x < in, unknown dtype, NULL pointer), WORKSPACE, HIP.
+ * ------------------------------------------------------------------------------------------------- */
+size_t gptq_hessian_workspace_bytes(int64_t n_rows, int64_t in, int x_dtype);
+int gptq_hessian_accumulate(const void* X, int x_dtype, int64_t n_rows, int64_t in, int64_t ld_x,
+                            double* S, double* colsq, int64_t* n_total,
+                            void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------------------------
+ * 2. Damping, dead inputs, order and the factor U. GPTQ guide, "The code, line by line"
+ *    (_hessian_inverse_chol and the act_order bullet), "How it works" (Damping; GPTQ's two tricks,
+ *    trick 2) and "When it breaks" (bad H).
+ *
+ *  H = 2 S / n_total (S's lower triangle). Input i is dead when colsq[i] == 0 exactly; dead inputs get
+ *  H[i][i] = 1 (diagonal only). Then lambda = damp * mean(diag H) is added to the diagonal.
+ *  act_order != 0: perm sorts inputs by decreasing colsq (= diag X^T X, taken before the dead fix),
+ *  equal keys by increasing index; otherwise perm is the identity. U is the factor for P^T H P.
+ *
+ *  S, colsq   as left by gptq_hessian_accumulate (in x in lower triangle; in).
+ *  U          out: in x in fp64, upper triangular with positive diagonal, U^T U = (P^T H P)^-1, in
+ *             quantization order; the strictly lower triangle is set to 0.
+ *  perm       out: int32[in], perm[j] = original input index quantized at position j.
+ *  dead       out: uint8[in], 1 for dead inputs (original order).
+ *  flags      GPTQ_FACTOR_INVERSE_RECHOL or GPTQ_FACTOR_REVERSED.
+ *  ws         at least gptq_prepare_workspace_bytes(in) bytes.
+ *  Synchronises `stream` once. Errors: INVALID_ARG (in < 1, n_total < 1, damp < 0 or not finite, NULL
+ *  pointer, unknown flags), WORKSPACE, NOT_SPD (a pivot <= 0, e.g. damp = 0 with a rank-deficient X),
+ *  NONFINITE (NaN/Inf in S or colsq, or met in a pivot), HIP. On NOT_SPD/NONFINITE, U is unspecified.
+ * ------------------------------------------------------------------------------------------------- */
+size_t gptq_prepare_workspace_bytes(int64_t in);
+int gptq_prepare_chol(const double* S, const double* colsq, int64_t n_total, int64_t in,
+                      double damp, int act_order, unsigned flags,
+                      double* U, int32_t* perm, uint8_t* dead,
+                      void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------------------------
+ * 3. The error-compensation loop. Lesson "GPTQ's error-compensation loop" (the four steps: round column
+ *    j of every row, err = (w - q) / U[j][j], W[:, j+1:] -= outer(err, U[j, j+1:])) and GPTQ guide,
+ *    "The code, line by line" (per-row scales from the starting weights; with groups, scales from the
+ *    already-updated weights at each group boundary; clip to +-qmax) and "When it breaks" (g_idx).
+ *    The guide's "Simplifications" mentions lazy updates in 128-column blocks; this library quantizes
+ *    128-column panels in registers and applies each panel's errors to the columns on its right as one
+ *    matrix product, which computes the same loop.
+ *
+ *  W          out x in, leading dimension ld_w >= in, dtype w_dtype (GPTQ_F32 or GPTQ_BF16).
+ *  U, perm, dead  as produced by gptq_prepare_chol (or supplied by the caller with the same meaning).
+ *  bits       2..8; codes lie in [-qmax, qmax], qmax = 2^(bits-1) - 1.
+ *  group      0 = one scale per row from the starting (dead-zeroed) weights; otherwise scales for each
+ *             run of `group` columns in quantization order. Supported: group divides 128 or is a multiple
+ *             of 128 (group boundaries must fall on the 128-column panel grid); others -> UNSUPPORTED.
+ *  codes      out: int8, out x in, ORIGINAL column order (codes[r][perm[j]] is position j's code).
+ *  scales     out: fp32, out x G, G = group ? ceil(in/group) : 1; column g = g-th group in quantization
+ *             order. The arithmetic is fp64; the stored scale is rounded to fp32.
+ *  g_idx      out (may be NULL): int32[in], g_idx[perm[j]] = j / group (0 when group == 0).
+ *  row_loss   out (may be NULL): fp64[out], sum over columns of err^2, which equals (q - w0) H (q - w0)^T
+ *             for the row's dead-zeroed, permuted start w0 and result q.
+ *  Dequantized weights: Q[r][c] = codes[r][c] * scales[r][g_idx[c]] (with fp64 scales: see row_loss).
+ *  ws         at least gptq_quantize_workspace_bytes(out, in) bytes.
+ *  Non-finite weights are not detected; their codes are unspecified.
+ *  Errors: INVALID_ARG (out/in < 1, ld_w < in, bits outside 2..8, group < 0, unknown dtype, NULL required
+ *  pointer), UNSUPPORTED (group), WORKSPACE, HIP.
+ * ------------------------------------------------------------------------------------------------- */
+size_t gptq_quantize_workspace_bytes(int64_t out, int64_t in);
+int gptq_quantize_layer(const void* W, int w_dtype, int64_t out, int64_t in, int64_t ld_w,
+                        const double* U, const int32_t* perm, const uint8_t* dead,
+                        int bits, int group,
+                        int8_t* codes, float* scales, int32_t* g_idx, double* row_loss,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/* Human-readable name of a gptq_status value (static storage). */
+const char* gptq_status_string(int status);
+
+/* Library version string (static storage). */
+const char* gptq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GPTQ_MI355X_H */

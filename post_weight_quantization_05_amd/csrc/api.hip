@@ -1,0 +1,97 @@
+// C ABI of libgptq_mi355x: argument validation, workspace sizing and launch sequencing. Every check runs
+// on the host before anything is launched, so an argument error writes nothing.
+#include <cmath>
+#include <cstring>
+
+#include "common.h"
+
+using namespace gptq;
+
+namespace {
+
+bool valid_dtype(int t) { return t == GPTQ_F32 || t == GPTQ_BF16; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? GPTQ_OK : GPTQ_ERR_HIP; }
+
+// Sizes are bounded so that every index the kernels form fits their int arithmetic.
+constexpr int64_t MAX_IN = 65536;
+constexpr int64_t MAX_OUT = 1 << 20;
+
+}  // namespace
+
+extern "C" {
+
+const char* gptq_status_string(int status) {
+  switch (status) {
+    case GPTQ_OK: return "GPTQ_OK";
+    case GPTQ_ERR_INVALID_ARG: return "GPTQ_ERR_INVALID_ARG";
+    case GPTQ_ERR_UNSUPPORTED: return "GPTQ_ERR_UNSUPPORTED";
+    case GPTQ_ERR_NOT_SPD: return "GPTQ_ERR_NOT_SPD";
+    case GPTQ_ERR_NONFINITE: return "GPTQ_ERR_NONFINITE";
+    case GPTQ_ERR_WORKSPACE: return "GPTQ_ERR_WORKSPACE";
+    case GPTQ_ERR_HIP: return "GPTQ_ERR_HIP";
+    default: return "GPTQ_ERR_UNKNOWN";
+  }
+}
+
+const char* gptq_version(void) { return "gptq_mi355x 0.1 (gfx950)"; }
+
+size_t gptq_hessian_workspace_bytes(int64_t n_rows, int64_t in, int x_dtype) {
+  if (n_rows < 1 || in < 1 || in > MAX_IN || !valid_dtype(x_dtype)) return 0;
+  return hessian_plan(n_rows, in, x_dtype).total_bytes;
+}
+
+int gptq_hessian_accumulate(const void* X, int x_dtype, int64_t n_rows, int64_t in, int64_t ld_x, double* S,
+                            double* colsq, int64_t* n_total, void* ws, size_t ws_bytes, void* stream) {
+  if (!X || !S || !colsq || !n_total) return GPTQ_ERR_INVALID_ARG;
+  if (n_rows < 1 || in < 1 || in > MAX_IN || ld_x < in || !valid_dtype(x_dtype)) return GPTQ_ERR_INVALID_ARG;
+  if (*n_total < 0) return GPTQ_ERR_INVALID_ARG;
+  HessianPlan p = hessian_plan(n_rows, in, x_dtype);
+  p.ld = ld_x;
+  if (!ws || ws_bytes < p.total_bytes) return GPTQ_ERR_WORKSPACE;
+  const int st = hip_status(hessian_launch(p, X, S, colsq, ws, reinterpret_cast<hipStream_t>(stream)));
+  if (st == GPTQ_OK) *n_total += n_rows;
+  return st;
+}
+
+size_t gptq_prepare_workspace_bytes(int64_t in) {
+  if (in < 1 || in > MAX_IN) return 0;
+  return prepare_ws_bytes(in);
+}
+
+int gptq_prepare_chol(const double* S, const double* colsq, int64_t n_total, int64_t in, double damp, int act_order,
+                      unsigned flags, double* U, int32_t* perm, uint8_t* dead, void* ws, size_t ws_bytes,
+                      void* stream) {
+  if (!S || !colsq || !U || !perm || !dead) return GPTQ_ERR_INVALID_ARG;
+  if (in < 1 || in > MAX_IN || n_total < 1) return GPTQ_ERR_INVALID_ARG;
+  if (!(damp >= 0.0) || !std::isfinite(damp)) return GPTQ_ERR_INVALID_ARG;
+  if ((flags & ~GPTQ_FACTOR_REVERSED) != 0u) return GPTQ_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < prepare_ws_bytes(in)) return GPTQ_ERR_WORKSPACE;
+  unsigned dev_status = 0;
+  hipError_t e = prepare_launch(S, colsq, n_total, in, damp, act_order ? 1 : 0, flags, U, perm, dead, ws,
+                                reinterpret_cast<hipStream_t>(stream), &dev_status);
+  if (e != hipSuccess) return GPTQ_ERR_HIP;
+  if (dev_status & DEV_STATUS_NONFINITE) return GPTQ_ERR_NONFINITE;
+  if (dev_status & DEV_STATUS_NOT_SPD) return GPTQ_ERR_NOT_SPD;
+  return GPTQ_OK;
+}
+
+size_t gptq_quantize_workspace_bytes(int64_t out, int64_t in) {
+  if (out < 1 || in < 1 || in > MAX_IN || out > MAX_OUT) return 0;
+  return quantize_ws_bytes(out, in);
+}
+
+int gptq_quantize_layer(const void* W, int w_dtype, int64_t out, int64_t in, int64_t ld_w, const double* U,
+                        const int32_t* perm, const uint8_t* dead, int bits, int group, int8_t* codes, float* scales,
+                        int32_t* g_idx, double* row_loss, void* ws, size_t ws_bytes, void* stream) {
+  if (!W || !U || !perm || !dead || !codes || !scales) return GPTQ_ERR_INVALID_ARG;
+  if (out < 1 || in < 1 || in > MAX_IN || out > MAX_OUT || ld_w < in || !valid_dtype(w_dtype))
+    return GPTQ_ERR_INVALID_ARG;
+  if (bits < 2 || bits > 8 || group < 0) return GPTQ_ERR_INVALID_ARG;
+  if (group != 0 && !(128 % group == 0 || group % 128 == 0)) return GPTQ_ERR_UNSUPPORTED;
+  if (!ws || ws_bytes < quantize_ws_bytes(out, in)) return GPTQ_ERR_WORKSPACE;
+  return hip_status(quantize_launch(W, w_dtype, out, in, ld_w, U, perm, dead, bits, group, codes, scales, g_idx,
+                                    row_loss, ws, reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

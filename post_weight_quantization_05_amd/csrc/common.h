@@ -1,0 +1,57 @@
+// Shared device/host definitions of libgptq_mi355x (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/gptq_mi355x.h"
+
+namespace gptq {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) double f64x4;
+
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// Device status word bits (written with atomicOr, read once by the host at the end of prepare).
+enum : unsigned {
+  DEV_STATUS_NOT_SPD = 1u,
+  DEV_STATUS_NONFINITE = 2u,
+};
+
+static inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+static inline size_t align_up(size_t a, size_t b) { return (a + b - 1) / b * b; }
+
+// ---- kernel launchers (defined in the .hip files) --------------------------------------------------
+
+// Hessian (hessian.hip)
+struct HessianPlan {
+  int64_t n_rows, in, ld;
+  int dtype;
+  int tile;        // square output tile (256)
+  int n_tb;        // tile blocks per side = ceil(in / tile)
+  int n_tiles;     // lower-triangle tiles = n_tb (n_tb + 1) / 2
+  int splits;      // row slices (split-K)
+  int64_t rows_per_split;
+  size_t part_bytes, colsq_part_bytes, total_bytes;
+};
+HessianPlan hessian_plan(int64_t n_rows, int64_t in, int dtype);
+hipError_t hessian_launch(const HessianPlan& p, const void* X, double* S, double* colsq, void* ws,
+                          hipStream_t stream);
+
+// Prepare + factorization (factor.hip)
+size_t prepare_ws_bytes(int64_t in);
+hipError_t prepare_launch(const double* S, const double* colsq, int64_t n_total, int64_t in, double damp,
+                          int act_order, unsigned flags, double* U, int32_t* perm, uint8_t* dead, void* ws,
+                          hipStream_t stream, unsigned* host_status);
+
+// Quantize (quant.hip)
+size_t quantize_ws_bytes(int64_t out, int64_t in);
+hipError_t quantize_launch(const void* W, int w_dtype, int64_t out, int64_t in, int64_t ld_w, const double* U,
+                           const int32_t* perm, const uint8_t* dead, int bits, int group, int8_t* codes,
+                           float* scales, int32_t* g_idx, double* row_loss, void* ws, hipStream_t stream);
+
+}  // namespace gptq

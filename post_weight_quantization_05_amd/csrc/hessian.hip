@@ -1,0 +1,424 @@
+// Hessian accumulation S += X^T X (lower triangle) and colsq += sum x^2, on gfx950 matrix cores.
+//
+// GPTQ guide ("GPTQ", herodthegreater.github.io/pigeon/guide/gptq/), "The idea": H = 2 X^T X / n over
+// the calibration inputs; the 2/n scaling is applied in the prepare step, this file only sums.
+//
+// Design (bf16 X, the transformer workloads):
+//  * Output tiles of 256 x 256 over the lower triangle only (i-block >= j-block); the n calibration rows
+//    are cut into `splits` row slices so that tiles x splits fills the chip (split-K).
+//  * One workgroup = 4 waves (2 x 2), each wave a 128 x 128 block of fp32 accumulators fed by
+//    v_mfma_f32_32x32x16_bf16 (bf16 x bf16 products are exact in fp32).
+//  * X is row-major (rows = tokens), so a tile of 32 rows x 256 columns is read with 16-byte coalesced
+//    loads and stored to LDS as [k][i]. The MFMA operands need 8 consecutive k per lane: they are read
+//    with ds_read_b64_tr_b16, which transposes a 4 x 16 block of 16-bit elements across 16 lanes.
+//  * Double-buffered LDS, one barrier per 32-row stage; the next stage's global loads are in flight
+//    while the current stage's MFMAs run.
+//  * Diagonal tiles read one column block (A = B) and also form the fp64 column sums of squares from
+//    the staged registers (x^2 of a bf16/fp32 value is exact in fp64).
+//  * Each (slice, tile) writes an fp32 partial; a second kernel adds the slices in a fixed order in fp64
+//    to S, so the result is bitwise reproducible.
+//  * Workgroup index -> (slice, tile) is remapped so that the workgroups resident on one XCD (dispatch is
+//    round-robin over the 8 XCDs) work on the same row slice and share its rows in that XCD's L2.
+// fp32 X (small layers) uses the same structure with v_mfma_f32_16x16x4f32 on 128 x 128 tiles; fp32
+// operands need no transpose (one k per lane).
+#include <algorithm>
+
+#include "common.h"
+
+namespace gptq {
+
+namespace {
+
+constexpr int BT = 256;       // bf16 tile edge
+constexpr int BK = 32;        // rows per stage
+constexpr int BROW = BT + 32; // LDS row stride in bf16 elements (576 B; the pad spreads rows over banks)
+
+constexpr int FT = 128;       // fp32 tile edge
+constexpr int FK = 16;        // rows per stage
+constexpr int FROW = FT + 4;  // LDS row stride in floats
+
+__device__ __forceinline__ void tile_coords(int t, int& I, int& J) {
+  // t = I (I + 1) / 2 + J with 0 <= J <= I
+  int I0 = (int)((sqrtf(8.0f * (float)t + 1.0f) - 1.0f) * 0.5f);
+  while ((I0 + 1) * (I0 + 2) / 2 <= t) ++I0;
+  while (I0 * (I0 + 1) / 2 > t) --I0;
+  I = I0;
+  J = t - I0 * (I0 + 1) / 2;
+}
+
+// Load 8 consecutive bf16 of one row (cols c..c+7), zero outside [0, d) or beyond the valid rows.
+template <bool VEC>
+__device__ __forceinline__ uint4 load8_bf16(const uint16_t* __restrict__ X, int64_t ld, int64_t row, bool row_ok,
+                                            int c, int d) {
+  uint4 v = make_uint4(0, 0, 0, 0);
+  if (!row_ok) return v;
+  const uint16_t* p = X + row * ld + c;
+  if (VEC && c + 8 <= d) {
+    v = *reinterpret_cast<const uint4*>(p);
+  } else {
+    uint16_t e[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) e[q] = (c + q < d) ? p[q] : (uint16_t)0;
+    v.x = e[0] | ((uint32_t)e[1] << 16);
+    v.y = e[2] | ((uint32_t)e[3] << 16);
+    v.z = e[4] | ((uint32_t)e[5] << 16);
+    v.w = e[6] | ((uint32_t)e[7] << 16);
+  }
+  return v;
+}
+
+__device__ __forceinline__ void sq_accum8(double* acc, uint4 v) {
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    double lo = (double)__uint_as_float(w[q] << 16);
+    double hi = (double)__uint_as_float(w[q] & 0xFFFF0000u);
+    acc[2 * q] = fma(lo, lo, acc[2 * q]);
+    acc[2 * q + 1] = fma(hi, hi, acc[2 * q + 1]);
+  }
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(256, 1) void k_xtx_bf16(const uint16_t* __restrict__ X, int64_t ld, int64_t n_rows,
+                                                     int d, int n_tiles, int64_t rps, int remap,
+                                                     float* __restrict__ part, double* __restrict__ colsq_part,
+                                                     int colsq_stride) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][BK][BROW];
+
+  const int G = gridDim.x;
+  const int b = blockIdx.x;
+  const int L = remap ? (b % 8) * (G / 8) + b / 8 : b;
+  const int split = L / n_tiles;
+  const int t = L - split * n_tiles;
+  int I, J;
+  tile_coords(t, I, J);
+  const bool diag = (I == J);
+  const int colA = I * BT, colB = J * BT;
+  const int64_t r0 = (int64_t)split * rps;
+  const int64_t r1 = min(n_rows, r0 + rps);
+  const int nk = (int)((r1 - r0 + BK - 1) / BK);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const bool active = !(diag && wm == 0 && wn == 1);  // upper-right quadrant of a diagonal tile
+
+  // global -> register staging: pass p covers rows (tid/32) + 8p, 8 columns at (tid%32)*8
+  const int ld_row = tid >> 5;
+  const int ld_col = (tid & 31) * 8;
+  uint4 ra[4], rb[4];
+  double csq[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) csq[q] = 0.0;
+
+  auto gload = [&](int kt) {
+    const int64_t base = r0 + (int64_t)kt * BK;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int64_t row = base + ld_row + 8 * p;
+      const bool ok = row < r1;
+      ra[p] = load8_bf16<VEC>(X, ld, row, ok, colA + ld_col, d);
+      if (!diag) rb[p] = load8_bf16<VEC>(X, ld, row, ok, colB + ld_col, d);
+    }
+  };
+  auto lstore = [&](int st) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      *reinterpret_cast<uint4*>(&lds[st][0][ld_row + 8 * p][ld_col]) = ra[p];
+      if (!diag) *reinterpret_cast<uint4*>(&lds[st][1][ld_row + 8 * p][ld_col]) = rb[p];
+    }
+    if (diag) {
+#pragma unroll
+      for (int p = 0; p < 4; ++p) sq_accum8(csq, ra[p]);
+    }
+  };
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mb][nb][r] = 0.0f;
+
+  const int g = lane >> 4, s = lane & 15;
+  const int opB = diag ? 0 : 1;
+
+  if (nk > 0) {
+    gload(0);
+    lstore(0);
+  }
+  __syncthreads();
+
+  for (int kt = 0; kt < nk; ++kt) {
+    const int st = kt & 1;
+    if (kt + 1 < nk) gload(kt + 1);
+    if (active) {
+#pragma unroll 1
+      for (int k16 = 0; k16 < BK; k16 += 16) {
+        const int kb = k16 + 8 * (g >> 1) + (s >> 2);
+        const int ioff = 16 * (g & 1) + (s & 3) * 4;
+        bf16x8 fa[4], fb[4];
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+          const int ic = wm * 128 + mb * 32 + ioff;
+          i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)&lds[st][0][kb][ic]);
+          i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)&lds[st][0][kb + 4][ic]);
+          fa[mb] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+          const int jc = wn * 128 + nb * 32 + ioff;
+          i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)&lds[st][opB][kb][jc]);
+          i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)&lds[st][opB][kb + 4][jc]);
+          fb[nb] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb)
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mb], fb[nb], acc[mb][nb], 0, 0, 0);
+      }
+    }
+    if (kt + 1 < nk) lstore(st ^ 1);
+    __syncthreads();
+  }
+
+  // fp32 partial of this (slice, tile): element (i, j) at i * 256 + j
+  if (active) {
+    float* dst = part + ((int64_t)split * n_tiles + t) * (BT * BT);
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int i = wm * 128 + mb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          const int j = wn * 128 + nb * 32 + (lane & 31);
+          dst[i * BT + j] = acc[mb][nb][r];
+        }
+  }
+  if (diag) {
+    // reduce the 8 row-groups of column sums in a fixed order
+    double* red = reinterpret_cast<double*>(&lds[0][0][0][0]);  // 8 x 256 doubles = 16 KB
+#pragma unroll
+    for (int q = 0; q < 8; ++q) red[ld_row * BT + ld_col + q] = csq[q];
+    __syncthreads();
+    double sum = 0.0;
+#pragma unroll
+    for (int rg = 0; rg < 8; ++rg) sum += red[rg * BT + tid];
+    colsq_part[(int64_t)split * colsq_stride + colA + tid] = sum;
+  }
+}
+
+// ---------------------------------------------------------------------------------------------------
+// fp32 X
+// ---------------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256, 1) void k_xtx_f32(const float* __restrict__ X, int64_t ld, int64_t n_rows, int d,
+                                                    int n_tiles, int64_t rps, int remap, float* __restrict__ part,
+                                                    double* __restrict__ colsq_part, int colsq_stride) {
+  __shared__ __attribute__((aligned(16))) float lds[2][2][FK][FROW];
+  const int G = gridDim.x;
+  const int b = blockIdx.x;
+  const int L = remap ? (b % 8) * (G / 8) + b / 8 : b;
+  const int split = L / n_tiles;
+  const int t = L - split * n_tiles;
+  int I, J;
+  tile_coords(t, I, J);
+  const bool diag = (I == J);
+  const int colA = I * FT, colB = J * FT;
+  const int64_t r0 = (int64_t)split * rps;
+  const int64_t r1 = min(n_rows, r0 + rps);
+  const int nk = (int)((r1 - r0 + FK - 1) / FK);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const bool active = !(diag && wm == 0 && wn == 1);
+
+  // staging: 16 rows x 128 floats per operand = 2048 floats = 8 per thread: row tid/16 (0..15), cols (tid%16)*8
+  const int ld_row = tid >> 4;
+  const int ld_col = (tid & 15) * 8;
+  float ra[8], rb[8];
+  double csq[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) csq[q] = 0.0;
+
+  auto gload = [&](int kt) {
+    const int64_t row = r0 + (int64_t)kt * FK + ld_row;
+    const bool ok = row < r1;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int ca = colA + ld_col + q, cb = colB + ld_col + q;
+      ra[q] = (ok && ca < d) ? X[row * ld + ca] : 0.0f;
+      rb[q] = (!diag && ok && cb < d) ? X[row * ld + cb] : 0.0f;
+    }
+  };
+  auto lstore = [&](int st) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      lds[st][0][ld_row][ld_col + q] = ra[q];
+      if (!diag) lds[st][1][ld_row][ld_col + q] = rb[q];
+    }
+    if (diag) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) csq[q] = fma((double)ra[q], (double)ra[q], csq[q]);
+    }
+  };
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  const int opB = diag ? 0 : 1;
+
+  if (nk > 0) {
+    gload(0);
+    lstore(0);
+  }
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int st = kt & 1;
+    if (kt + 1 < nk) gload(kt + 1);
+    if (active) {
+#pragma unroll
+      for (int k4 = 0; k4 < FK; k4 += 4) {
+        const int k = k4 + (lane >> 4);
+        float fa[4], fb[4];
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) fa[mb] = lds[st][0][k][wm * 64 + mb * 16 + (lane & 15)];
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) fb[nb] = lds[st][opB][k][wn * 64 + nb * 16 + (lane & 15)];
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb)
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[mb], fb[nb], acc[mb][nb], 0, 0, 0);
+      }
+    }
+    if (kt + 1 < nk) lstore(st ^ 1);
+    __syncthreads();
+  }
+  if (active) {
+    float* dst = part + ((int64_t)split * n_tiles + t) * (FT * FT);
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = wm * 64 + mb * 16 + 4 * (lane >> 4) + r;
+          const int j = wn * 64 + nb * 16 + (lane & 15);
+          dst[i * FT + j] = acc[mb][nb][r];
+        }
+  }
+  if (diag) {
+    double* red = reinterpret_cast<double*>(&lds[0][0][0][0]);  // 16 x 128 doubles = 16 KB
+#pragma unroll
+    for (int q = 0; q < 8; ++q) red[ld_row * FT + ld_col + q] = csq[q];
+    __syncthreads();
+    if (tid < FT) {
+      double sum = 0.0;
+#pragma unroll
+      for (int rg = 0; rg < 16; ++rg) sum += red[rg * FT + tid];
+      colsq_part[(int64_t)split * colsq_stride + colA + tid] = sum;
+    }
+  }
+}
+
+// S[gi][gj] += sum over slices (fixed order) of the fp32 partials, lower triangle only.
+// grid = n_tiles * tile rows; block = tile threads (one per column of the tile row).
+__global__ __launch_bounds__(256) void k_xtx_combine(const float* __restrict__ part, int tile, int n_tiles, int splits,
+                                                     int d, double* __restrict__ S) {
+  const int t = blockIdx.x / tile;
+  const int i = blockIdx.x - t * tile;
+  int I, J;
+  tile_coords(t, I, J);
+  const int gi = I * tile + i;
+  if (gi >= d) return;
+  const int64_t tsz = (int64_t)tile * tile;
+  for (int j = threadIdx.x; j < tile; j += blockDim.x) {
+    const int gj = J * tile + j;
+    if (gj > gi || gj >= d) continue;
+    const float* p = part + (int64_t)t * tsz + (int64_t)i * tile + j;
+    double sum = 0.0;
+    for (int sidx = 0; sidx < splits; ++sidx) sum += (double)p[(int64_t)sidx * n_tiles * tsz];
+    S[(int64_t)gi * d + gj] += sum;
+  }
+}
+
+__global__ void k_colsq_combine(const double* __restrict__ cpart, int stride, int splits, int d,
+                                double* __restrict__ colsq) {
+  const int c = blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= d) return;
+  double sum = 0.0;
+  for (int s = 0; s < splits; ++s) sum += cpart[(int64_t)s * stride + c];
+  colsq[c] += sum;
+}
+
+}  // namespace
+
+HessianPlan hessian_plan(int64_t n_rows, int64_t in, int dtype) {
+  HessianPlan p{};
+  p.n_rows = n_rows;
+  p.in = in;
+  p.dtype = dtype;
+  p.tile = (dtype == GPTQ_BF16) ? BT : FT;
+  const int kstep = (dtype == GPTQ_BF16) ? BK : FK;
+  p.n_tb = (int)ceil_div(in, p.tile);
+  p.n_tiles = p.n_tb * (p.n_tb + 1) / 2;
+  // Row slices: balance tiles x slices over the CUs (one resident workgroup per CU), keep each slice at
+  // least 1024 rows, and charge a little for every extra slice (its fp32 partial is re-read once).
+  const int cus = 256;  // planning constant (MI355X); the launch itself works for any CU count
+  const int64_t max_splits = std::max<int64_t>(1, std::min<int64_t>(64, n_rows / 1024));
+  double best = 1e30;
+  int best_s = 1;
+  for (int s = 1; s <= max_splits; ++s) {
+    const double rounds = (double)ceil_div((int64_t)p.n_tiles * s, cus);
+    const double cost = rounds / s + 0.004 * s;
+    if (cost < best - 1e-12) {
+      best = cost;
+      best_s = s;
+    }
+  }
+  p.splits = best_s;
+  p.rows_per_split = ceil_div(ceil_div(n_rows, p.splits), kstep) * kstep;
+  p.splits = (int)ceil_div(n_rows, p.rows_per_split);
+  p.part_bytes = align_up((size_t)p.splits * p.n_tiles * p.tile * p.tile * sizeof(float), 256);
+  p.colsq_part_bytes = align_up((size_t)p.splits * p.n_tb * p.tile * sizeof(double), 256);
+  p.total_bytes = p.part_bytes + p.colsq_part_bytes;
+  p.ld = 0;
+  return p;
+}
+
+hipError_t hessian_launch(const HessianPlan& p, const void* X, double* S, double* colsq, void* ws,
+                          hipStream_t stream) {
+  float* part = reinterpret_cast<float*>(ws);
+  double* cpart = reinterpret_cast<double*>(reinterpret_cast<char*>(ws) + p.part_bytes);
+  const int grid = p.splits * p.n_tiles;
+  const int remap = (grid % 8 == 0) ? 1 : 0;
+  const int cstride = p.n_tb * p.tile;
+  if (p.dtype == GPTQ_BF16) {
+    const bool vec = (p.ld % 8 == 0) && (p.in % 8 == 0) && ((reinterpret_cast<uintptr_t>(X) & 15) == 0);
+    if (vec)
+      hipLaunchKernelGGL(k_xtx_bf16<true>, dim3(grid), dim3(256), 0, stream, (const uint16_t*)X, p.ld, p.n_rows,
+                         (int)p.in, p.n_tiles, p.rows_per_split, remap, part, cpart, cstride);
+    else
+      hipLaunchKernelGGL(k_xtx_bf16<false>, dim3(grid), dim3(256), 0, stream, (const uint16_t*)X, p.ld, p.n_rows,
+                         (int)p.in, p.n_tiles, p.rows_per_split, remap, part, cpart, cstride);
+  } else {
+    hipLaunchKernelGGL(k_xtx_f32, dim3(grid), dim3(256), 0, stream, (const float*)X, p.ld, p.n_rows, (int)p.in,
+                       p.n_tiles, p.rows_per_split, remap, part, cpart, cstride);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_xtx_combine, dim3(p.n_tiles * p.tile), dim3(256), 0, stream, part, p.tile, p.n_tiles,
+                     p.splits, (int)p.in, S);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_colsq_combine, dim3((unsigned)ceil_div(p.in, 256)), dim3(256), 0, stream, cpart, cstride,
+                     p.splits, (int)p.in, colsq);
+  return hipGetLastError();
+}
+
+}  // namespace gptq

@@ -1,0 +1,300 @@
+// The error-compensation loop on gfx950 (fp64 working copy).
+//
+// Lesson "GPTQ's error-compensation loop" (herodthegreater.github.io/pigeon/school/gptq_loop/): for
+// columns j = 0, 1, ...: q = round_to_grid(W[:, j]); err = (W[:, j] - q) / U[j][j];
+// W[:, j+1:] -= outer(err, U[j, j+1:]). GPTQ guide ("GPTQ", herodthegreater.github.io/pigeon/guide/gptq/),
+// "The code, line by line": one scale per row from the starting weights, or, with groups, a scale from
+// the already-updated weights of columns [j, j + group) at each group boundary; codes are
+// clip(round(w / scale), -qmax, qmax). "Simplifications" mentions lazy 128-column batch updates.
+//
+// Schedule (right-looking, 128-column panels):
+//  k_rowprep   W (bf16/fp32) -> fp64 working copy in quantization order, dead columns zeroed, per-row
+//              start scale (block max reduction).
+//  k_panel     per panel: 16 lanes per row (lane c holds columns c, c+16, ..., c+112 in registers), the
+//              128 x 128 block of U in LDS. Each step j broadcasts w_j from its owner lane with DPP
+//              (row_newbcast), every lane of the row rounds it (IEEE division, round-half-even), and
+//              updates its own columns with U[j][col] from LDS. Group maxima are 16-lane DPP max
+//              reductions. Codes and errors stay in registers and are stored once per panel.
+//  trailing    W[:, b1:] -= Err[:, panel] U[panel, b1:] on the fp64 MFMA GEMM core.
+#include <type_traits>
+#include <utility>
+
+#include "common.h"
+#include "dgemm.h"
+
+namespace gptq {
+
+namespace {
+
+constexpr int PW = 128;  // panel width
+constexpr double SCALE_FLOOR = 1e-12;
+
+template <int J, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (J < N) {
+    f(std::integral_constant<int, J>{});
+    static_for<J + 1, N>(f);
+  }
+}
+
+// value of lane K of this lane's 16-lane row
+template <int K>
+__device__ __forceinline__ double bcast16(double v) {
+  const long long x = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(x & 0xFFFFFFFFll), 0x150 + K, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(x >> 32), 0x150 + K, 0xF, 0xF, false);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+
+template <int R>
+__device__ __forceinline__ double ror16(double v) {
+  const long long x = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(x & 0xFFFFFFFFll), 0x120 + R, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(x >> 32), 0x120 + R, 0xF, 0xF, false);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+
+__device__ __forceinline__ double max16(double v) {
+  v = fmax(v, ror16<8>(v));
+  v = fmax(v, ror16<4>(v));
+  v = fmax(v, ror16<2>(v));
+  v = fmax(v, ror16<1>(v));
+  return v;
+}
+
+__device__ __forceinline__ double sum16(double v) {
+  v += ror16<8>(v);
+  v += ror16<4>(v);
+  v += ror16<2>(v);
+  v += ror16<1>(v);
+  return v;
+}
+
+template <typename T>
+__device__ __forceinline__ double to_f64(T v);
+template <>
+__device__ __forceinline__ double to_f64<float>(float v) { return (double)v; }
+template <>
+__device__ __forceinline__ double to_f64<uint16_t>(uint16_t v) {
+  return (double)__uint_as_float(((uint32_t)v) << 16);
+}
+
+// One workgroup per row: Wq[r][j] = W[r][perm[j]] (0 for dead inputs), scale_row[r] = max(max|w|,
+// 1e-12) / qmax; per-row scales are also the output scales when group == 0.
+template <typename T>
+__global__ __launch_bounds__(256) void k_rowprep(const T* __restrict__ W, int64_t ld_w, int in,
+                                                 const int32_t* __restrict__ perm, const uint8_t* __restrict__ dead,
+                                                 double qmax, int group, double* __restrict__ Wq,
+                                                 double* __restrict__ scale_row, float* __restrict__ scales,
+                                                 double* __restrict__ row_loss) {
+  __shared__ double red[256];
+  const int r = blockIdx.x;
+  const T* wr = W + (int64_t)r * ld_w;
+  double* q = Wq + (int64_t)r * in;
+  double mx = 0.0;
+  for (int j = threadIdx.x; j < in; j += 256) {
+    const int p = min(max(perm[j], 0), in - 1);
+    const double v = dead[p] ? 0.0 : to_f64<T>(wr[p]);
+    q[j] = v;
+    mx = fmax(mx, fabs(v));
+  }
+  red[threadIdx.x] = mx;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (threadIdx.x < s) red[threadIdx.x] = fmax(red[threadIdx.x], red[threadIdx.x + s]);
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const double s = fmax(red[0], SCALE_FLOOR) / qmax;
+    scale_row[r] = s;
+    if (group == 0) scales[r] = (float)s;
+    if (row_loss) row_loss[r] = 0.0;
+  }
+}
+
+// INPANEL = false: one scale per row, or groups that are multiples of 128 (the scale is recomputed at
+// panels where b0 % group == 0 and carried across panels in scale_row); INPANEL = true: groups dividing
+// 128 (boundaries inside the panel at j % group == 0).
+template <bool INPANEL>
+__global__ __launch_bounds__(256) void k_panel(double* __restrict__ Wq, int out, int in, int b0,
+                                               const double* __restrict__ U, const int32_t* __restrict__ perm,
+                                               double* __restrict__ scale_row, double qmax, int group,
+                                               int n_groups, int8_t* __restrict__ codes,
+                                               float* __restrict__ scales, double* __restrict__ Err,
+                                               double* __restrict__ row_loss) {
+  __shared__ double Us[PW][PW];
+  __shared__ double rdiag[PW];
+  __shared__ int pidx[PW];
+  const int tid = threadIdx.x;
+  const int pw = min(PW, in - b0);
+  for (int e = tid; e < PW * PW; e += 256) {
+    const int a = e / PW, b = e % PW;
+    Us[a][b] = (a < pw && b < pw && b >= a) ? U[(int64_t)(b0 + a) * in + b0 + b] : 0.0;
+  }
+  for (int a = tid; a < PW; a += 256) {
+    rdiag[a] = (a < pw) ? 1.0 / U[(int64_t)(b0 + a) * in + b0 + a] : 0.0;
+    pidx[a] = (a < pw) ? min(max(perm[b0 + a], 0), in - 1) : 0;
+  }
+  __syncthreads();
+
+  const int c = tid & 15;
+  const int r = blockIdx.x * 16 + (tid >> 4);
+  const bool rok = r < out;
+  double* wrow = Wq + (int64_t)(rok ? r : 0) * in;
+  double w[8];
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+    const int col = c + 16 * m;
+    w[m] = (rok && col < pw) ? wrow[b0 + col] : 0.0;
+  }
+
+  double s = 1.0;
+  if (!INPANEL) {
+    if (group != 0 && b0 % group == 0) {
+      const int glen = min(group, in - b0);
+      double lm = 0.0;
+      if (rok)
+        for (int col = c; col < glen; col += 16) lm = fmax(lm, fabs(wrow[b0 + col]));
+      lm = max16(lm);
+      s = fmax(lm, SCALE_FLOOR) / qmax;
+      if (rok && c == 0) {
+        scale_row[r] = s;
+        scales[(int64_t)r * n_groups + b0 / group] = (float)s;
+      }
+    } else {
+      s = rok ? scale_row[r] : 1.0;
+    }
+  }
+
+  int code_m[8];
+  double err_m[8];
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+    code_m[m] = 0;
+    err_m[m] = 0.0;
+  }
+
+#pragma unroll
+  for (int jm = 0; jm < 8; ++jm) {
+    static_for<0, 16>([&](auto jlc) {
+      constexpr int jl = decltype(jlc)::value;
+      const int j = jm * 16 + jl;
+      if (j < pw) {
+        if (INPANEL && (j % group) == 0) {
+          double lm = 0.0;
+#pragma unroll
+          for (int m = 0; m < 8; ++m) {
+            const int col = c + 16 * m;
+            lm = (col >= j && col < j + group) ? fmax(lm, fabs(w[m])) : lm;
+          }
+          lm = max16(lm);
+          s = fmax(lm, SCALE_FLOOR) / qmax;
+          if (rok && c == 0) scales[(int64_t)r * n_groups + (b0 + j) / group] = (float)s;
+        }
+        const double wj = bcast16<jl>(w[jm]);
+        // q = c * scale and err = (w - q) / U[j][j] with the rounding steps of the definition (no fused
+        // multiply-add): a weight that sits exactly on the grid leaves err = 0
+        const double cq = fmin(fmax(rint(wj / s), -qmax), qmax);
+        const double e = __dmul_rn(__dsub_rn(wj, __dmul_rn(cq, s)), rdiag[j]);
+        if (c == jl) {
+          code_m[jm] = (int)cq;
+          err_m[jm] = e;
+        }
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          if (m >= jm) w[m] = fma(-e, Us[j][c + 16 * m], w[m]);
+        }
+      }
+    });
+  }
+
+  double lsum = 0.0;
+  if (rok) {
+    int8_t* crow = codes + (int64_t)r * in;
+    double* erow = Err + (int64_t)r * PW;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const int col = c + 16 * m;
+      if (col < pw) {
+        crow[pidx[col]] = (int8_t)code_m[m];
+        erow[col] = err_m[m];
+        lsum = fma(err_m[m], err_m[m], lsum);
+      }
+    }
+  }
+  if (row_loss) {
+    lsum = sum16(lsum);
+    if (rok && c == 0) row_loss[r] += lsum;
+  }
+}
+
+__global__ void k_gidx(const int32_t* __restrict__ perm, int in, int group, int32_t* __restrict__ g_idx) {
+  const int j = blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= in) return;
+  const int p = min(max(perm[j], 0), in - 1);
+  g_idx[p] = group ? j / group : 0;
+}
+
+}  // namespace
+
+size_t quantize_ws_bytes(int64_t out, int64_t in) {
+  size_t b = 0;
+  b += align_up((size_t)out * in * sizeof(double), 256);  // working copy
+  b += align_up((size_t)out * PW * sizeof(double), 256);  // panel errors
+  b += align_up((size_t)out * sizeof(double), 256);       // current fp64 scale per row
+  return b;
+}
+
+hipError_t quantize_launch(const void* W, int w_dtype, int64_t out64, int64_t in64, int64_t ld_w, const double* U,
+                           const int32_t* perm, const uint8_t* dead, int bits, int group, int8_t* codes,
+                           float* scales, int32_t* g_idx, double* row_loss, void* ws, hipStream_t stream) {
+  const int out = (int)out64, in = (int)in64;
+  char* w = reinterpret_cast<char*>(ws);
+  double* Wq = reinterpret_cast<double*>(w);
+  w += align_up((size_t)out * in * sizeof(double), 256);
+  double* Err = reinterpret_cast<double*>(w);
+  w += align_up((size_t)out * PW * sizeof(double), 256);
+  double* scale_row = reinterpret_cast<double*>(w);
+  const double qmax = (double)((1 << (bits - 1)) - 1);
+  const int n_groups = group ? (int)ceil_div(in, group) : 1;
+
+  if (w_dtype == GPTQ_BF16)
+    hipLaunchKernelGGL(k_rowprep<uint16_t>, dim3(out), dim3(256), 0, stream, (const uint16_t*)W, ld_w, in, perm, dead,
+                       qmax, group, Wq, scale_row, scales, row_loss);
+  else
+    hipLaunchKernelGGL(k_rowprep<float>, dim3(out), dim3(256), 0, stream, (const float*)W, ld_w, in, perm, dead, qmax,
+                       group, Wq, scale_row, scales, row_loss);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  const dim3 pgrid((unsigned)ceil_div(out, 16));
+  for (int b0 = 0; b0 < in; b0 += PW) {
+    if (group != 0 && PW % group == 0)
+      k_panel<true><<<pgrid, dim3(256), 0, stream>>>(Wq, out, in, b0, U, perm, scale_row, qmax, group, n_groups,
+                                                     codes, scales, Err, row_loss);
+    else
+      k_panel<false><<<pgrid, dim3(256), 0, stream>>>(Wq, out, in, b0, U, perm, scale_row, qmax, group, n_groups,
+                                                      codes, scales, Err, row_loss);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int b1 = b0 + PW;
+    if (b1 < in) {
+      DgemmArgs t{};
+      t.A = Err; t.lda = PW;
+      t.B = U + (int64_t)b0 * in + b1; t.ldb = in;
+      t.C = Wq + b1; t.ldc = in;
+      t.M = out; t.N = in - b1; t.K = PW;
+      t.alpha = -1.0; t.beta = 1.0;
+      t.kmode = KMODE_FULL;
+      e = dgemm_launch(t, false, false, 1, stream);
+      if (e != hipSuccess) return e;
+    }
+  }
+  if (g_idx) {
+    hipLaunchKernelGGL(k_gidx, dim3((unsigned)ceil_div(in, 256)), dim3(256), 0, stream, perm, in, group, g_idx);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+}  // namespace gptq

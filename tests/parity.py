@@ -1,0 +1,70 @@
+"""Comparison helpers between the GPU path and the CPU oracle (test infrastructure).
+
+Gates (numbers from the target statement):
+  C-1  integer codes identical on >= 99.9% of entries
+  C-2  layer output error within 1% (relative) of the oracle's
+  C-3  every GPU code is one a correct loop could have chosen: replaying the oracle's loop with the GPU's
+       codes forced, |clip(w/scale) - c| <= 0.5 + tau for every entry ("mismatches only at round-half
+       boundaries")
+  C-4  dequantized Q relative Frobenius difference <= 1e-3
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from oracle import gptq_oracle as O
+import synthetic as syn
+
+TAU = 1e-4
+
+
+def to_device(arr: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
+    """Encoded synthetic array (fp32 or bf16 bit patterns) -> device tensor of that dtype."""
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).to(device)
+
+
+def dev64(a: np.ndarray, device="cuda") -> torch.Tensor:
+    """fp64/int array -> contiguous device tensor (numpy views such as U = L.T are not row-major)."""
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+def codes_in_quant_order(codes: np.ndarray, perm: np.ndarray) -> np.ndarray:
+    return codes[:, perm]
+
+
+def compare(res_gpu, ref: dict, W64: np.ndarray, bits: int, group: int, tau: float = TAU) -> dict:
+    """All gates for one layer. res_gpu: QuantResult (device); ref: the oracle's dict."""
+    codes = res_gpu.codes.cpu().numpy().astype(np.int64)
+    scales = res_gpu.scales.cpu().numpy().astype(np.float64)
+    g_idx = res_gpu.g_idx.cpu().numpy().astype(np.int64)
+    perm = ref["perm"]
+    agree = float(np.mean(codes == ref["codes"]))
+    # dequantize both with fp64 scales rounded as the GPU stores them (fp32)
+    Q_gpu = codes * scales[:, g_idx]
+    Q_ref = ref["Q"]
+    q_rel = float(np.linalg.norm(Q_gpu - Q_ref) / max(np.linalg.norm(Q_ref), 1e-300))
+    e_gpu = O.output_error(W64, Q_gpu, ref["S"])
+    e_ref = O.output_error(W64, Q_ref, ref["S"])
+    out_rel = abs(e_gpu - e_ref) / max(e_ref, 1e-300)
+    dist, _ = O.forced_replay(ref["W0"], ref["U"], bits, group, codes[:, perm])
+    excess = float(dist.max() - 0.5)
+    return dict(agree=agree, mismatches=int(np.sum(codes != ref["codes"])), q_rel=q_rel, out_rel=out_rel,
+                replay_excess=excess, e_gpu=e_gpu, e_ref=e_ref,
+                gidx_ok=bool(np.array_equal(g_idx, ref["g_idx"])))
+
+
+def assert_gates(m: dict, tau: float = TAU, q_gate: float = 1e-3):
+    assert m["gidx_ok"], m
+    assert m["agree"] >= 0.999, m
+    assert m["out_rel"] <= 0.01, m
+    assert m["replay_excess"] <= tau, m
+    assert m["q_rel"] <= q_gate, m
+
+
+def layer_inputs(cfg):
+    W = syn.gen_w(cfg)
+    X = syn.gen_x(cfg)
+    return W, X, O.to_f64(W, cfg.dtype), O.to_f64(X, cfg.dtype)
