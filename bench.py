@@ -1,0 +1,208 @@
+#!/usr/bin/env python3
+"""Benchmark of one GPTQ layer quantization on one MI355X.
+
+A step is one pass of the whole path on the q_proj workload (W 4096 x 4096 bf16, X 262144 x 4096 bf16 =
+128 segments x 2048 tokens, 4-bit per-row scales, damp 0.01): zero S, accumulate X^T X over all rows,
+prepare U, run the compensation loop. Inputs are resident in HBM before timing starts.
+Prints ONE JSON line (see the fields below). `--gpus N` with N > 1 exits: this path runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "ms per layer-quantize (4096², n=262k) + % MFMA/HBM roofline, at 1 GPU"
+PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA
+PEAK_FP64_TFLOPS = 78.6    # MI355X fp64 (vector = matrix rate)
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", default="q_proj", help="workload name (q_proj, up_gate, down, tiny, teacher)")
+    ap.add_argument("--factor", choices=["rechol", "reversed"], default="reversed")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-rows", type=int, default=16384)
+    ap.add_argument("--cpu-loop-rows", type=int, default=32)
+    return ap.parse_args()
+
+
+def cpu_baseline(cfg, W, X, sample_rows, loop_rows):
+    """The oracle as it stands, timed on this host on a bounded sample of the workload, scaled to one layer."""
+    from oracle import gptq_oracle as O
+
+    t_all = time.perf_counter()
+    rows = min(sample_rows, cfg.n)
+    X64 = O.to_f64(X[:rows], cfg.dtype)
+    t0 = time.perf_counter()
+    S, colsq, n = O.hessian_from_x(X64)
+    t_hess = (time.perf_counter() - t0) * (cfg.n / rows)
+    del X64
+    t0 = time.perf_counter()
+    H_p, perm, dead, lam = O.prepare(S, colsq, n, cfg.damp, cfg.act_order)
+    U = O.upper_factor_of_inverse(H_p)
+    t_factor = time.perf_counter() - t0
+    lr = min(loop_rows, cfg.out)
+    W64 = O.to_f64(W[:lr], cfg.dtype)
+    t0 = time.perf_counter()
+    W0 = O.start_weights(W64, perm, dead)
+    O.compensation_loop(W0, U, cfg.bits, cfg.group)
+    t_loop = (time.perf_counter() - t0) * (cfg.out / lr)
+    total_ms = (t_hess + t_factor + t_loop) * 1e3
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count()
+    return {
+        "value": round(total_ms, 1),
+        "unit": "ms",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": (f"numpy fp64 oracle: X^T X over {rows} of {cfg.n} rows (scaled x{cfg.n / rows:g}), "
+                   f"inv+cholesky at full in={cfg.d_in}, compensation loop on {lr} of {cfg.out} rows "
+                   f"(scaled x{cfg.out / lr:g}; the loop is numpy element-wise, one core); "
+                   f"measured {time.perf_counter() - t_all:.1f} s"),
+        "stages_ms": {"hessian": round(t_hess * 1e3, 1), "factor": round(t_factor * 1e3, 1),
+                      "loop": round(t_loop * 1e3, 1)},
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this GPTQ layer path runs on one GPU; --gpus {args.gpus} is not supported "
+              f"(rows of W and calibration tokens would shard across GPUs; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import post_weight_quantization_05_amd as G
+    import synthetic as syn
+
+    G.load()  # fails loudly when the HIP library is missing
+    cfg = syn.config_by_name(args.config)
+    flags = G.GPTQ_FACTOR_REVERSED if args.factor == "reversed" else G.GPTQ_FACTOR_INVERSE_RECHOL
+    t0 = time.perf_counter()
+    W = syn.gen_w(cfg)
+    X = syn.gen_x(cfg)
+    gen_s = time.perf_counter() - t0
+
+    def dev(a):
+        if cfg.dtype == "bf16":
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(a).cuda()
+
+    Wd, Xd = dev(W), dev(X)
+    torch.cuda.synchronize()
+    d, out = cfg.d_in, cfg.out
+    st = G.HessianState(d)
+    st.workspace(cfg.n, G.GPTQ_BF16 if cfg.dtype == "bf16" else G.GPTQ_F32)
+    U = torch.empty((d, d), dtype=torch.float64, device="cuda")
+    perm = torch.empty(d, dtype=torch.int32, device="cuda")
+    dead = torch.empty(d, dtype=torch.uint8, device="cuda")
+    qws = torch.empty(G.load().gptq_quantize_workspace_bytes(out, d), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    ev = {k: [] for k in ("zero", "hessian", "prepare", "quantize")}
+
+    def step(record):
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(5)] if record else None
+        if record:
+            marks[0].record(stream)
+        st.S.zero_()
+        st.colsq.zero_()
+        st.n_total = 0
+        if record:
+            marks[1].record(stream)
+        G.hessian_accumulate(Xd, st)
+        if record:
+            marks[2].record(stream)
+        G.prepare_chol(st.S, st.colsq, st.n_total, cfg.damp, cfg.act_order, flags, out=(U, perm, dead))
+        if record:
+            marks[3].record(stream)
+        res = G.quantize_layer(Wd, U, perm, dead, cfg.bits, cfg.group, ws=qws)
+        if record:
+            marks[4].record(stream)
+            for i, k in enumerate(("zero", "hessian", "prepare", "quantize")):
+                ev[k].append((marks[i], marks[i + 1]))
+        return res
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    t_start.record(stream)
+    wall0 = time.perf_counter()
+    for _ in range(args.steps):
+        res = step(True)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / args.steps
+    stage_ms = {k: float(np.mean([a.elapsed_time(b) for a, b in v])) for k, v in ev.items()}
+
+    # algorithmic work (lower triangle of X^T X, the two-step factor, the loop's multiply-adds)
+    n = cfg.n
+    hess_flops = n * d * (d + 1)
+    factor_flops = (2.0 / 3.0 if flags else 4.0 / 3.0) * d ** 3
+    loop_flops = out * d * (d - 1)
+    x_bytes = n * d * (2 if cfg.dtype == "bf16" else 4)
+    hess_ms = stage_ms["hessian"]
+    achieved = hess_flops / (hess_ms * 1e-3) / 1e12
+    bound_ms = (hess_flops / (PEAK_BF16_TFLOPS * 1e12) + factor_flops / (PEAK_FP64_TFLOPS * 1e12)
+                + loop_flops / (PEAK_FP64_TFLOPS * 1e12)) * 1e3
+    line = {
+        "metric": METRIC,
+        "value": round(ms_per_step, 4),
+        "unit": "ms",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 products, fp32 accumulation, fp64 after the Hessian",
+        "data": "synthetic (seeded; shapes and value structure of the workload)",
+        "config": {"workload": f"{cfg.name}: W {out}x{d} {cfg.dtype}, X {n}x{d} {cfg.dtype} "
+                               f"({cfg.n_segments} x 2048 tokens), {cfg.bits}-bit, group {cfg.group}, "
+                               f"act_order {cfg.act_order}, damp {cfg.damp}",
+                   "factor_route": args.factor},
+        "roofline": {
+            "kernel": "k_xtx_bf16 (Hessian X^T X, lower triangle)",
+            "bound": "mfma",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+            "algorithmic_per_launch": f"{hess_flops:.4e} flop (n*in*(in+1)), {x_bytes:.4e} B of X",
+            "launch_ms": round(hess_ms, 4),
+        },
+        "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+        "weights_per_s": round(out * d / (ms_per_step * 1e-3), 1),
+        "combined_bound_ms": round(bound_ms, 4),
+        "frac_of_combined_bound": round(bound_ms / ms_per_step, 4),
+        "wall_s_timed": round(wall, 3),
+        "gen_s": round(gen_s, 2),
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(cfg, W, X, args.cpu_sample_rows, args.cpu_loop_rows)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -78,12 +78,56 @@ __device__ __forceinline__ void sq_accum8(double* acc, uint4 v) {
   }
 }
 
+// Split-K completion: every (slice, tile) workgroup publishes its fp32 partial (release fence, then a
+// per-tile counter); the workgroup that arrives last sums the slices of that tile in slice order in fp64
+// and adds them to S's lower triangle (and, for diagonal tiles, the column sums to colsq). The order of
+// the sum does not depend on which workgroup arrives last, so results are bitwise reproducible.
+template <int TILE>
+__device__ __forceinline__ void finish_tile(int t, int I, int J, bool diag, int d, int n_tiles, int splits,
+                                            const float* __restrict__ part, const double* __restrict__ colsq_part,
+                                            int colsq_stride, unsigned* __restrict__ counters,
+                                            double* __restrict__ S, double* __restrict__ colsq, int* s_last) {
+  const int tid = threadIdx.x;
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) *s_last = (atomicAdd(&counters[t], 1u) == (unsigned)(splits - 1)) ? 1 : 0;
+  __syncthreads();
+  if (!*s_last) return;
+  __threadfence();
+  const int64_t tsz = (int64_t)TILE * TILE;
+  const int64_t sstride = (int64_t)n_tiles * tsz;
+  const float* p0 = part + (int64_t)t * tsz;
+  for (int i = 0; i < TILE; ++i) {
+    const int gi = I * TILE + i;
+    if (gi >= d) break;
+    for (int j = tid; j < TILE; j += blockDim.x) {
+      const int gj = J * TILE + j;
+      if (gj > gi || gj >= d) continue;
+      const float* p = p0 + (int64_t)i * TILE + j;
+      double sum = 0.0;
+      for (int sidx = 0; sidx < splits; ++sidx) sum += (double)p[sidx * sstride];
+      S[(int64_t)gi * d + gj] += sum;
+    }
+  }
+  if (diag) {
+    for (int c = tid; c < TILE; c += blockDim.x) {
+      const int gc = I * TILE + c;
+      if (gc >= d) break;
+      double sum = 0.0;
+      for (int sidx = 0; sidx < splits; ++sidx) sum += colsq_part[(int64_t)sidx * colsq_stride + gc];
+      colsq[gc] += sum;
+    }
+  }
+}
+
 template <bool VEC>
 __global__ __launch_bounds__(256, 1) void k_xtx_bf16(const uint16_t* __restrict__ X, int64_t ld, int64_t n_rows,
-                                                     int d, int n_tiles, int64_t rps, int remap,
+                                                     int d, int n_tiles, int64_t rps, int remap, int splits,
                                                      float* __restrict__ part, double* __restrict__ colsq_part,
-                                                     int colsq_stride) {
+                                                     int colsq_stride, unsigned* __restrict__ counters,
+                                                     double* __restrict__ S, double* __restrict__ colsq) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][BK][BROW];
+  __shared__ int s_last;
 
   const int G = gridDim.x;
   const int b = blockIdx.x;
@@ -210,15 +254,19 @@ __global__ __launch_bounds__(256, 1) void k_xtx_bf16(const uint16_t* __restrict_
     for (int rg = 0; rg < 8; ++rg) sum += red[rg * BT + tid];
     colsq_part[(int64_t)split * colsq_stride + colA + tid] = sum;
   }
+  finish_tile<BT>(t, I, J, diag, d, n_tiles, splits, part, colsq_part, colsq_stride, counters, S, colsq, &s_last);
 }
 
 // ---------------------------------------------------------------------------------------------------
 // fp32 X
 // ---------------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256, 1) void k_xtx_f32(const float* __restrict__ X, int64_t ld, int64_t n_rows, int d,
-                                                    int n_tiles, int64_t rps, int remap, float* __restrict__ part,
-                                                    double* __restrict__ colsq_part, int colsq_stride) {
+                                                    int n_tiles, int64_t rps, int remap, int splits,
+                                                    float* __restrict__ part, double* __restrict__ colsq_part,
+                                                    int colsq_stride, unsigned* __restrict__ counters,
+                                                    double* __restrict__ S, double* __restrict__ colsq) {
   __shared__ __attribute__((aligned(16))) float lds[2][2][FK][FROW];
+  __shared__ int s_last;
   const int G = gridDim.x;
   const int b = blockIdx.x;
   const int L = remap ? (b % 8) * (G / 8) + b / 8 : b;
@@ -324,36 +372,12 @@ __global__ __launch_bounds__(256, 1) void k_xtx_f32(const float* __restrict__ X,
       colsq_part[(int64_t)split * colsq_stride + colA + tid] = sum;
     }
   }
+  finish_tile<FT>(t, I, J, diag, d, n_tiles, splits, part, colsq_part, colsq_stride, counters, S, colsq, &s_last);
 }
 
-// S[gi][gj] += sum over slices (fixed order) of the fp32 partials, lower triangle only.
-// grid = n_tiles * tile rows; block = tile threads (one per column of the tile row).
-__global__ __launch_bounds__(256) void k_xtx_combine(const float* __restrict__ part, int tile, int n_tiles, int splits,
-                                                     int d, double* __restrict__ S) {
-  const int t = blockIdx.x / tile;
-  const int i = blockIdx.x - t * tile;
-  int I, J;
-  tile_coords(t, I, J);
-  const int gi = I * tile + i;
-  if (gi >= d) return;
-  const int64_t tsz = (int64_t)tile * tile;
-  for (int j = threadIdx.x; j < tile; j += blockDim.x) {
-    const int gj = J * tile + j;
-    if (gj > gi || gj >= d) continue;
-    const float* p = part + (int64_t)t * tsz + (int64_t)i * tile + j;
-    double sum = 0.0;
-    for (int sidx = 0; sidx < splits; ++sidx) sum += (double)p[(int64_t)sidx * n_tiles * tsz];
-    S[(int64_t)gi * d + gj] += sum;
-  }
-}
-
-__global__ void k_colsq_combine(const double* __restrict__ cpart, int stride, int splits, int d,
-                                double* __restrict__ colsq) {
-  const int c = blockIdx.x * blockDim.x + threadIdx.x;
-  if (c >= d) return;
-  double sum = 0.0;
-  for (int s = 0; s < splits; ++s) sum += cpart[(int64_t)s * stride + c];
-  colsq[c] += sum;
+__global__ void k_zero_counters(unsigned* __restrict__ c, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) c[i] = 0u;
 }
 
 }  // namespace
@@ -386,7 +410,8 @@ HessianPlan hessian_plan(int64_t n_rows, int64_t in, int dtype) {
   p.splits = (int)ceil_div(n_rows, p.rows_per_split);
   p.part_bytes = align_up((size_t)p.splits * p.n_tiles * p.tile * p.tile * sizeof(float), 256);
   p.colsq_part_bytes = align_up((size_t)p.splits * p.n_tb * p.tile * sizeof(double), 256);
-  p.total_bytes = p.part_bytes + p.colsq_part_bytes;
+  p.counter_bytes = align_up((size_t)p.n_tiles * sizeof(unsigned), 256);
+  p.total_bytes = p.part_bytes + p.colsq_part_bytes + p.counter_bytes;
   p.ld = 0;
   return p;
 }
@@ -395,29 +420,29 @@ hipError_t hessian_launch(const HessianPlan& p, const void* X, double* S, double
                           hipStream_t stream) {
   float* part = reinterpret_cast<float*>(ws);
   double* cpart = reinterpret_cast<double*>(reinterpret_cast<char*>(ws) + p.part_bytes);
+  unsigned* counters = reinterpret_cast<unsigned*>(reinterpret_cast<char*>(ws) + p.part_bytes + p.colsq_part_bytes);
   const int grid = p.splits * p.n_tiles;
   const int remap = (grid % 8 == 0) ? 1 : 0;
   const int cstride = p.n_tb * p.tile;
+  // counters start at zero on every call (a small fill kernel, safe under stream capture)
+  hipLaunchKernelGGL(k_zero_counters, dim3((unsigned)ceil_div(p.n_tiles, 256)), dim3(256), 0, stream, counters,
+                     p.n_tiles);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   if (p.dtype == GPTQ_BF16) {
     const bool vec = (p.ld % 8 == 0) && (p.in % 8 == 0) && ((reinterpret_cast<uintptr_t>(X) & 15) == 0);
     if (vec)
       hipLaunchKernelGGL(k_xtx_bf16<true>, dim3(grid), dim3(256), 0, stream, (const uint16_t*)X, p.ld, p.n_rows,
-                         (int)p.in, p.n_tiles, p.rows_per_split, remap, part, cpart, cstride);
+                         (int)p.in, p.n_tiles, p.rows_per_split, remap, p.splits, part, cpart, cstride, counters, S,
+                         colsq);
     else
       hipLaunchKernelGGL(k_xtx_bf16<false>, dim3(grid), dim3(256), 0, stream, (const uint16_t*)X, p.ld, p.n_rows,
-                         (int)p.in, p.n_tiles, p.rows_per_split, remap, part, cpart, cstride);
+                         (int)p.in, p.n_tiles, p.rows_per_split, remap, p.splits, part, cpart, cstride, counters, S,
+                         colsq);
   } else {
     hipLaunchKernelGGL(k_xtx_f32, dim3(grid), dim3(256), 0, stream, (const float*)X, p.ld, p.n_rows, (int)p.in,
-                       p.n_tiles, p.rows_per_split, remap, part, cpart, cstride);
+                       p.n_tiles, p.rows_per_split, remap, p.splits, part, cpart, cstride, counters, S, colsq);
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_xtx_combine, dim3(p.n_tiles * p.tile), dim3(256), 0, stream, part, p.tile, p.n_tiles,
-                     p.splits, (int)p.in, S);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_colsq_combine, dim3((unsigned)ceil_div(p.in, 256)), dim3(256), 0, stream, cpart, cstride,
-                     p.splits, (int)p.in, colsq);
   return hipGetLastError();
 }
 
