@@ -17,6 +17,8 @@
 //  panel / SYRK / triangular-inverse levels / H^-1 = L^-T L^-1 use the fp64 MFMA GEMM core (dgemm.hip).
 // Routes (flags): INVERSE_RECHOL = potrf, trtri, lauum, potrf, transpose (the guide's order);
 // REVERSED = potrf and trtri of J H J, then U = J L^-1 J (same unique U, half the work).
+#include <type_traits>
+
 #include "common.h"
 #include "dgemm.h"
 
@@ -25,6 +27,16 @@ namespace gptq {
 namespace {
 
 constexpr int NB = 64;
+
+// compile-time loop (the 64-step elimination loops are too large for the unroller, and a runtime index
+// into the register-resident row would move it to scratch memory)
+template <int K, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (K < N) {
+    f(std::integral_constant<int, K>{});
+    static_for<K + 1, N>(f);
+  }
+}
 
 __device__ __forceinline__ double readlane_d(double v, int l) {
   const long long x = __double_as_longlong(v);
@@ -126,63 +138,119 @@ __global__ __launch_bounds__(256) void k_gather(const double* __restrict__ S, co
 }
 
 // Factor the diagonal block kb of A in place (lower, zeros above) and write its inverse to Dinv[kb].
-// One wave; lane i holds row i of the block in registers. Rows/columns past the matrix edge act as the
-// identity.
+// One wave. Cholesky: lane i holds row i of the block in registers (right-looking: after pivot k every
+// lane updates its own entries j > k with column k, which goes through LDS). Inverse: lane j holds
+// column j of L^-1 and eliminates right-looking as well (c[i] -= L[i][k] c[k] for i > k). In both
+// phases a step's LDS values are read in chunks of 8 with three chunks in flight ahead of the
+// multiply-adds that use them, so a step waits for one LDS round trip, not one per chunk.
+// Rows/columns past the matrix edge act as the identity.
+template <int K>
+struct ChunkSpan {
+  static constexpr int first = ((K + 1) & ~7);                // first chunk start with entries > K
+  static constexpr int count = (NB - first) / 8;               // chunks of 8 from `first` to NB
+};
+
 __global__ __launch_bounds__(64) void k_potrf_diag(double* __restrict__ A, int64_t lda, int d, int kb,
                                                    double* __restrict__ Dinv, unsigned* status) {
   __shared__ double col[NB];
   __shared__ double Ls[NB][NB + 1];
-  __shared__ double dinv[NB];
+  __shared__ double rdg[NB];
   const int o = kb * NB;
   const int m = min(NB, d - o);
   const int i = threadIdx.x;
-  double r[NB];
-#pragma unroll
-  for (int j = 0; j < NB; ++j) {
-    double v = (i == j) ? 1.0 : 0.0;
-    if (i < m && j < m && j <= i) v = A[(int64_t)(o + i) * lda + o + j];
-    r[j] = v;
-  }
   unsigned flags = 0;
+  {
+    double r[NB];
 #pragma unroll
-  for (int k = 0; k < NB; ++k) {
-    double piv = readlane_d(r[k], k);
-    if (!(piv > 0.0)) {
-      flags |= isfinite(piv) ? DEV_STATUS_NOT_SPD : DEV_STATUS_NONFINITE;
-      piv = 1.0;
-    } else if (!isfinite(piv)) {
-      flags |= DEV_STATUS_NONFINITE;
-      piv = 1.0;
+    for (int j = 0; j < NB; ++j) {
+      double v = (i == j) ? 1.0 : 0.0;
+      if (i < m && j < m && j <= i) v = A[(int64_t)(o + i) * lda + o + j];
+      r[j] = v;
     }
-    const double lkk = sqrt(piv);
-    const double inv = 1.0 / lkk;
-    r[k] = (i == k) ? lkk : r[k] * inv;
-    col[i] = r[k];
-    __syncthreads();
+    static_for<0, NB>([&](auto kc) {
+      constexpr int k = decltype(kc)::value;
+      double piv = readlane_d(r[k], k);
+      if (!(piv > 0.0)) {
+        flags |= isfinite(piv) ? DEV_STATUS_NOT_SPD : DEV_STATUS_NONFINITE;
+        piv = 1.0;
+      } else if (!isfinite(piv)) {
+        flags |= DEV_STATUS_NONFINITE;
+        piv = 1.0;
+      }
+      const double lkk = sqrt(piv);
+      const double inv = 1.0 / lkk;
+      r[k] = (i == k) ? lkk : r[k] * inv;
+      if (i == k) rdg[k] = inv;  // 1 / L[k][k] for the inverse
+      if constexpr (k + 1 < NB) {
+        col[i] = r[k];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        constexpr int F = ChunkSpan<k>::first, NC = ChunkSpan<k>::count;
+        double buf[4][8];
+        auto rd = [&](auto cc) {
+          constexpr int c = decltype(cc)::value;
 #pragma unroll
-    for (int j = k + 1; j < NB; ++j) r[j] = fma(-r[k], col[j], r[j]);
-    __syncthreads();
+          for (int q = 0; q < 8; ++q) buf[c & 3][q] = col[F + 8 * c + q];
+        };
+        static_for<0, (NC < 3 ? NC : 3)>(rd);
+        static_for<0, NC>([&](auto cc) {
+          constexpr int c = decltype(cc)::value;
+          if constexpr (c + 3 < NC) rd(std::integral_constant<int, c + 3>{});
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            constexpr int dummy = 0;
+            (void)dummy;
+            const int jj = F + 8 * c + q;
+            if (jj > k) r[F + 8 * c + q] = fma(-r[k], buf[c & 3][q], r[F + 8 * c + q]);
+          }
+        });
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int j = k + 1; j < NB; ++j) asm volatile("" : "+v"(r[j]));
+      }
+    });
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const double v = (j <= i) ? r[j] : 0.0;
+      Ls[i][j] = v;
+      if (i < m && j < m) A[(int64_t)(o + i) * lda + o + j] = v;
+    }
   }
   if (flags && i == 0) atomicOr(status, flags);
-  // store L (lower) and keep it in LDS for the inverse
-#pragma unroll
-  for (int j = 0; j < NB; ++j) {
-    const double v = (j <= i) ? r[j] : 0.0;
-    Ls[i][j] = v;
-    if (i < m && j < m) A[(int64_t)(o + i) * lda + o + j] = v;
-  }
-  dinv[i] = 1.0 / r[i];
   __syncthreads();
-  // inverse: lane j computes column j of L^-1 by forward substitution
+  // inverse: lane j holds column j of L^-1 (starts as e_j), right-looking elimination
   const int jc = i;
   double c[NB];
 #pragma unroll
-  for (int k = 0; k < NB; ++k) {
-    double s = (k == jc) ? 1.0 : 0.0;
+  for (int k = 0; k < NB; ++k) c[k] = (k == jc) ? 1.0 : 0.0;
+  static_for<0, NB>([&](auto kc) {
+    constexpr int k = decltype(kc)::value;
+    c[k] = c[k] * rdg[k];
+    if constexpr (k + 1 < NB) {
+      constexpr int F = ChunkSpan<k>::first, NC = ChunkSpan<k>::count;
+      double buf[4][8];
+      auto rd = [&](auto cc) {
+        constexpr int cb = decltype(cc)::value;
 #pragma unroll
-    for (int q = 0; q < k; ++q) s = fma(-Ls[k][q], c[q], s);
-    c[k] = s * dinv[k];
-  }
+        for (int q = 0; q < 8; ++q) buf[cb & 3][q] = Ls[F + 8 * cb + q][k];
+      };
+      static_for<0, (NC < 3 ? NC : 3)>(rd);
+      static_for<0, NC>([&](auto cc) {
+        constexpr int cb = decltype(cc)::value;
+        if constexpr (cb + 3 < NC) rd(std::integral_constant<int, cb + 3>{});
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const int r2 = F + 8 * cb + q;
+          if (r2 > k) c[F + 8 * cb + q] = fma(-buf[cb & 3][q], c[k], c[F + 8 * cb + q]);
+        }
+      });
+#pragma unroll
+      for (int j = k; j < NB; ++j) asm volatile("" : "+v"(c[j]));
+    }
+  });
   double* D = Dinv + (int64_t)kb * NB * NB;
 #pragma unroll
   for (int k = 0; k < NB; ++k) D[k * NB + jc] = (k < m && jc < m) ? c[k] : ((k == jc) ? 1.0 : 0.0);

@@ -258,6 +258,252 @@ __global__ __launch_bounds__(256, 1) void k_xtx_bf16(const uint16_t* __restrict_
 }
 
 // ---------------------------------------------------------------------------------------------------
+// bf16 X, 16-byte aligned rows: direct-to-LDS pipeline
+//
+// Each 32-row stage of a 256-column operand block is fetched with buffer_load_dwordx4 ... lds (no staging
+// registers) into one of NSTG LDS stage buffers, NSTG - 1 stages ahead of the MFMAs. One DMA instruction
+// moves 1 KB = two rows; rows are stored in pairs of 1152 B (1 KB + 128 B pad) and the odd row of a pair
+// has its 16-byte chunks XOR-swizzled by 4, so the 4 x 64 B that the transposing reads of 32 lanes touch
+// fall on 64 distinct banks. Rows past the slice end and columns past `in` are outside the buffer range
+// and arrive as zeros. Stage buffers are separate LDS arrays addressed with compile-time indices, so the
+// compiler can tell a DMA into one stage from reads of another and only the explicit vmcnt waits order
+// them.
+// ---------------------------------------------------------------------------------------------------
+constexpr int NSTG = 4;
+constexpr int PAIR_B = 1152;
+constexpr int OP_B = (BK / 2) * PAIR_B;  // 18432 B per operand per stage
+constexpr int STG_B = 2 * OP_B;          // 36864 B per stage
+constexpr int XWAVES = 8;                // waves per workgroup: 2 (M) x 4 (N), each a 128 x 64 block
+constexpr int DMA_PAIRS = (BK / 2) / XWAVES;  // row pairs per wave per operand per stage
+
+__shared__ __attribute__((aligned(1024))) uint8_t g_stage0[STG_B];
+__shared__ __attribute__((aligned(1024))) uint8_t g_stage1[STG_B];
+__shared__ __attribute__((aligned(1024))) uint8_t g_stage2[STG_B];
+__shared__ __attribute__((aligned(1024))) uint8_t g_stage3[STG_B];
+
+template <int S>
+__device__ __forceinline__ uint8_t* stage_buf() {
+  if constexpr (S == 0) return g_stage0;
+  else if constexpr (S == 1) return g_stage1;
+  else if constexpr (S == 2) return g_stage2;
+  else return g_stage3;
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// byte offset of (row k, 8-element chunk q) inside one operand's stage buffer
+__device__ __forceinline__ int stage_off(int k, int q) {
+  return (k >> 1) * PAIR_B + (k & 1) * 512 + ((q ^ ((k & 1) << 2)) << 4);
+}
+
+// s_waitcnt with vmcnt = N (expcnt and lgkmcnt left unconstrained)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+typedef __attribute__((ext_vector_type(4))) int i32x4;
+
+struct DmaCtx {
+  i32x4 rsrc;         // buffer resource of this workgroup's row slice (out-of-range reads return 0)
+  int64_t row_bytes;  // ld * 2
+  int colA, colB, d;
+  int wave, lane;
+};
+
+// buffer_load_dwordx4 ... lds: 64 lanes x 16 B to LDS[m0 + lane * 16]. Written as inline asm so that the
+// compiler does not add its own (conservative, vmcnt(0)) waits before every LDS read that follows; the
+// stage pipeline orders the DMA with explicit vmcnt waits and barriers, and the main loop issues no other
+// vector-memory instruction.
+__device__ __forceinline__ void dma16(const i32x4& rsrc, uint32_t lds_addr, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+
+// Issue the DMA of stage kt (32 rows) of operand block `col0` into operand slot `op` of stage buffer S.
+template <int S>
+__device__ __forceinline__ void dma_stage(const DmaCtx& c, int kt, int op, int col0) {
+  const uint32_t base = (uint32_t)(uintptr_t)(stage_buf<S>() + op * OP_B);
+  const int half = c.lane >> 5;
+  const int q = (c.lane & 31) ^ (half << 2);
+  const int col = col0 + 8 * q;
+  const bool col_ok = col < c.d;
+#pragma unroll
+  for (int pp = 0; pp < DMA_PAIRS; ++pp) {
+    const int p = c.wave * DMA_PAIRS + pp;    // row pair within the stage
+    const int row = kt * BK + 2 * p + half;   // row within the slice
+    const uint32_t voff = col_ok ? (uint32_t)(row * c.row_bytes + col * 2) : 0x80000000u;
+    dma16(c.rsrc, __builtin_amdgcn_readfirstlane(base + p * PAIR_B), voff);
+  }
+}
+
+// load the 2 x 4 bf16 of an MFMA operand fragment (32 x 16 block starting at column c0, k-rows k16..k16+15)
+__device__ __forceinline__ bf16x8 frag_tr(const uint8_t* opbase, int k16, int c0, int g, int s) {
+  const int k = k16 + 8 * (g >> 1) + (s >> 2);
+  const int c = c0 + 16 * (g & 1) + (s & 3) * 4;
+  const int off = stage_off(k, c >> 3) + (c & 7) * 2;
+  i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(opbase + off));
+  i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(opbase + off + 2 * PAIR_B));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// One 32-row stage: wait for this stage's DMA, barrier, start the DMA of the stage NSTG - 1 ahead (issued
+// unconditionally: past the slice end its offsets are out of range and it fetches zeros into a stage
+// buffer that is never read, which keeps the vmcnt bookkeeping uniform), then 2 x 8 MFMAs per wave with
+// the second half's fragments in flight while the first half's MFMAs run. Two waves share each SIMD, so
+// one wave's MFMAs cover the other's barrier and LDS waits. In diagonal tiles the two waves whose block
+// lies above the diagonal add the fp64 squares of the stage instead (4 columns x 16 rows per lane).
+template <bool DIAG, int S>
+__device__ __forceinline__ void xtx_stage(const DmaCtx& c, int kt, f32x16 (&acc)[4][2], double (&csq)[4], int wm,
+                                          int wn, bool active) {
+  constexpr int PER = (DIAG ? 1 : 2) * DMA_PAIRS;  // DMA instructions per wave per stage
+  wait_vmcnt<(NSTG - 2) * PER>();
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  {
+    constexpr int SN = (S + NSTG - 1) % NSTG;
+    dma_stage<SN>(c, kt + NSTG - 1, 0, c.colA);
+    if (!DIAG) dma_stage<SN>(c, kt + NSTG - 1, 1, c.colB);
+  }
+  const uint8_t* A = stage_buf<S>();
+  const uint8_t* B = DIAG ? A : A + OP_B;
+  const int g = c.lane >> 4, s = c.lane & 15;
+  if (active) {
+    bf16x8 fa0[4], fb0[2], fa1[4], fb1[2];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) fa0[mb] = frag_tr(A, 0, wm * 128 + mb * 32, g, s);
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) fb0[nb] = frag_tr(B, 0, wn * 64 + nb * 32, g, s);
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) fa1[mb] = frag_tr(A, 16, wm * 128 + mb * 32, g, s);
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) fb1[nb] = frag_tr(B, 16, wn * 64 + nb * 32, g, s);
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa0[mb], fb0[nb], acc[mb][nb], 0, 0, 0);
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa1[mb], fb1[nb], acc[mb][nb], 0, 0, 0);
+  } else if (DIAG) {
+    const int cc = c.lane * 4;              // columns cc..cc+3
+    const int kr = (wn - 2) * 16;           // rows kr..kr+15 of the stage (waves (0,2) and (0,3))
+#pragma unroll 4
+    for (int k = 0; k < 16; ++k) {
+      const uint2 v = *reinterpret_cast<const uint2*>(A + stage_off(kr + k, cc >> 3) + (cc & 7) * 2);
+      const double x0 = (double)__uint_as_float(v.x << 16), x1 = (double)__uint_as_float(v.x & 0xFFFF0000u);
+      const double x2 = (double)__uint_as_float(v.y << 16), x3 = (double)__uint_as_float(v.y & 0xFFFF0000u);
+      csq[0] = fma(x0, x0, csq[0]);
+      csq[1] = fma(x1, x1, csq[1]);
+      csq[2] = fma(x2, x2, csq[2]);
+      csq[3] = fma(x3, x3, csq[3]);
+    }
+  }
+}
+
+template <bool DIAG>
+__device__ __forceinline__ void xtx_dma_body(const DmaCtx& c, int nk, f32x16 (&acc)[4][2], double (&csq)[4], int wm,
+                                             int wn, bool active) {
+  // prologue: stages 0 .. NSTG-2 in flight (stages past the slice fetch zeros)
+  dma_stage<0>(c, 0, 0, c.colA);
+  if (!DIAG) dma_stage<0>(c, 0, 1, c.colB);
+  dma_stage<1>(c, 1, 0, c.colA);
+  if (!DIAG) dma_stage<1>(c, 1, 1, c.colB);
+  dma_stage<2>(c, 2, 0, c.colA);
+  if (!DIAG) dma_stage<2>(c, 2, 1, c.colB);
+  for (int kt = 0; kt < nk; kt += NSTG) {
+    xtx_stage<DIAG, 0>(c, kt, acc, csq, wm, wn, active);
+    if (kt + 1 >= nk) break;
+    xtx_stage<DIAG, 1>(c, kt + 1, acc, csq, wm, wn, active);
+    if (kt + 2 >= nk) break;
+    xtx_stage<DIAG, 2>(c, kt + 2, acc, csq, wm, wn, active);
+    if (kt + 3 >= nk) break;
+    xtx_stage<DIAG, 3>(c, kt + 3, acc, csq, wm, wn, active);
+  }
+  wait_vmcnt<0>();  // no DMA may still be writing LDS when the workgroup moves on
+  __builtin_amdgcn_s_barrier();
+}
+
+__global__ __launch_bounds__(512, 1) void k_xtx_bf16_dma(const uint16_t* __restrict__ X, int64_t ld, int64_t n_rows,
+                                                         int d, int n_tiles, int64_t rps, int remap, int splits,
+                                                         float* __restrict__ part, double* __restrict__ colsq_part,
+                                                         int colsq_stride, unsigned* __restrict__ counters,
+                                                         double* __restrict__ S, double* __restrict__ colsq) {
+  __shared__ int s_last;
+  const int G = gridDim.x;
+  const int b = blockIdx.x;
+  const int L = remap ? (b % 8) * (G / 8) + b / 8 : b;
+  const int split = L / n_tiles;
+  const int t = L - split * n_tiles;
+  int I, J;
+  tile_coords(t, I, J);
+  const bool diag = (I == J);
+  const int64_t r0 = (int64_t)split * rps;
+  const int64_t r1 = min(n_rows, r0 + rps);
+  const int nk = (int)((r1 - r0 + BK - 1) / BK);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 2, wn = wave & 3;  // 2 x 4 waves of 128 x 64
+  const bool active = !(diag && wm == 0 && wn >= 2);  // blocks above the diagonal of a diagonal tile
+
+  DmaCtx c;
+  {
+    const uint64_t addr = (uint64_t)(uintptr_t)(X + r0 * ld);
+    c.rsrc = (i32x4){__builtin_amdgcn_readfirstlane((int)(uint32_t)addr),
+                     __builtin_amdgcn_readfirstlane((int)(uint32_t)(addr >> 32) & 0xFFFF),
+                     __builtin_amdgcn_readfirstlane((int)((r1 - r0) * ld * 2)), 0x00020000};
+  }
+  c.row_bytes = ld * 2;
+  c.colA = I * BT;
+  c.colB = J * BT;
+  c.d = d;
+  c.wave = wave;
+  c.lane = lane;
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mb][nb][r] = 0.0f;
+  double csq[4] = {0.0, 0.0, 0.0, 0.0};
+
+  if (diag) xtx_dma_body<true>(c, nk, acc, csq, wm, wn, active);
+  else xtx_dma_body<false>(c, nk, acc, csq, wm, wn, active);
+
+  if (active) {
+    float* dst = part + ((int64_t)split * n_tiles + t) * (BT * BT);
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int i = wm * 128 + mb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          const int j = wn * 64 + nb * 32 + (lane & 31);
+          dst[i * BT + j] = acc[mb][nb][r];
+        }
+  }
+  if (diag) {
+    // the two column-sum waves hold rows 0..15 and 16..31 of every stage; add them in a fixed order
+    double* red = reinterpret_cast<double*>(g_stage0);  // 2 x 256 doubles; the DMA ring is drained
+    if (!active) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) red[(wn - 2) * 256 + lane * 4 + q] = csq[q];
+    }
+    __syncthreads();
+    if (tid < BT) colsq_part[(int64_t)split * colsq_stride + c.colA + tid] = red[tid] + red[256 + tid];
+  }
+  finish_tile<BT>(t, I, J, diag, d, n_tiles, splits, part, colsq_part, colsq_stride, counters, S, colsq, &s_last);
+}
+
+// ---------------------------------------------------------------------------------------------------
 // fp32 X
 // ---------------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256, 1) void k_xtx_f32(const float* __restrict__ X, int64_t ld, int64_t n_rows, int d,
@@ -431,7 +677,12 @@ hipError_t hessian_launch(const HessianPlan& p, const void* X, double* S, double
   if (e != hipSuccess) return e;
   if (p.dtype == GPTQ_BF16) {
     const bool vec = (p.ld % 8 == 0) && (p.in % 8 == 0) && ((reinterpret_cast<uintptr_t>(X) & 15) == 0);
-    if (vec)
+    const bool dma = vec && (p.rows_per_split * p.ld * 2 < ((int64_t)1 << 31));
+    if (dma)
+      hipLaunchKernelGGL(k_xtx_bf16_dma, dim3(grid), dim3(512), 0, stream, (const uint16_t*)X, p.ld, p.n_rows,
+                         (int)p.in, p.n_tiles, p.rows_per_split, remap, p.splits, part, cpart, cstride, counters, S,
+                         colsq);
+    else if (vec)
       hipLaunchKernelGGL(k_xtx_bf16<true>, dim3(grid), dim3(256), 0, stream, (const uint16_t*)X, p.ld, p.n_rows,
                          (int)p.in, p.n_tiles, p.rows_per_split, remap, p.splits, part, cpart, cstride, counters, S,
                          colsq);

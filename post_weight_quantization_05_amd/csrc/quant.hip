@@ -70,6 +70,15 @@ __device__ __forceinline__ double sum16(double v) {
   return v;
 }
 
+// a / b correctly rounded from y = RN(1 / b): q = RN(a y), r = a - b q (exact with an FMA),
+// RN(q + r y) = RN(a / b) (Markstein's theorem; finite normal operands, no overflow or underflow).
+// The same quotient as an IEEE division, in three dependent operations.
+__device__ __forceinline__ double div_rn(double a, double b, double y) {
+  const double q = a * y;
+  const double r = fma(-b, q, a);
+  return fma(r, y, q);
+}
+
 template <typename T>
 __device__ __forceinline__ double to_f64(T v);
 template <>
@@ -127,9 +136,21 @@ __global__ __launch_bounds__(256) void k_panel(double* __restrict__ Wq, int out,
   __shared__ int pidx[PW];
   const int tid = threadIdx.x;
   const int pw = min(PW, in - b0);
-  for (int e = tid; e < PW * PW; e += 256) {
-    const int a = e / PW, b = e % PW;
-    Us[a][b] = (a < pw && b < pw && b >= a) ? U[(int64_t)(b0 + a) * in + b0 + b] : 0.0;
+  // U panel block: loads are issued in batches of 16 per thread before they are stored to LDS
+#pragma unroll
+  for (int q0 = 0; q0 < PW * PW / 256; q0 += 16) {
+    double v[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int e = tid + 256 * (q0 + q);
+      const int a = e / PW, b = e % PW;
+      v[q] = (a < pw && b < pw && b >= a) ? U[(int64_t)(b0 + a) * in + b0 + b] : 0.0;
+    }
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int e = tid + 256 * (q0 + q);
+      Us[e / PW][e % PW] = v[q];
+    }
   }
   for (int a = tid; a < PW; a += 256) {
     rdiag[a] = (a < pw) ? 1.0 / U[(int64_t)(b0 + a) * in + b0 + a] : 0.0;
@@ -149,6 +170,7 @@ __global__ __launch_bounds__(256) void k_panel(double* __restrict__ Wq, int out,
   }
 
   double s = 1.0;
+  double sy = 1.0;  // RN(1 / s)
   if (!INPANEL) {
     if (group != 0 && b0 % group == 0) {
       const int glen = min(group, in - b0);
@@ -164,6 +186,7 @@ __global__ __launch_bounds__(256) void k_panel(double* __restrict__ Wq, int out,
     } else {
       s = rok ? scale_row[r] : 1.0;
     }
+    sy = 1.0 / s;
   }
 
   int code_m[8];
@@ -176,10 +199,12 @@ __global__ __launch_bounds__(256) void k_panel(double* __restrict__ Wq, int out,
 
 #pragma unroll
   for (int jm = 0; jm < 8; ++jm) {
+    // steps past the panel edge (j >= pw) need no guard: there w = 0, U = 0 and 1/U = 0, so they
+    // change nothing and their codes are never stored
     static_for<0, 16>([&](auto jlc) {
       constexpr int jl = decltype(jlc)::value;
       const int j = jm * 16 + jl;
-      if (j < pw) {
+      {
         if (INPANEL && (j % group) == 0) {
           double lm = 0.0;
 #pragma unroll
@@ -189,12 +214,13 @@ __global__ __launch_bounds__(256) void k_panel(double* __restrict__ Wq, int out,
           }
           lm = max16(lm);
           s = fmax(lm, SCALE_FLOOR) / qmax;
-          if (rok && c == 0) scales[(int64_t)r * n_groups + (b0 + j) / group] = (float)s;
+          sy = 1.0 / s;
+          if (rok && c == 0 && j < pw) scales[(int64_t)r * n_groups + (b0 + j) / group] = (float)s;
         }
         const double wj = bcast16<jl>(w[jm]);
         // q = c * scale and err = (w - q) / U[j][j] with the rounding steps of the definition (no fused
         // multiply-add): a weight that sits exactly on the grid leaves err = 0
-        const double cq = fmin(fmax(rint(wj / s), -qmax), qmax);
+        const double cq = fmin(fmax(rint(div_rn(wj, s, sy)), -qmax), qmax);
         const double e = __dmul_rn(__dsub_rn(wj, __dmul_rn(cq, s)), rdiag[j]);
         if (c == jl) {
           code_m[jm] = (int)cq;

@@ -75,7 +75,8 @@ def test_hessian_streaming_determinism_and_strided_rows():
     d = G.HessianState(cfg.d_in)
     G.hessian_accumulate(big[:, 1:1 + cfg.d_in], d)
     torch.cuda.synchronize()
-    assert torch.equal(d.colsq, a.colsq)
+    # the strided rows take the generic kernel, which sums the squares in another order
+    torch.testing.assert_close(d.colsq, a.colsq, rtol=1e-14, atol=0)
     S2 = d.S.cpu().numpy()
     assert np.linalg.norm((S2 - S_ref)[low]) / np.linalg.norm(S_ref[low]) <= 1e-6
 
