@@ -35,6 +35,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-rows", type=int, default=16384)
     ap.add_argument("--cpu-loop-rows", type=int, default=32)
+    ap.add_argument("--mode", choices=["layer", "hessian", "copy"], default="layer",
+                    help="layer: the timed benchmark; hessian: only the accumulate calls (for counter "
+                         "passes); copy: a plain 1 GiB device copy (calibrates FETCH_SIZE/WRITE_SIZE)")
     return ap.parse_args()
 
 
@@ -91,6 +94,15 @@ def main():
     import synthetic as syn
 
     G.load()  # fails loudly when the HIP library is missing
+    if args.mode == "copy":
+        n = 1 << 30
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(max(1, args.steps)):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"mode": "copy", "bytes_per_copy": n, "copies": max(1, args.steps)}), flush=True)
+        return
     cfg = syn.config_by_name(args.config)
     flags = G.GPTQ_FACTOR_REVERSED if args.factor == "reversed" else G.GPTQ_FACTOR_INVERSE_RECHOL
     t0 = time.perf_counter()
@@ -137,6 +149,16 @@ def main():
             for i, k in enumerate(("zero", "hessian", "prepare", "quantize")):
                 ev[k].append((marks[i], marks[i + 1]))
         return res
+
+    if args.mode == "hessian":
+        for _ in range(max(1, args.steps)):
+            st.S.zero_()
+            st.colsq.zero_()
+            st.n_total = 0
+            G.hessian_accumulate(Xd, st)
+        torch.cuda.synchronize()
+        print(json.dumps({"mode": "hessian", "config": cfg.name, "launches": max(1, args.steps)}), flush=True)
+        return
 
     for _ in range(args.warmup):
         step(False)

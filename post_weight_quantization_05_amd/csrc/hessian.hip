@@ -46,6 +46,38 @@ __device__ __forceinline__ void tile_coords(int t, int& I, int& J) {
   J = t - I0 * (I0 + 1) / 2;
 }
 
+// Position p of the lower tiles listed in super-tile order: blocks are grouped 4 at a time, super-tiles
+// (A >= B) are visited in order and the tiles inside each one row by row. Consecutive positions then
+// share few column blocks, so a contiguous run of positions (one XCD's share) reads a narrow set of
+// X's columns.
+__device__ __forceinline__ void supertile_coords(int p, int n_tb, int& I, int& J) {
+  constexpr int SB = 4;
+  const int ns = (n_tb + SB - 1) / SB;
+  for (int A = 0; A < ns; ++A) {
+    const int i0 = A * SB, i1 = min(n_tb, i0 + SB);
+    for (int B = 0; B <= A; ++B) {
+      const int j0 = B * SB, j1 = min(n_tb, j0 + SB);
+      int cnt;
+      if (A != B) cnt = (i1 - i0) * (j1 - j0);
+      else cnt = (i1 - i0) * (i1 - i0 + 1) / 2;
+      if (p < cnt) {
+        if (A != B) {
+          I = i0 + p / (j1 - j0);
+          J = j0 + p % (j1 - j0);
+        } else {
+          int r = 0;
+          while ((r + 1) * (r + 2) / 2 <= p) ++r;
+          I = i0 + r;
+          J = i0 + (p - r * (r + 1) / 2);
+        }
+        return;
+      }
+      p -= cnt;
+    }
+  }
+  I = J = 0;  // not reached for p < n_tiles
+}
+
 // Load 8 consecutive bf16 of one row (cols c..c+7), zero outside [0, d) or beyond the valid rows.
 template <bool VEC>
 __device__ __forceinline__ uint4 load8_bf16(const uint16_t* __restrict__ X, int64_t ld, int64_t row, bool row_ok,
@@ -273,7 +305,12 @@ constexpr int NSTG = 4;
 constexpr int PAIR_B = 1152;
 constexpr int OP_B = (BK / 2) * PAIR_B;  // 18432 B per operand per stage
 constexpr int STG_B = 2 * OP_B;          // 36864 B per stage
-constexpr int XWAVES = 8;                // waves per workgroup: 2 (M) x 4 (N), each a 128 x 64 block
+#ifndef GPTQ_XTX_WAVES
+#define GPTQ_XTX_WAVES 8
+#endif
+constexpr int XWAVES = GPTQ_XTX_WAVES;   // waves per workgroup: 2 (M) x XWAVES/2 (N)
+constexpr int XWN = XWAVES / 2;          // waves along N
+constexpr int XNB = (BT / XWN) / 32;     // 32-column MFMA blocks per wave along N
 constexpr int DMA_PAIRS = (BK / 2) / XWAVES;  // row pairs per wave per operand per stage
 
 __shared__ __attribute__((aligned(1024))) uint8_t g_stage0[STG_B];
@@ -357,7 +394,7 @@ __device__ __forceinline__ bf16x8 frag_tr(const uint8_t* opbase, int k16, int c0
 // one wave's MFMAs cover the other's barrier and LDS waits. In diagonal tiles the two waves whose block
 // lies above the diagonal add the fp64 squares of the stage instead (4 columns x 16 rows per lane).
 template <bool DIAG, int S>
-__device__ __forceinline__ void xtx_stage(const DmaCtx& c, int kt, f32x16 (&acc)[4][2], double (&csq)[4], int wm,
+__device__ __forceinline__ void xtx_stage(const DmaCtx& c, int kt, f32x16 (&acc)[4][XNB], double (&csq)[4], int wm,
                                           int wn, bool active) {
   constexpr int PER = (DIAG ? 1 : 2) * DMA_PAIRS;  // DMA instructions per wave per stage
   wait_vmcnt<(NSTG - 2) * PER>();
@@ -372,30 +409,33 @@ __device__ __forceinline__ void xtx_stage(const DmaCtx& c, int kt, f32x16 (&acc)
   const uint8_t* B = DIAG ? A : A + OP_B;
   const int g = c.lane >> 4, s = c.lane & 15;
   if (active) {
-    bf16x8 fa0[4], fb0[2], fa1[4], fb1[2];
+    bf16x8 fa0[4], fb0[XNB], fa1[4], fb1[XNB];
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) fa0[mb] = frag_tr(A, 0, wm * 128 + mb * 32, g, s);
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) fb0[nb] = frag_tr(B, 0, wn * 64 + nb * 32, g, s);
+    for (int nb = 0; nb < XNB; ++nb) fb0[nb] = frag_tr(B, 0, wn * (BT / XWN) + nb * 32, g, s);
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) fa1[mb] = frag_tr(A, 16, wm * 128 + mb * 32, g, s);
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) fb1[nb] = frag_tr(B, 16, wn * 64 + nb * 32, g, s);
+    for (int nb = 0; nb < XNB; ++nb) fb1[nb] = frag_tr(B, 16, wn * (BT / XWN) + nb * 32, g, s);
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
+      for (int nb = 0; nb < XNB; ++nb)
         acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa0[mb], fb0[nb], acc[mb][nb], 0, 0, 0);
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
+      for (int nb = 0; nb < XNB; ++nb)
         acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa1[mb], fb1[nb], acc[mb][nb], 0, 0, 0);
   } else if (DIAG) {
+    // the waves above the diagonal of a diagonal tile share the stage's rows between them
+    constexpr int NIDLE = XWN / 2;          // waves (0, wn) with wn >= XWN/2
+    constexpr int RPW = BK / NIDLE;         // rows per idle wave
     const int cc = c.lane * 4;              // columns cc..cc+3
-    const int kr = (wn - 2) * 16;           // rows kr..kr+15 of the stage (waves (0,2) and (0,3))
+    const int kr = (wn - XWN / 2) * RPW;
 #pragma unroll 4
-    for (int k = 0; k < 16; ++k) {
+    for (int k = 0; k < RPW; ++k) {
       const uint2 v = *reinterpret_cast<const uint2*>(A + stage_off(kr + k, cc >> 3) + (cc & 7) * 2);
       const double x0 = (double)__uint_as_float(v.x << 16), x1 = (double)__uint_as_float(v.x & 0xFFFF0000u);
       const double x2 = (double)__uint_as_float(v.y << 16), x3 = (double)__uint_as_float(v.y & 0xFFFF0000u);
@@ -408,7 +448,7 @@ __device__ __forceinline__ void xtx_stage(const DmaCtx& c, int kt, f32x16 (&acc)
 }
 
 template <bool DIAG>
-__device__ __forceinline__ void xtx_dma_body(const DmaCtx& c, int nk, f32x16 (&acc)[4][2], double (&csq)[4], int wm,
+__device__ __forceinline__ void xtx_dma_body(const DmaCtx& c, int nk, f32x16 (&acc)[4][XNB], double (&csq)[4], int wm,
                                              int wn, bool active) {
   // prologue: stages 0 .. NSTG-2 in flight (stages past the slice fetch zeros)
   dma_stage<0>(c, 0, 0, c.colA);
@@ -430,26 +470,32 @@ __device__ __forceinline__ void xtx_dma_body(const DmaCtx& c, int nk, f32x16 (&a
   __builtin_amdgcn_s_barrier();
 }
 
-__global__ __launch_bounds__(512, 1) void k_xtx_bf16_dma(const uint16_t* __restrict__ X, int64_t ld, int64_t n_rows,
+__global__ __launch_bounds__(XWAVES * 64, 1) void k_xtx_bf16_dma(const uint16_t* __restrict__ X, int64_t ld, int64_t n_rows,
                                                          int d, int n_tiles, int64_t rps, int remap, int splits,
                                                          float* __restrict__ part, double* __restrict__ colsq_part,
                                                          int colsq_stride, unsigned* __restrict__ counters,
                                                          double* __restrict__ S, double* __restrict__ colsq) {
   __shared__ int s_last;
-  const int G = gridDim.x;
+  // Workgroup b runs on XCD b % 8 (round-robin dispatch). Each XCD owns a contiguous run of `cs` tiles in
+  // super-tile order and walks the row slices in order; all XCDs are on the same slices at the same time,
+  // so each slice comes from HBM about once and the XCDs share it through the last-level cache.
   const int b = blockIdx.x;
-  const int L = remap ? (b % 8) * (G / 8) + b / 8 : b;
-  const int split = L / n_tiles;
-  const int t = L - split * n_tiles;
+  const int xcd = b & 7;
+  const int m = b >> 3;
+  const int cs = remap;  // tiles per XCD
+  const int split = m / cs;
+  const int p = xcd * cs + (m - split * cs);
+  if (p >= n_tiles) return;  // padding slot (tile count not a multiple of 8)
   int I, J;
-  tile_coords(t, I, J);
+  supertile_coords(p, (int)((d + BT - 1) / BT), I, J);
+  int t = I * (I + 1) / 2 + J;
   const bool diag = (I == J);
   const int64_t r0 = (int64_t)split * rps;
   const int64_t r1 = min(n_rows, r0 + rps);
   const int nk = (int)((r1 - r0 + BK - 1) / BK);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 2, wn = wave & 3;  // 2 x 4 waves of 128 x 64
-  const bool active = !(diag && wm == 0 && wn >= 2);  // blocks above the diagonal of a diagonal tile
+  const int wm = wave / XWN, wn = wave % XWN;  // 2 x XWN waves of 128 x (256 / XWN)
+  const bool active = !(diag && wm == 0 && wn >= XWN / 2);  // blocks above the diagonal of a diagonal tile
 
   DmaCtx c;
   {
@@ -465,11 +511,11 @@ __global__ __launch_bounds__(512, 1) void k_xtx_bf16_dma(const uint16_t* __restr
   c.wave = wave;
   c.lane = lane;
 
-  f32x16 acc[4][2];
+  f32x16 acc[4][XNB];
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
+    for (int nb = 0; nb < XNB; ++nb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mb][nb][r] = 0.0f;
   double csq[4] = {0.0, 0.0, 0.0, 0.0};
@@ -482,23 +528,29 @@ __global__ __launch_bounds__(512, 1) void k_xtx_bf16_dma(const uint16_t* __restr
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
+      for (int nb = 0; nb < XNB; ++nb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int i = wm * 128 + mb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-          const int j = wn * 64 + nb * 32 + (lane & 31);
+          const int j = wn * (BT / XWN) + nb * 32 + (lane & 31);
           dst[i * BT + j] = acc[mb][nb][r];
         }
   }
   if (diag) {
-    // the two column-sum waves hold rows 0..15 and 16..31 of every stage; add them in a fixed order
-    double* red = reinterpret_cast<double*>(g_stage0);  // 2 x 256 doubles; the DMA ring is drained
+    // the column-sum waves hold disjoint row ranges of every stage; add them in a fixed order
+    constexpr int NIDLE = XWN / 2;
+    double* red = reinterpret_cast<double*>(g_stage0);  // NIDLE x 256 doubles; the DMA ring is drained
     if (!active) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) red[(wn - 2) * 256 + lane * 4 + q] = csq[q];
+      for (int q = 0; q < 4; ++q) red[(wn - XWN / 2) * 256 + lane * 4 + q] = csq[q];
     }
     __syncthreads();
-    if (tid < BT) colsq_part[(int64_t)split * colsq_stride + c.colA + tid] = red[tid] + red[256 + tid];
+    if (tid < BT) {
+      double sum = red[tid];
+#pragma unroll
+      for (int w = 1; w < NIDLE; ++w) sum += red[w * 256 + tid];
+      colsq_part[(int64_t)split * colsq_stride + c.colA + tid] = sum;
+    }
   }
   finish_tile<BT>(t, I, J, diag, d, n_tiles, splits, part, colsq_part, colsq_stride, counters, S, colsq, &s_last);
 }
@@ -669,6 +721,8 @@ hipError_t hessian_launch(const HessianPlan& p, const void* X, double* S, double
   unsigned* counters = reinterpret_cast<unsigned*>(reinterpret_cast<char*>(ws) + p.part_bytes + p.colsq_part_bytes);
   const int grid = p.splits * p.n_tiles;
   const int remap = (grid % 8 == 0) ? 1 : 0;
+  const int cs = (p.n_tiles + 7) / 8;         // tiles per XCD for the direct-to-LDS kernel
+  const int grid_dma = 8 * cs * p.splits;
   const int cstride = p.n_tb * p.tile;
   // counters start at zero on every call (a small fill kernel, safe under stream capture)
   hipLaunchKernelGGL(k_zero_counters, dim3((unsigned)ceil_div(p.n_tiles, 256)), dim3(256), 0, stream, counters,
@@ -679,9 +733,9 @@ hipError_t hessian_launch(const HessianPlan& p, const void* X, double* S, double
     const bool vec = (p.ld % 8 == 0) && (p.in % 8 == 0) && ((reinterpret_cast<uintptr_t>(X) & 15) == 0);
     const bool dma = vec && (p.rows_per_split * p.ld * 2 < ((int64_t)1 << 31));
     if (dma)
-      hipLaunchKernelGGL(k_xtx_bf16_dma, dim3(grid), dim3(512), 0, stream, (const uint16_t*)X, p.ld, p.n_rows,
-                         (int)p.in, p.n_tiles, p.rows_per_split, remap, p.splits, part, cpart, cstride, counters, S,
-                         colsq);
+      hipLaunchKernelGGL(k_xtx_bf16_dma, dim3(grid_dma), dim3(XWAVES * 64), 0, stream, (const uint16_t*)X, p.ld,
+                         p.n_rows, (int)p.in, p.n_tiles, p.rows_per_split, cs, p.splits, part, cpart, cstride,
+                         counters, S, colsq);
     else if (vec)
       hipLaunchKernelGGL(k_xtx_bf16<true>, dim3(grid), dim3(256), 0, stream, (const uint16_t*)X, p.ld, p.n_rows,
                          (int)p.in, p.n_tiles, p.rows_per_split, remap, p.splits, part, cpart, cstride, counters, S,
