@@ -114,6 +114,11 @@ __device__ __forceinline__ void sq_accum8(double* acc, uint4 v) {
 // per-tile counter); the workgroup that arrives last sums the slices of that tile in slice order in fp64
 // and adds them to S's lower triangle (and, for diagonal tiles, the column sums to colsq). The order of
 // the sum does not depend on which workgroup arrives last, so results are bitwise reproducible.
+// The last workgroup reads splits x TILE^2 floats; it keeps FIN_E x FIN_SB 16-byte loads in flight per
+// thread (two 4-column groups, eight slices each) so that the combine runs at bandwidth, not latency.
+constexpr int FIN_E = 2;
+constexpr int FIN_SB = 8;
+
 template <int TILE>
 __device__ __forceinline__ void finish_tile(int t, int I, int J, bool diag, int d, int n_tiles, int splits,
                                             const float* __restrict__ part, const double* __restrict__ colsq_part,
@@ -126,27 +131,77 @@ __device__ __forceinline__ void finish_tile(int t, int I, int J, bool diag, int 
   __syncthreads();
   if (!*s_last) return;
   __threadfence();
+  constexpr int Q = TILE / 4;    // 4-column groups per tile row
+  constexpr int NE = TILE * Q;   // 4-column groups per tile
   const int64_t tsz = (int64_t)TILE * TILE;
-  const int64_t sstride = (int64_t)n_tiles * tsz;
-  const float* p0 = part + (int64_t)t * tsz;
-  for (int i = 0; i < TILE; ++i) {
-    const int gi = I * TILE + i;
-    if (gi >= d) break;
-    for (int j = tid; j < TILE; j += blockDim.x) {
-      const int gj = J * TILE + j;
-      if (gj > gi || gj >= d) continue;
-      const float* p = p0 + (int64_t)i * TILE + j;
-      double sum = 0.0;
-      for (int sidx = 0; sidx < splits; ++sidx) sum += (double)p[sidx * sstride];
-      S[(int64_t)gi * d + gj] += sum;
+  const int64_t sstride4 = (int64_t)n_tiles * tsz / 4;  // one slice's partials, in float4
+  const float4* p0 = reinterpret_cast<const float4*>(part + (int64_t)t * tsz);
+  const int nthr = blockDim.x;
+  for (int e0 = tid; e0 < NE; e0 += FIN_E * nthr) {
+    int gi[FIN_E], gj[FIN_E];
+    bool live[FIN_E];
+    double acc[FIN_E][4];
+#pragma unroll
+    for (int k = 0; k < FIN_E; ++k) {
+      const int e = e0 + k * nthr;
+      gi[k] = I * TILE + e / Q;
+      gj[k] = J * TILE + (e % Q) * 4;
+      live[k] = e < NE && gi[k] < d && gj[k] <= gi[k] && gj[k] < d;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[k][c] = 0.0;
     }
+    for (int s0 = 0; s0 < splits; s0 += FIN_SB) {
+      // unconditional loads from clamped (valid) addresses, then a select: no branch between the loads
+      float4 v[FIN_E][FIN_SB];
+#pragma unroll
+      for (int k = 0; k < FIN_E; ++k)
+#pragma unroll
+        for (int u = 0; u < FIN_SB; ++u) {
+          const int e = min(e0 + k * nthr, NE - 1);
+          const int sl = min(s0 + u, splits - 1);
+          const float4 x = p0[e + (int64_t)sl * sstride4];
+          const bool use = live[k] && s0 + u < splits;
+          v[k][u] = make_float4(use ? x.x : 0.f, use ? x.y : 0.f, use ? x.z : 0.f, use ? x.w : 0.f);
+        }
+      // slice order; a slice past the end adds an exact zero
+#pragma unroll
+      for (int k = 0; k < FIN_E; ++k)
+#pragma unroll
+        for (int u = 0; u < FIN_SB; ++u) {
+          acc[k][0] += (double)v[k][u].x;
+          acc[k][1] += (double)v[k][u].y;
+          acc[k][2] += (double)v[k][u].z;
+          acc[k][3] += (double)v[k][u].w;
+        }
+    }
+    // read the S entries first (clamped to valid addresses), then store only the lower-triangle ones
+    double old[FIN_E][4];
+#pragma unroll
+    for (int k = 0; k < FIN_E; ++k)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        old[k][c] = S[(int64_t)min(gi[k], d - 1) * d + min(gj[k] + c, d - 1)];
+#pragma unroll
+    for (int k = 0; k < FIN_E; ++k)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (live[k] && gj[k] + c <= gi[k] && gj[k] + c < d) S[(int64_t)gi[k] * d + gj[k] + c] = old[k][c] + acc[k][c];
   }
   if (diag) {
-    for (int c = tid; c < TILE; c += blockDim.x) {
+    for (int c = tid; c < TILE; c += nthr) {
       const int gc = I * TILE + c;
       if (gc >= d) break;
       double sum = 0.0;
-      for (int sidx = 0; sidx < splits; ++sidx) sum += colsq_part[(int64_t)sidx * colsq_stride + gc];
+      for (int s0 = 0; s0 < splits; s0 += FIN_SB) {
+        double v[FIN_SB];
+#pragma unroll
+        for (int u = 0; u < FIN_SB; ++u) {
+          const double x = colsq_part[(int64_t)min(s0 + u, splits - 1) * colsq_stride + gc];
+          v[u] = (s0 + u < splits) ? x : 0.0;
+        }
+#pragma unroll
+        for (int u = 0; u < FIN_SB; ++u) sum += v[u];
+      }
       colsq[gc] += sum;
     }
   }
@@ -703,6 +758,9 @@ HessianPlan hessian_plan(int64_t n_rows, int64_t in, int dtype) {
       best_s = s;
     }
   }
+#ifdef GPTQ_XTX_SPLITS
+  best_s = (int)std::min<int64_t>(GPTQ_XTX_SPLITS, max_splits);
+#endif
   p.splits = best_s;
   p.rows_per_split = ceil_div(ceil_div(n_rows, p.splits), kstep) * kstep;
   p.splits = (int)ceil_div(n_rows, p.rows_per_split);
