@@ -22,6 +22,7 @@
 // fp32 X (small layers) uses the same structure with v_mfma_f32_16x16x4f32 on 128 x 128 tiles; fp32
 // operands need no transpose (one k per lane).
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 
@@ -349,17 +350,21 @@ __global__ __launch_bounds__(256, 1) void k_xtx_bf16(const uint16_t* __restrict_
 //
 // Each 32-row stage of a 256-column operand block is fetched with buffer_load_dwordx4 ... lds (no staging
 // registers) into one of NSTG LDS stage buffers, NSTG - 1 stages ahead of the MFMAs. One DMA instruction
-// moves 1 KB = two rows; rows are stored in pairs of 1152 B (1 KB + 128 B pad) and the odd row of a pair
-// has its 16-byte chunks XOR-swizzled by 4, so the 4 x 64 B that the transposing reads of 32 lanes touch
-// fall on 64 distinct banks. Rows past the slice end and columns past `in` are outside the buffer range
+// moves 1 KB = two 512-byte rows. Rows are stored unpadded; the 16-byte chunks of row k are XOR-swizzled
+// by 4 * (k mod 4), so the four rows that one transposing read touches (64 B each) fall on four disjoint
+// quarters of the 64 banks. Rows past the slice end and columns past `in` are outside the buffer range
 // and arrive as zeros. Stage buffers are separate LDS arrays addressed with compile-time indices, so the
 // compiler can tell a DMA into one stage from reads of another and only the explicit vmcnt waits order
-// them.
+// them. With five stages the ring fills the 160 KB of LDS; four stages (128 KB) are in flight per CU,
+// which is what covers the fabric latency at this request rate.
 // ---------------------------------------------------------------------------------------------------
-constexpr int NSTG = 4;
-constexpr int PAIR_B = 1152;
-constexpr int OP_B = (BK / 2) * PAIR_B;  // 18432 B per operand per stage
-constexpr int STG_B = 2 * OP_B;          // 36864 B per stage
+#ifndef GPTQ_XTX_STAGES
+#define GPTQ_XTX_STAGES 5
+#endif
+constexpr int NSTG = GPTQ_XTX_STAGES;
+constexpr int ROW_B = 512;               // one row of a 256-column bf16 operand block
+constexpr int OP_B = BK * ROW_B;         // 16384 B per operand per stage
+constexpr int STG_B = 2 * OP_B;          // 32768 B per stage
 #ifndef GPTQ_XTX_WAVES
 #define GPTQ_XTX_WAVES 8
 #endif
@@ -367,25 +372,28 @@ constexpr int XWAVES = GPTQ_XTX_WAVES;   // waves per workgroup: 2 (M) x XWAVES/
 constexpr int XWN = XWAVES / 2;          // waves along N
 constexpr int XNB = (BT / XWN) / 32;     // 32-column MFMA blocks per wave along N
 constexpr int DMA_PAIRS = (BK / 2) / XWAVES;  // row pairs per wave per operand per stage
+static_assert(NSTG >= 3 && NSTG <= 5, "stage count");
 
 __shared__ __attribute__((aligned(1024))) uint8_t g_stage0[STG_B];
 __shared__ __attribute__((aligned(1024))) uint8_t g_stage1[STG_B];
 __shared__ __attribute__((aligned(1024))) uint8_t g_stage2[STG_B];
 __shared__ __attribute__((aligned(1024))) uint8_t g_stage3[STG_B];
+__shared__ __attribute__((aligned(1024))) uint8_t g_stage4[STG_B];
 
 template <int S>
 __device__ __forceinline__ uint8_t* stage_buf() {
   if constexpr (S == 0) return g_stage0;
   else if constexpr (S == 1) return g_stage1;
   else if constexpr (S == 2) return g_stage2;
-  else return g_stage3;
+  else if constexpr (S == 3) return g_stage3;
+  else return g_stage4;
 }
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 // byte offset of (row k, 8-element chunk q) inside one operand's stage buffer
 __device__ __forceinline__ int stage_off(int k, int q) {
-  return (k >> 1) * PAIR_B + (k & 1) * 512 + ((q ^ ((k & 1) << 2)) << 4);
+  return k * ROW_B + ((q ^ ((k & 3) << 2)) << 4);
 }
 
 // s_waitcnt with vmcnt = N (expcnt and lgkmcnt left unconstrained)
@@ -415,20 +423,34 @@ __device__ __forceinline__ void dma16(const i32x4& rsrc, uint32_t lds_addr, uint
                : "memory", "m0");
 }
 
+// One DMA instruction of stage kt: row pair wave * DMA_PAIRS + pp of operand slot `op` (block `col0`).
+template <int S>
+__device__ __forceinline__ void dma_one(const DmaCtx& c, int kt, int op, int col0, int pp) {
+  const uint32_t base = (uint32_t)(uintptr_t)(stage_buf<S>() + op * OP_B);
+  const int half = c.lane >> 5;
+  const int p = c.wave * DMA_PAIRS + pp;
+  const int k = 2 * p + half;
+  const int q = (c.lane & 31) ^ ((k & 3) << 2);
+  const int col = col0 + 8 * q;
+  const int row = kt * BK + k;
+  const uint32_t voff = (col < c.d) ? (uint32_t)(row * c.row_bytes + col * 2) : 0x80000000u;
+  dma16(c.rsrc, __builtin_amdgcn_readfirstlane(base + p * 2 * ROW_B), voff);
+}
+
 // Issue the DMA of stage kt (32 rows) of operand block `col0` into operand slot `op` of stage buffer S.
 template <int S>
 __device__ __forceinline__ void dma_stage(const DmaCtx& c, int kt, int op, int col0) {
   const uint32_t base = (uint32_t)(uintptr_t)(stage_buf<S>() + op * OP_B);
   const int half = c.lane >> 5;
-  const int q = (c.lane & 31) ^ (half << 2);
-  const int col = col0 + 8 * q;
-  const bool col_ok = col < c.d;
 #pragma unroll
   for (int pp = 0; pp < DMA_PAIRS; ++pp) {
     const int p = c.wave * DMA_PAIRS + pp;    // row pair within the stage
-    const int row = kt * BK + 2 * p + half;   // row within the slice
-    const uint32_t voff = col_ok ? (uint32_t)(row * c.row_bytes + col * 2) : 0x80000000u;
-    dma16(c.rsrc, __builtin_amdgcn_readfirstlane(base + p * PAIR_B), voff);
+    const int k = 2 * p + half;               // row within the stage; LDS chunk (lane & 31) of it holds
+    const int q = (c.lane & 31) ^ ((k & 3) << 2);  // logical chunk q (the swizzle of stage_off)
+    const int col = col0 + 8 * q;
+    const int row = kt * BK + k;              // row within the slice
+    const uint32_t voff = (col < c.d) ? (uint32_t)(row * c.row_bytes + col * 2) : 0x80000000u;
+    dma16(c.rsrc, __builtin_amdgcn_readfirstlane(base + p * 2 * ROW_B), voff);
   }
 }
 
@@ -438,31 +460,41 @@ __device__ __forceinline__ bf16x8 frag_tr(const uint8_t* opbase, int k16, int c0
   const int c = c0 + 16 * (g & 1) + (s & 3) * 4;
   const int off = stage_off(k, c >> 3) + (c & 7) * 2;
   i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(opbase + off));
-  i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(opbase + off + 2 * PAIR_B));
+  i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(opbase + off + 4 * ROW_B));
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// One 32-row stage: wait for this stage's DMA, barrier, start the DMA of the stage NSTG - 1 ahead (issued
-// unconditionally: past the slice end its offsets are out of range and it fetches zeros into a stage
-// buffer that is never read, which keeps the vmcnt bookkeeping uniform), then 2 x 8 MFMAs per wave with
-// the second half's fragments in flight while the first half's MFMAs run. Two waves share each SIMD, so
-// one wave's MFMAs cover the other's barrier and LDS waits. In diagonal tiles the two waves whose block
-// lies above the diagonal add the fp64 squares of the stage instead (4 columns x 16 rows per lane).
+template <int I, int N, typename F>
+__device__ __forceinline__ void xstatic_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    xstatic_for<I + 1, N>(f);
+  }
+}
+
+// One 32-row stage: wait for this stage's DMA, barrier, read all 2 x (4 + XNB) operand fragments of the
+// stage, then issue the DMA of the stage NSTG - 1 ahead one instruction at a time between the first
+// half's MFMAs (a burst of DMA instructions would stall the issuing waves while the address unit drains
+// it, leaving the matrix units idle), then the second half's MFMAs. The DMA is issued unconditionally:
+// past the slice end its offsets are out of range and it fetches zeros into a stage buffer that is never
+// read, which keeps the vmcnt bookkeeping uniform. Two waves share each SIMD, so one wave's MFMAs cover
+// the other's barrier and LDS waits. In diagonal tiles the waves whose block lies above the diagonal
+// add the fp64 squares of the stage instead (4 columns per lane).
 template <bool DIAG, int S>
 __device__ __forceinline__ void xtx_stage(const DmaCtx& c, int kt, f32x16 (&acc)[4][XNB], double (&csq)[4], int wm,
                                           int wn, bool active) {
   constexpr int PER = (DIAG ? 1 : 2) * DMA_PAIRS;  // DMA instructions per wave per stage
+  constexpr int SN = (S + NSTG - 1) % NSTG;        // buffer of stage kt + NSTG - 1
   wait_vmcnt<(NSTG - 2) * PER>();
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-  {
-    constexpr int SN = (S + NSTG - 1) % NSTG;
-    dma_stage<SN>(c, kt + NSTG - 1, 0, c.colA);
-    if (!DIAG) dma_stage<SN>(c, kt + NSTG - 1, 1, c.colB);
-  }
   const uint8_t* A = stage_buf<S>();
   const uint8_t* B = DIAG ? A : A + OP_B;
   const int g = c.lane >> 4, s = c.lane & 15;
+  auto dma_i = [&](auto ic) {
+    constexpr int i = decltype(ic)::value;
+    dma_one<SN>(c, kt + NSTG - 1, i / DMA_PAIRS, (i / DMA_PAIRS) ? c.colB : c.colA, i % DMA_PAIRS);
+  };
   if (active) {
     bf16x8 fa0[4], fb0[XNB], fa1[4], fb1[XNB];
 #pragma unroll
@@ -473,54 +505,76 @@ __device__ __forceinline__ void xtx_stage(const DmaCtx& c, int kt, f32x16 (&acc)
     for (int mb = 0; mb < 4; ++mb) fa1[mb] = frag_tr(A, 16, wm * 128 + mb * 32, g, s);
 #pragma unroll
     for (int nb = 0; nb < XNB; ++nb) fb1[nb] = frag_tr(B, 16, wn * (BT / XWN) + nb * 32, g, s);
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < XNB; ++nb)
-        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa0[mb], fb0[nb], acc[mb][nb], 0, 0, 0);
+    constexpr int NM = 4 * XNB;     // MFMAs per half
+    constexpr int GM = NM / PER;    // first-half MFMAs after each DMA instruction
+    static_assert(NM % PER == 0, "MFMA groups");
+    xstatic_for<0, PER>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      __builtin_amdgcn_sched_barrier(0);
+      dma_i(ic);
+      __builtin_amdgcn_sched_barrier(0);
+      xstatic_for<0, GM>([&](auto jc) {
+        constexpr int f = i * GM + decltype(jc)::value;
+        acc[f / XNB][f % XNB] =
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa0[f / XNB], fb0[f % XNB], acc[f / XNB][f % XNB], 0, 0, 0);
+      });
+    });
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
       for (int nb = 0; nb < XNB; ++nb)
         acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa1[mb], fb1[nb], acc[mb][nb], 0, 0, 0);
-  } else if (DIAG) {
-    // the waves above the diagonal of a diagonal tile share the stage's rows between them
-    constexpr int NIDLE = XWN / 2;          // waves (0, wn) with wn >= XWN/2
-    constexpr int RPW = BK / NIDLE;         // rows per idle wave
-    const int cc = c.lane * 4;              // columns cc..cc+3
-    const int kr = (wn - XWN / 2) * RPW;
+  } else {
+    xstatic_for<0, PER>(dma_i);
+    if (DIAG) {
+      // the waves above the diagonal of a diagonal tile share the stage's rows between them
+      constexpr int NIDLE = XWN / 2;          // waves (0, wn) with wn >= XWN/2
+      constexpr int RPW = BK / NIDLE;         // rows per idle wave
+      const int cc = c.lane * 4;              // columns cc..cc+3
+      const int kr = (wn - XWN / 2) * RPW;
 #pragma unroll 4
-    for (int k = 0; k < RPW; ++k) {
-      const uint2 v = *reinterpret_cast<const uint2*>(A + stage_off(kr + k, cc >> 3) + (cc & 7) * 2);
-      const double x0 = (double)__uint_as_float(v.x << 16), x1 = (double)__uint_as_float(v.x & 0xFFFF0000u);
-      const double x2 = (double)__uint_as_float(v.y << 16), x3 = (double)__uint_as_float(v.y & 0xFFFF0000u);
-      csq[0] = fma(x0, x0, csq[0]);
-      csq[1] = fma(x1, x1, csq[1]);
-      csq[2] = fma(x2, x2, csq[2]);
-      csq[3] = fma(x3, x3, csq[3]);
+      for (int k = 0; k < RPW; ++k) {
+        const uint2 v = *reinterpret_cast<const uint2*>(A + stage_off(kr + k, cc >> 3) + (cc & 7) * 2);
+        const double x0 = (double)__uint_as_float(v.x << 16), x1 = (double)__uint_as_float(v.x & 0xFFFF0000u);
+        const double x2 = (double)__uint_as_float(v.y << 16), x3 = (double)__uint_as_float(v.y & 0xFFFF0000u);
+        csq[0] = fma(x0, x0, csq[0]);
+        csq[1] = fma(x1, x1, csq[1]);
+        csq[2] = fma(x2, x2, csq[2]);
+        csq[3] = fma(x3, x3, csq[3]);
+      }
     }
+  }
+}
+
+// stages kt + S .. kt + NSTG - 1 of one turn of the ring; false once the slice is done
+template <bool DIAG, int S>
+__device__ __forceinline__ bool xtx_ring(const DmaCtx& c, int kt, int nk, f32x16 (&acc)[4][XNB], double (&csq)[4],
+                                         int wm, int wn, bool active) {
+  if constexpr (S == NSTG) {
+    return true;
+  } else {
+    if (kt + S >= nk) return false;
+    xtx_stage<DIAG, S>(c, kt + S, acc, csq, wm, wn, active);
+    return xtx_ring<DIAG, S + 1>(c, kt, nk, acc, csq, wm, wn, active);
+  }
+}
+
+template <bool DIAG, int S>
+__device__ __forceinline__ void xtx_prologue(const DmaCtx& c) {
+  if constexpr (S < NSTG - 1) {
+    dma_stage<S>(c, S, 0, c.colA);
+    if (!DIAG) dma_stage<S>(c, S, 1, c.colB);
+    xtx_prologue<DIAG, S + 1>(c);
   }
 }
 
 template <bool DIAG>
 __device__ __forceinline__ void xtx_dma_body(const DmaCtx& c, int nk, f32x16 (&acc)[4][XNB], double (&csq)[4], int wm,
                                              int wn, bool active) {
-  // prologue: stages 0 .. NSTG-2 in flight (stages past the slice fetch zeros)
-  dma_stage<0>(c, 0, 0, c.colA);
-  if (!DIAG) dma_stage<0>(c, 0, 1, c.colB);
-  dma_stage<1>(c, 1, 0, c.colA);
-  if (!DIAG) dma_stage<1>(c, 1, 1, c.colB);
-  dma_stage<2>(c, 2, 0, c.colA);
-  if (!DIAG) dma_stage<2>(c, 2, 1, c.colB);
-  for (int kt = 0; kt < nk; kt += NSTG) {
-    xtx_stage<DIAG, 0>(c, kt, acc, csq, wm, wn, active);
-    if (kt + 1 >= nk) break;
-    xtx_stage<DIAG, 1>(c, kt + 1, acc, csq, wm, wn, active);
-    if (kt + 2 >= nk) break;
-    xtx_stage<DIAG, 2>(c, kt + 2, acc, csq, wm, wn, active);
-    if (kt + 3 >= nk) break;
-    xtx_stage<DIAG, 3>(c, kt + 3, acc, csq, wm, wn, active);
-  }
+  xtx_prologue<DIAG, 0>(c);  // stages 0 .. NSTG-2 in flight (stages past the slice fetch zeros)
+  for (int kt = 0; kt < nk; kt += NSTG)
+    if (!xtx_ring<DIAG, 0>(c, kt, nk, acc, csq, wm, wn, active)) break;
   wait_vmcnt<0>();  // no DMA may still be writing LDS when the workgroup moves on
   __builtin_amdgcn_s_barrier();
 }
@@ -530,7 +584,6 @@ __global__ __launch_bounds__(XWAVES * 64, 1) void k_xtx_bf16_dma(const uint16_t*
                                                          float* __restrict__ part, double* __restrict__ colsq_part,
                                                          int colsq_stride, unsigned* __restrict__ counters,
                                                          double* __restrict__ S, double* __restrict__ colsq) {
-  __shared__ int s_last;
   // Workgroup b runs on XCD b % 8 (round-robin dispatch). Each XCD owns a contiguous run of `cs` tiles in
   // super-tile order and walks the row slices in order; all XCDs are on the same slices at the same time,
   // so each slice comes from HBM about once and the XCDs share it through the last-level cache.
@@ -607,7 +660,9 @@ __global__ __launch_bounds__(XWAVES * 64, 1) void k_xtx_bf16_dma(const uint16_t*
       colsq_part[(int64_t)split * colsq_stride + c.colA + tid] = sum;
     }
   }
-  finish_tile<BT>(t, I, J, diag, d, n_tiles, splits, part, colsq_part, colsq_stride, counters, S, colsq, &s_last);
+  // the ring fills LDS; the completion flag lives in a drained stage buffer
+  finish_tile<BT>(t, I, J, diag, d, n_tiles, splits, part, colsq_part, colsq_stride, counters, S, colsq,
+                  reinterpret_cast<int*>(g_stage1));
 }
 
 // ---------------------------------------------------------------------------------------------------
