@@ -15,7 +15,13 @@
 //              (row_newbcast), every lane of the row rounds it (IEEE division, round-half-even), and
 //              updates its own columns with U[j][col] from LDS. Group maxima are 16-lane DPP max
 //              reductions. Codes and errors stay in registers and are stored once per panel.
-//  trailing    W[:, b1:] -= Err[:, panel] U[panel, b1:] on the fp64 MFMA GEMM core.
+//  trailing    two levels of lazy updates on the fp64 MFMA GEMM core. Panels are grouped into outer
+//              blocks of OB columns. After a panel, only the rest of its outer block is updated,
+//              W[:, b1:ob1] -= Err[:, panel] U[panel, b1:ob1] (K = 128); after the last panel of an outer
+//              block, every later column gets the whole block at once, W[:, ob1:] -= Err[:, block]
+//              U[block, ob1:] (K = OB). The products are the ones of the column-by-column loop; only
+//              their grouping (and so the floating-point summation order) changes, and the fp64 W is
+//              read and written a few times instead of once per panel.
 #include <type_traits>
 #include <utility>
 
@@ -27,6 +33,11 @@ namespace gptq {
 namespace {
 
 constexpr int PW = 128;  // panel width
+#ifndef GPTQ_QUANT_OB
+#define GPTQ_QUANT_OB 1024
+#endif
+constexpr int OB = GPTQ_QUANT_OB;  // outer block of the lazy updates (a multiple of PW)
+static_assert(OB % PW == 0, "outer block");
 constexpr double SCALE_FLOOR = 1e-12;
 
 template <int J, int N, typename F>
@@ -130,7 +141,7 @@ __global__ __launch_bounds__(256) void k_panel(double* __restrict__ Wq, int out,
                                                double* __restrict__ scale_row, double qmax, int group,
                                                int n_groups, int8_t* __restrict__ codes,
                                                float* __restrict__ scales, double* __restrict__ Err,
-                                               double* __restrict__ row_loss) {
+                                               int ld_err, double* __restrict__ row_loss) {
   __shared__ double Us[PW][PW];
   __shared__ double rdiag[PW];
   __shared__ int pidx[PW];
@@ -237,7 +248,7 @@ __global__ __launch_bounds__(256) void k_panel(double* __restrict__ Wq, int out,
   double lsum = 0.0;
   if (rok) {
     int8_t* crow = codes + (int64_t)r * in;
-    double* erow = Err + (int64_t)r * PW;
+    double* erow = Err + (int64_t)r * ld_err;
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
       const int col = c + 16 * m;
@@ -266,7 +277,7 @@ __global__ void k_gidx(const int32_t* __restrict__ perm, int in, int group, int3
 size_t quantize_ws_bytes(int64_t out, int64_t in) {
   size_t b = 0;
   b += align_up((size_t)out * in * sizeof(double), 256);  // working copy
-  b += align_up((size_t)out * PW * sizeof(double), 256);  // panel errors
+  b += align_up((size_t)out * OB * sizeof(double), 256);  // errors of one outer block
   b += align_up((size_t)out * sizeof(double), 256);       // current fp64 scale per row
   return b;
 }
@@ -279,7 +290,7 @@ hipError_t quantize_launch(const void* W, int w_dtype, int64_t out64, int64_t in
   double* Wq = reinterpret_cast<double*>(w);
   w += align_up((size_t)out * in * sizeof(double), 256);
   double* Err = reinterpret_cast<double*>(w);
-  w += align_up((size_t)out * PW * sizeof(double), 256);
+  w += align_up((size_t)out * OB * sizeof(double), 256);
   double* scale_row = reinterpret_cast<double*>(w);
   const double qmax = (double)((1 << (bits - 1)) - 1);
   const int n_groups = group ? (int)ceil_div(in, group) : 1;
@@ -294,22 +305,37 @@ hipError_t quantize_launch(const void* W, int w_dtype, int64_t out64, int64_t in
   if (e != hipSuccess) return e;
 
   const dim3 pgrid((unsigned)ceil_div(out, 16));
-  for (int b0 = 0; b0 < in; b0 += PW) {
-    if (group != 0 && PW % group == 0)
-      k_panel<true><<<pgrid, dim3(256), 0, stream>>>(Wq, out, in, b0, U, perm, scale_row, qmax, group, n_groups,
-                                                     codes, scales, Err, row_loss);
-    else
-      k_panel<false><<<pgrid, dim3(256), 0, stream>>>(Wq, out, in, b0, U, perm, scale_row, qmax, group, n_groups,
-                                                      codes, scales, Err, row_loss);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const int b1 = b0 + PW;
-    if (b1 < in) {
+  for (int ob0 = 0; ob0 < in; ob0 += OB) {
+    const int ob1 = min(in, ob0 + OB);
+    for (int b0 = ob0; b0 < ob1; b0 += PW) {
+      double* errp = Err + (b0 - ob0);  // this panel's columns of the outer block's error matrix
+      if (group != 0 && PW % group == 0)
+        k_panel<true><<<pgrid, dim3(256), 0, stream>>>(Wq, out, in, b0, U, perm, scale_row, qmax, group, n_groups,
+                                                       codes, scales, errp, OB, row_loss);
+      else
+        k_panel<false><<<pgrid, dim3(256), 0, stream>>>(Wq, out, in, b0, U, perm, scale_row, qmax, group, n_groups,
+                                                        codes, scales, errp, OB, row_loss);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      const int b1 = b0 + PW;
+      if (b1 < ob1) {  // the rest of the outer block: W[:, b1:ob1] -= Err[:, panel] U[b0:b1, b1:ob1]
+        DgemmArgs t{};
+        t.A = errp; t.lda = OB;
+        t.B = U + (int64_t)b0 * in + b1; t.ldb = in;
+        t.C = Wq + b1; t.ldc = in;
+        t.M = out; t.N = ob1 - b1; t.K = PW;
+        t.alpha = -1.0; t.beta = 1.0;
+        t.kmode = KMODE_FULL;
+        e = dgemm_launch(t, false, false, 1, stream);
+        if (e != hipSuccess) return e;
+      }
+    }
+    if (ob1 < in) {  // every later column: W[:, ob1:] -= Err[:, block] U[ob0:ob1, ob1:]
       DgemmArgs t{};
-      t.A = Err; t.lda = PW;
-      t.B = U + (int64_t)b0 * in + b1; t.ldb = in;
-      t.C = Wq + b1; t.ldc = in;
-      t.M = out; t.N = in - b1; t.K = PW;
+      t.A = Err; t.lda = OB;
+      t.B = U + (int64_t)ob0 * in + ob1; t.ldb = in;
+      t.C = Wq + ob1; t.ldc = in;
+      t.M = out; t.N = in - ob1; t.K = ob1 - ob0;
       t.alpha = -1.0; t.beta = 1.0;
       t.kmode = KMODE_FULL;
       e = dgemm_launch(t, false, false, 1, stream);
