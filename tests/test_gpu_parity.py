@@ -31,6 +31,10 @@ HESS_CASES = [
     _cfg("f32_ragged", 40, 300, 333, dtype="f32", w_std=0.05, w_seed=15, x_seed=16),
 ]
 
+# wider than two 1024-column outer blocks of the quantize loop, with a ragged last panel: covers the
+# outer-block updates and their side-stream look-ahead
+WIDE = _cfg("bf16_wide", 40, 2600, 4096, dtype="bf16", w_std=0.02, outlier_channels=8, w_seed=17, x_seed=18)
+
 
 @pytest.mark.parametrize("cfg", HESS_CASES, ids=lambda c: c.name)
 def test_hessian_matches_oracle(cfg):
@@ -92,7 +96,7 @@ def _oracle_prep(cfg, act_order, damp=0.01):
 
 
 PREP_CASES = [(HESS_CASES[1], False), (HESS_CASES[1], True), (HESS_CASES[3], True), (HESS_CASES[4], False),
-              (HESS_CASES[2], False)]
+              (HESS_CASES[2], False), (WIDE, True)]
 
 
 @pytest.mark.parametrize("flags", [G.GPTQ_FACTOR_INVERSE_RECHOL, G.GPTQ_FACTOR_REVERSED], ids=["rechol", "reversed"])
@@ -157,6 +161,8 @@ QUANT_CASES = [
     (HESS_CASES[3], 8, 16, True),
     (HESS_CASES[4], 2, 64, False),
     (HESS_CASES[2], 4, 128, False),
+    (WIDE, 4, 128, True),
+    (WIDE, 3, 0, False),
 ]
 
 
@@ -191,6 +197,7 @@ E2E_CASES = [
     (HESS_CASES[1], 2, 0, True),
     (HESS_CASES[2], 4, 128, False),
     (HESS_CASES[3], 3, 128, True),
+    (WIDE, 4, 0, True),
 ]
 
 
