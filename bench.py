@@ -33,12 +33,37 @@ def parse():
     ap.add_argument("--config", default="q_proj", help="workload name (q_proj, up_gate, down, tiny, teacher)")
     ap.add_argument("--factor", choices=["rechol", "reversed"], default="reversed")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-rows", type=int, default=16384)
-    ap.add_argument("--cpu-loop-rows", type=int, default=32)
+    ap.add_argument("--cpu-sample-rows", type=int, default=65536)
+    ap.add_argument("--cpu-loop-rows", type=int, default=64)
     ap.add_argument("--mode", choices=["layer", "hessian", "copy"], default="layer",
                     help="layer: the timed benchmark; hessian: only the accumulate calls (for counter "
                          "passes); copy: a plain 1 GiB device copy (calibrates FETCH_SIZE/WRITE_SIZE)")
     return ap.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_xtx_bf16_dma_q_proj_traffic.md")
+HESSIAN_SRC = os.path.join(ROOT, "post_weight_quantization_05_amd", "csrc", "hessian.hip")
+
+
+def hessian_traffic():
+    """HBM bytes per launch of the Hessian kernel from the committed counter summary (FETCH_SIZE and
+    WRITE_SIZE scaled by a plain-copy calibration), or None when that summary was taken on a different
+    version of the kernel source than the one built here."""
+    import hashlib
+    try:
+        fields = {}
+        with open(TRAFFIC_FILE) as f:
+            for line in f:
+                if ":" in line and not line.startswith(("#", "|", " ")):
+                    k, v = line.split(":", 1)
+                    fields[k.strip().strip("`*- ")] = v.strip().strip("`* ")
+        with open(HESSIAN_SRC, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+        if fields.get("source_sha256") != sha:
+            return None
+        return float(fields["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(cfg, W, X, sample_rows, loop_rows):
@@ -204,13 +229,13 @@ def main():
                                f"act_order {cfg.act_order}, damp {cfg.damp}",
                    "factor_route": args.factor},
         "roofline": {
-            "kernel": "k_xtx_bf16 (Hessian X^T X, lower triangle)",
+            "kernel": "k_xtx_bf16_dma (Hessian X^T X, lower triangle)",
             "bound": "mfma",
             "achieved": round(achieved, 1),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": hessian_traffic(),
             "algorithmic_per_launch": f"{hess_flops:.4e} flop (n*in*(in+1)), {x_bytes:.4e} B of X",
             "launch_ms": round(hess_ms, 4),
         },
