@@ -36,7 +36,7 @@ struct HessianPlan {
   int n_tiles;     // lower-triangle tiles = n_tb (n_tb + 1) / 2
   int splits;      // row slices (split-K)
   int64_t rows_per_split;
-  size_t part_bytes, colsq_part_bytes, counter_bytes, total_bytes;
+  size_t part_bytes, colsq_part_bytes, total_bytes;
 };
 HessianPlan hessian_plan(int64_t n_rows, int64_t in, int dtype);
 hipError_t hessian_launch(const HessianPlan& p, const void* X, double* S, double* colsq, void* ws,

@@ -6,19 +6,19 @@
 // Design (bf16 X, the transformer workloads):
 //  * Output tiles of 256 x 256 over the lower triangle only (i-block >= j-block); the n calibration rows
 //    are cut into `splits` row slices so that tiles x splits fills the chip (split-K).
-//  * One workgroup = 4 waves (2 x 2), each wave a 128 x 128 block of fp32 accumulators fed by
-//    v_mfma_f32_32x32x16_bf16 (bf16 x bf16 products are exact in fp32).
-//  * X is row-major (rows = tokens), so a tile of 32 rows x 256 columns is read with 16-byte coalesced
-//    loads and stored to LDS as [k][i]. The MFMA operands need 8 consecutive k per lane: they are read
-//    with ds_read_b64_tr_b16, which transposes a 4 x 16 block of 16-bit elements across 16 lanes.
-//  * Double-buffered LDS, one barrier per 32-row stage; the next stage's global loads are in flight
-//    while the current stage's MFMAs run.
-//  * Diagonal tiles read one column block (A = B) and also form the fp64 column sums of squares from
-//    the staged registers (x^2 of a bf16/fp32 value is exact in fp64).
-//  * Each (slice, tile) writes an fp32 partial; a second kernel adds the slices in a fixed order in fp64
-//    to S, so the result is bitwise reproducible.
+//  * X is row-major (rows = tokens). The MFMA operands (v_mfma_f32_32x32x16_bf16; bf16 x bf16 products are
+//    exact in fp32) need 8 consecutive k per lane: they are read from LDS with ds_read_b64_tr_b16, which
+//    transposes a 4 x 16 block of 16-bit elements across 16 lanes.
+//  * Rows 16-byte aligned (k_xtx_bf16_dma): 8 waves of 128 x 64 per tile; 32-row stages of both operand
+//    blocks go HBM -> LDS with buffer_load_dwordx4 ... lds, four stages ahead, no staging registers.
+//    Otherwise (k_xtx_bf16): 4 waves of 128 x 128, register-staged double-buffered loads.
+//  * Diagonal tiles read one column block (A = B); the waves whose block lies above the diagonal form the
+//    fp64 column sums of squares instead (x^2 of a bf16/fp32 value is exact in fp64).
+//  * Each (slice, tile) writes an fp32 partial; a second kernel (k_xtx_reduce) adds the slices in a fixed
+//    order in fp64 to S, so the result is bitwise reproducible.
 //  * Workgroup index -> (slice, tile) is remapped so that the workgroups resident on one XCD (dispatch is
-//    round-robin over the 8 XCDs) work on the same row slice and share its rows in that XCD's L2.
+//    round-robin over the 8 XCDs) work on a narrow set of column blocks of the same row slice and share
+//    those rows in that XCD's L2.
 // fp32 X (small layers) uses the same structure with v_mfma_f32_16x16x4f32 on 128 x 128 tiles; fp32
 // operands need no transpose (one k per lane).
 #include <algorithm>
@@ -111,97 +111,93 @@ __device__ __forceinline__ void sq_accum8(double* acc, uint4 v) {
   }
 }
 
-// Split-K completion: every (slice, tile) workgroup publishes its fp32 partial (release fence, then a
-// per-tile counter); the workgroup that arrives last sums the slices of that tile in slice order in fp64
-// and adds them to S's lower triangle (and, for diagonal tiles, the column sums to colsq). The order of
-// the sum does not depend on which workgroup arrives last, so results are bitwise reproducible.
-// The last workgroup reads splits x TILE^2 floats; it keeps FIN_E x FIN_SB 16-byte loads in flight per
-// thread (two 4-column groups, eight slices each) so that the combine runs at bandwidth, not latency.
-constexpr int FIN_E = 2;
-constexpr int FIN_SB = 8;
+// Split-K combine, a kernel of its own after the accumulation: workgroup (tile, 16-row chunk) sums the
+// slices' fp32 partials of its rows in slice order in fp64 and adds them to S's lower triangle; the first
+// chunk of a diagonal tile also combines that tile's column sums into colsq. The order of every sum is
+// fixed, so results are bitwise reproducible. Each thread keeps FIN_G x FIN_SB 16-byte loads in flight
+// (its 4-column groups, eight slices at a time), and the n_tiles x TILE/16 workgroups spread the
+// combine over every CU.
+constexpr int FIN_RC = 16;  // rows per workgroup
+constexpr int FIN_SB = 8;   // slices in flight
 
 template <int TILE>
-__device__ __forceinline__ void finish_tile(int t, int I, int J, bool diag, int d, int n_tiles, int splits,
-                                            const float* __restrict__ part, const double* __restrict__ colsq_part,
-                                            int colsq_stride, unsigned* __restrict__ counters,
-                                            double* __restrict__ S, double* __restrict__ colsq, int* s_last) {
+__global__ __launch_bounds__(256) void k_xtx_reduce(const float* __restrict__ part,
+                                                    const double* __restrict__ colsq_part, int colsq_stride,
+                                                    int n_tiles, int splits, int d, double* __restrict__ S,
+                                                    double* __restrict__ colsq) {
+  constexpr int Q = TILE / 4;                 // 4-column groups per tile row
+  constexpr int NCH = TILE / FIN_RC;          // row chunks per tile
+  constexpr int FIN_G = FIN_RC * Q / 256;     // groups per thread
+  static_assert(FIN_G * 256 == FIN_RC * Q, "groups per thread");
+  const int t = blockIdx.x / NCH, rc = blockIdx.x - (blockIdx.x / NCH) * NCH;
+  int I, J;
+  tile_coords(t, I, J);
   const int tid = threadIdx.x;
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) *s_last = (atomicAdd(&counters[t], 1u) == (unsigned)(splits - 1)) ? 1 : 0;
-  __syncthreads();
-  if (!*s_last) return;
-  __threadfence();
-  constexpr int Q = TILE / 4;    // 4-column groups per tile row
-  constexpr int NE = TILE * Q;   // 4-column groups per tile
   const int64_t tsz = (int64_t)TILE * TILE;
   const int64_t sstride4 = (int64_t)n_tiles * tsz / 4;  // one slice's partials, in float4
   const float4* p0 = reinterpret_cast<const float4*>(part + (int64_t)t * tsz);
-  const int nthr = blockDim.x;
-  for (int e0 = tid; e0 < NE; e0 += FIN_E * nthr) {
-    int gi[FIN_E], gj[FIN_E];
-    bool live[FIN_E];
-    double acc[FIN_E][4];
+  int e4[FIN_G], gi[FIN_G], gj[FIN_G];
+  bool live[FIN_G];
+  double acc[FIN_G][4];
 #pragma unroll
-    for (int k = 0; k < FIN_E; ++k) {
-      const int e = e0 + k * nthr;
-      gi[k] = I * TILE + e / Q;
-      gj[k] = J * TILE + (e % Q) * 4;
-      live[k] = e < NE && gi[k] < d && gj[k] <= gi[k] && gj[k] < d;
+  for (int k = 0; k < FIN_G; ++k) {
+    const int e = tid + 256 * k;               // group within the chunk
+    const int r = rc * FIN_RC + e / Q, c4 = (e % Q) * 4;
+    e4[k] = r * Q + e % Q;                     // float4 index within the tile
+    gi[k] = I * TILE + r;
+    gj[k] = J * TILE + c4;
+    live[k] = gi[k] < d && gj[k] <= gi[k] && gj[k] < d;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) acc[k][c] = 0.0;
-    }
-    for (int s0 = 0; s0 < splits; s0 += FIN_SB) {
-      // unconditional loads from clamped (valid) addresses, then a select: no branch between the loads
-      float4 v[FIN_E][FIN_SB];
-#pragma unroll
-      for (int k = 0; k < FIN_E; ++k)
-#pragma unroll
-        for (int u = 0; u < FIN_SB; ++u) {
-          const int e = min(e0 + k * nthr, NE - 1);
-          const int sl = min(s0 + u, splits - 1);
-          const float4 x = p0[e + (int64_t)sl * sstride4];
-          const bool use = live[k] && s0 + u < splits;
-          v[k][u] = make_float4(use ? x.x : 0.f, use ? x.y : 0.f, use ? x.z : 0.f, use ? x.w : 0.f);
-        }
-      // slice order; a slice past the end adds an exact zero
-#pragma unroll
-      for (int k = 0; k < FIN_E; ++k)
-#pragma unroll
-        for (int u = 0; u < FIN_SB; ++u) {
-          acc[k][0] += (double)v[k][u].x;
-          acc[k][1] += (double)v[k][u].y;
-          acc[k][2] += (double)v[k][u].z;
-          acc[k][3] += (double)v[k][u].w;
-        }
-    }
-    // read the S entries first (clamped to valid addresses), then store only the lower-triangle ones
-    double old[FIN_E][4];
-#pragma unroll
-    for (int k = 0; k < FIN_E; ++k)
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        old[k][c] = S[(int64_t)min(gi[k], d - 1) * d + min(gj[k] + c, d - 1)];
-#pragma unroll
-    for (int k = 0; k < FIN_E; ++k)
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        if (live[k] && gj[k] + c <= gi[k] && gj[k] + c < d) S[(int64_t)gi[k] * d + gj[k] + c] = old[k][c] + acc[k][c];
+    for (int c = 0; c < 4; ++c) acc[k][c] = 0.0;
   }
-  if (diag) {
-    for (int c = tid; c < TILE; c += nthr) {
+  for (int s0 = 0; s0 < splits; s0 += FIN_SB) {
+    // unconditional loads from clamped (valid) addresses, then a select: no branch between the loads
+    float4 v[FIN_G][FIN_SB];
+#pragma unroll
+    for (int k = 0; k < FIN_G; ++k)
+#pragma unroll
+      for (int u = 0; u < FIN_SB; ++u) {
+        const int sl = min(s0 + u, splits - 1);
+        const float4 x = p0[e4[k] + (int64_t)sl * sstride4];
+        const bool use = live[k] && s0 + u < splits;
+        v[k][u] = make_float4(use ? x.x : 0.f, use ? x.y : 0.f, use ? x.z : 0.f, use ? x.w : 0.f);
+      }
+    // slice order; a slice past the end adds an exact zero
+#pragma unroll
+    for (int k = 0; k < FIN_G; ++k)
+#pragma unroll
+      for (int u = 0; u < FIN_SB; ++u) {
+        acc[k][0] += (double)v[k][u].x;
+        acc[k][1] += (double)v[k][u].y;
+        acc[k][2] += (double)v[k][u].z;
+        acc[k][3] += (double)v[k][u].w;
+      }
+  }
+  // read the S entries first (clamped to valid addresses), then store only the lower-triangle ones
+  double old[FIN_G][4];
+#pragma unroll
+  for (int k = 0; k < FIN_G; ++k)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) old[k][c] = S[(int64_t)min(gi[k], d - 1) * d + min(gj[k] + c, d - 1)];
+#pragma unroll
+  for (int k = 0; k < FIN_G; ++k)
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      if (live[k] && gj[k] + c <= gi[k] && gj[k] + c < d) S[(int64_t)gi[k] * d + gj[k] + c] = old[k][c] + acc[k][c];
+  if (I == J && rc == 0) {
+    for (int c = tid; c < TILE; c += 256) {
       const int gc = I * TILE + c;
       if (gc >= d) break;
       double sum = 0.0;
       for (int s0 = 0; s0 < splits; s0 += FIN_SB) {
-        double v[FIN_SB];
+        double w[FIN_SB];
 #pragma unroll
         for (int u = 0; u < FIN_SB; ++u) {
           const double x = colsq_part[(int64_t)min(s0 + u, splits - 1) * colsq_stride + gc];
-          v[u] = (s0 + u < splits) ? x : 0.0;
+          w[u] = (s0 + u < splits) ? x : 0.0;
         }
 #pragma unroll
-        for (int u = 0; u < FIN_SB; ++u) sum += v[u];
+        for (int u = 0; u < FIN_SB; ++u) sum += w[u];
       }
       colsq[gc] += sum;
     }
@@ -212,10 +208,8 @@ template <bool VEC>
 __global__ __launch_bounds__(256, 1) void k_xtx_bf16(const uint16_t* __restrict__ X, int64_t ld, int64_t n_rows,
                                                      int d, int n_tiles, int64_t rps, int remap, int splits,
                                                      float* __restrict__ part, double* __restrict__ colsq_part,
-                                                     int colsq_stride, unsigned* __restrict__ counters,
-                                                     double* __restrict__ S, double* __restrict__ colsq) {
+                                                     int colsq_stride) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][BK][BROW];
-  __shared__ int s_last;
 
   const int G = gridDim.x;
   const int b = blockIdx.x;
@@ -342,7 +336,6 @@ __global__ __launch_bounds__(256, 1) void k_xtx_bf16(const uint16_t* __restrict_
     for (int rg = 0; rg < 8; ++rg) sum += red[rg * BT + tid];
     colsq_part[(int64_t)split * colsq_stride + colA + tid] = sum;
   }
-  finish_tile<BT>(t, I, J, diag, d, n_tiles, splits, part, colsq_part, colsq_stride, counters, S, colsq, &s_last);
 }
 
 // ---------------------------------------------------------------------------------------------------
@@ -582,8 +575,7 @@ __device__ __forceinline__ void xtx_dma_body(const DmaCtx& c, int nk, f32x16 (&a
 __global__ __launch_bounds__(XWAVES * 64, 1) void k_xtx_bf16_dma(const uint16_t* __restrict__ X, int64_t ld, int64_t n_rows,
                                                          int d, int n_tiles, int64_t rps, int remap, int splits,
                                                          float* __restrict__ part, double* __restrict__ colsq_part,
-                                                         int colsq_stride, unsigned* __restrict__ counters,
-                                                         double* __restrict__ S, double* __restrict__ colsq) {
+                                                         int colsq_stride) {
   // Workgroup b runs on XCD b % 8 (round-robin dispatch). Each XCD owns a contiguous run of `cs` tiles in
   // super-tile order and walks the row slices in order; all XCDs are on the same slices at the same time,
   // so each slice comes from HBM about once and the XCDs share it through the last-level cache.
@@ -660,9 +652,6 @@ __global__ __launch_bounds__(XWAVES * 64, 1) void k_xtx_bf16_dma(const uint16_t*
       colsq_part[(int64_t)split * colsq_stride + c.colA + tid] = sum;
     }
   }
-  // the ring fills LDS; the completion flag lives in a drained stage buffer
-  finish_tile<BT>(t, I, J, diag, d, n_tiles, splits, part, colsq_part, colsq_stride, counters, S, colsq,
-                  reinterpret_cast<int*>(g_stage1));
 }
 
 // ---------------------------------------------------------------------------------------------------
@@ -671,10 +660,8 @@ __global__ __launch_bounds__(XWAVES * 64, 1) void k_xtx_bf16_dma(const uint16_t*
 __global__ __launch_bounds__(256, 1) void k_xtx_f32(const float* __restrict__ X, int64_t ld, int64_t n_rows, int d,
                                                     int n_tiles, int64_t rps, int remap, int splits,
                                                     float* __restrict__ part, double* __restrict__ colsq_part,
-                                                    int colsq_stride, unsigned* __restrict__ counters,
-                                                    double* __restrict__ S, double* __restrict__ colsq) {
+                                                    int colsq_stride) {
   __shared__ __attribute__((aligned(16))) float lds[2][2][FK][FROW];
-  __shared__ int s_last;
   const int G = gridDim.x;
   const int b = blockIdx.x;
   const int L = remap ? (b % 8) * (G / 8) + b / 8 : b;
@@ -780,12 +767,6 @@ __global__ __launch_bounds__(256, 1) void k_xtx_f32(const float* __restrict__ X,
       colsq_part[(int64_t)split * colsq_stride + colA + tid] = sum;
     }
   }
-  finish_tile<FT>(t, I, J, diag, d, n_tiles, splits, part, colsq_part, colsq_stride, counters, S, colsq, &s_last);
-}
-
-__global__ void k_zero_counters(unsigned* __restrict__ c, int n) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) c[i] = 0u;
 }
 
 }  // namespace
@@ -821,8 +802,7 @@ HessianPlan hessian_plan(int64_t n_rows, int64_t in, int dtype) {
   p.splits = (int)ceil_div(n_rows, p.rows_per_split);
   p.part_bytes = align_up((size_t)p.splits * p.n_tiles * p.tile * p.tile * sizeof(float), 256);
   p.colsq_part_bytes = align_up((size_t)p.splits * p.n_tb * p.tile * sizeof(double), 256);
-  p.counter_bytes = align_up((size_t)p.n_tiles * sizeof(unsigned), 256);
-  p.total_bytes = p.part_bytes + p.colsq_part_bytes + p.counter_bytes;
+  p.total_bytes = p.part_bytes + p.colsq_part_bytes;
   p.ld = 0;
   return p;
 }
@@ -831,35 +811,34 @@ hipError_t hessian_launch(const HessianPlan& p, const void* X, double* S, double
                           hipStream_t stream) {
   float* part = reinterpret_cast<float*>(ws);
   double* cpart = reinterpret_cast<double*>(reinterpret_cast<char*>(ws) + p.part_bytes);
-  unsigned* counters = reinterpret_cast<unsigned*>(reinterpret_cast<char*>(ws) + p.part_bytes + p.colsq_part_bytes);
   const int grid = p.splits * p.n_tiles;
   const int remap = (grid % 8 == 0) ? 1 : 0;
   const int cs = (p.n_tiles + 7) / 8;         // tiles per XCD for the direct-to-LDS kernel
   const int grid_dma = 8 * cs * p.splits;
   const int cstride = p.n_tb * p.tile;
-  // counters start at zero on every call (a small fill kernel, safe under stream capture)
-  hipLaunchKernelGGL(k_zero_counters, dim3((unsigned)ceil_div(p.n_tiles, 256)), dim3(256), 0, stream, counters,
-                     p.n_tiles);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   if (p.dtype == GPTQ_BF16) {
     const bool vec = (p.ld % 8 == 0) && (p.in % 8 == 0) && ((reinterpret_cast<uintptr_t>(X) & 15) == 0);
     const bool dma = vec && (p.rows_per_split * p.ld * 2 < ((int64_t)1 << 31));
     if (dma)
       hipLaunchKernelGGL(k_xtx_bf16_dma, dim3(grid_dma), dim3(XWAVES * 64), 0, stream, (const uint16_t*)X, p.ld,
-                         p.n_rows, (int)p.in, p.n_tiles, p.rows_per_split, cs, p.splits, part, cpart, cstride,
-                         counters, S, colsq);
+                         p.n_rows, (int)p.in, p.n_tiles, p.rows_per_split, cs, p.splits, part, cpart, cstride);
     else if (vec)
       hipLaunchKernelGGL(k_xtx_bf16<true>, dim3(grid), dim3(256), 0, stream, (const uint16_t*)X, p.ld, p.n_rows,
-                         (int)p.in, p.n_tiles, p.rows_per_split, remap, p.splits, part, cpart, cstride, counters, S,
-                         colsq);
+                         (int)p.in, p.n_tiles, p.rows_per_split, remap, p.splits, part, cpart, cstride);
     else
       hipLaunchKernelGGL(k_xtx_bf16<false>, dim3(grid), dim3(256), 0, stream, (const uint16_t*)X, p.ld, p.n_rows,
-                         (int)p.in, p.n_tiles, p.rows_per_split, remap, p.splits, part, cpart, cstride, counters, S,
-                         colsq);
+                         (int)p.in, p.n_tiles, p.rows_per_split, remap, p.splits, part, cpart, cstride);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_xtx_reduce<BT>, dim3((unsigned)(p.n_tiles * (BT / FIN_RC))), dim3(256), 0, stream, part,
+                       cpart, cstride, p.n_tiles, p.splits, (int)p.in, S, colsq);
   } else {
     hipLaunchKernelGGL(k_xtx_f32, dim3(grid), dim3(256), 0, stream, (const float*)X, p.ld, p.n_rows, (int)p.in,
-                       p.n_tiles, p.rows_per_split, remap, p.splits, part, cpart, cstride, counters, S, colsq);
+                       p.n_tiles, p.rows_per_split, remap, p.splits, part, cpart, cstride);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_xtx_reduce<FT>, dim3((unsigned)(p.n_tiles * (FT / FIN_RC))), dim3(256), 0, stream, part,
+                       cpart, cstride, p.n_tiles, p.splits, (int)p.in, S, colsq);
   }
   return hipGetLastError();
 }
