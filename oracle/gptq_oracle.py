@@ -19,6 +19,8 @@ What is computed (the method is a greedy sequential rounding heuristic, so the o
      with per-row scales from the starting weights, or per-group scales from the updated weights at each
      group boundary                                                  ([guide] "The code, line by line")
   7. codes back to the original column order, g_idx for act_order+groups ([guide] "When it breaks")
+  8. the same loop on the asymmetric grid: levels 0..2^b-1, (scale, zero) from min/max of the row or group
+     ([guide] "Simplifications": the paper's default; [handbook] quantize_weight, gptq_quantize_row)
 
 Readings where the pages leave a detail open (each is also listed with the build's design notes):
   * qmax for b bits is 2^(b-1) - 1 (the lesson's starter code; "2-bit" = ternary {-s, 0, s} in the guide).
@@ -29,6 +31,10 @@ Readings where the pages leave a detail open (each is also listed with the build
   * U for the permuted problem equals the factor of P^T H P (dead fix and damping commute with P).
   * g_idx[perm[j]] = j // group: groups are formed in quantization order.
   * Output error of a quantized layer is ||X (W - Q)^T||_F^2, relative to ||X W^T||_F^2 ([guide] simulations).
+  * Asymmetric grid: min/max over the weights themselves (0 is not forced into the range); the zero point
+    is clipped to the levels, so a group of all-positive (or all-negative) weights saturates at one end,
+    as the handbook's formulas do. Per-row mode takes (scale, zero) from the starting weights, groups
+    from the current weights at the group start (the handbook's per-column loop does the latter).
 """
 from __future__ import annotations
 
@@ -252,6 +258,141 @@ def rtn(W64: np.ndarray, bits: int, group: int = 0, dead: np.ndarray | None = No
     codes[:, perm] = codes_q
     Q[:, perm] = Qq
     return codes, Q
+
+
+# ---------------------------------------------------------------------------------------------
+# The asymmetric grid (min/max plus a zero point)
+# ---------------------------------------------------------------------------------------------
+# [guide] "Simplifications": the paper's default quantizer is asymmetric, min/max plus a zero point.
+# [handbook] "quantize_weight" / "dequantize_weight" and the group parameters in "gptq_quantize_row" give
+# the formulas: levels 0 .. 2^bits - 1; over a group's current weights, scale = (max - min) / (2^bits - 1)
+# when max > min and 1 otherwise; zero = round(-min / scale) clipped to the levels; a weight's code is
+# round(w / scale + zero) clipped to the levels, and its value is scale * (code - zero). Python's round
+# rounds half to even, as numpy's does. The error-compensation loop around the quantizer is the same.
+def asym_levels(bits: int) -> int:
+    """Largest code of the asymmetric grid {0..2^bits - 1}."""
+    if bits < 2:
+        raise ValueError("bits must be >= 2")
+    return 2 ** bits - 1
+
+
+def asym_params(Wblock: np.ndarray, bits: int):
+    """Per-row (scale, zero) of a block of columns ([handbook] group parameters)."""
+    levels = asym_levels(bits)
+    wmin = Wblock.min(axis=1)
+    wmax = Wblock.max(axis=1)
+    scale = np.where(wmax > wmin, (wmax - wmin) / levels, 1.0)
+    zero = np.clip(np.round(-wmin / scale), 0, levels)
+    return scale, zero
+
+
+def asym_code(w: np.ndarray, scale: np.ndarray, zero: np.ndarray, bits: int) -> np.ndarray:
+    """round(w / scale + zero) clipped to 0 .. 2^bits - 1 ([handbook] quantize_weight)."""
+    return np.clip(np.round(w / scale + zero), 0, asym_levels(bits))
+
+
+def asym_value(c: np.ndarray, scale: np.ndarray, zero: np.ndarray) -> np.ndarray:
+    """scale * (code - zero) ([handbook] dequantize_weight)."""
+    return scale * (c - zero)
+
+
+def compensation_loop_asym(W0: np.ndarray, U: np.ndarray, bits: int, group: int = 0):
+    """The loop of compensation_loop with the asymmetric grid: (scale, zero) per row from the starting
+    weights, or, with groups, from the current weights of columns [j, j + group) at each group start.
+
+    Returns codes (int64, 0..2^bits-1, quantization order), scales and zeros (out x G), errs, loss.
+    """
+    W = np.array(W0, dtype=np.float64, copy=True)
+    out, d = W.shape
+    n_groups = -(-d // group) if group else 1
+    codes = np.zeros((out, d), dtype=np.int64)
+    scales = np.zeros((out, n_groups))
+    zeros = np.zeros((out, n_groups))
+    errs = np.zeros((out, d))
+    scale, zero = asym_params(W, bits)
+    if not group:
+        scales[:, 0], zeros[:, 0] = scale, zero
+    for j in range(d):
+        if group and j % group == 0:
+            scale, zero = asym_params(W[:, j:j + group], bits)
+            scales[:, j // group], zeros[:, j // group] = scale, zero
+        w = W[:, j]
+        c = asym_code(w, scale, zero, bits)
+        q = asym_value(c, scale, zero)
+        e = (w - q) / U[j, j]
+        codes[:, j] = c.astype(np.int64)
+        errs[:, j] = e
+        if j + 1 < d:
+            W[:, j + 1:] -= np.outer(e, U[j, j + 1:])
+    loss = np.einsum("rj,rj->r", errs, errs)
+    return codes, scales, zeros, errs, loss
+
+
+def finalize_asym(codes_q: np.ndarray, scales: np.ndarray, zeros: np.ndarray, perm: np.ndarray, group: int):
+    """codes in original order, g_idx, and Q = scales[:, g_idx] * (codes - zeros[:, g_idx])."""
+    codes = np.empty_like(codes_q)
+    codes[:, perm] = codes_q
+    g_idx = group_index(perm, group)
+    Q = asym_value(codes, scales[:, g_idx], zeros[:, g_idx])
+    return codes, g_idx, Q
+
+
+def gptq_oracle_asym(W64: np.ndarray, X64: np.ndarray | None = None, bits: int = 4, group: int = 0,
+                     damp: float = 0.01, act_order: bool = False, hessian=None) -> dict:
+    """gptq_oracle with the asymmetric grid; the dict also holds `zeros`."""
+    if hessian is None:
+        S, colsq, n = hessian_from_x(X64)
+    else:
+        S, colsq, n = hessian
+    H_p, perm, dead, lam = prepare(S, colsq, n, damp, act_order)
+    U = upper_factor_of_inverse(H_p)
+    W0 = start_weights(W64, perm, dead)
+    codes_q, scales, zeros, errs, loss = compensation_loop_asym(W0, U, bits, group)
+    codes, g_idx, Q = finalize_asym(codes_q, scales, zeros, perm, group)
+    return dict(S=S, colsq=colsq, n=n, H_p=H_p, perm=perm, dead=dead, lam=lam, U=U, W0=W0,
+                codes_q=codes_q, codes=codes, scales=scales, zeros=zeros, g_idx=g_idx, Q=Q, errs=errs,
+                loss=loss)
+
+
+def rtn_asym(W64: np.ndarray, bits: int, group: int = 0, dead: np.ndarray | None = None,
+             perm: np.ndarray | None = None):
+    """Asymmetric round-to-nearest: (scale, zero) from the starting weights, no compensation."""
+    d = W64.shape[1]
+    perm = np.arange(d) if perm is None else perm
+    dead = np.zeros(d, dtype=bool) if dead is None else dead
+    W0 = start_weights(W64, perm, dead)
+    codes_q = np.zeros(W0.shape, dtype=np.int64)
+    Qq = np.zeros(W0.shape)
+    for g0 in range(0, d, group if group else d):
+        g1 = min(d, g0 + group) if group else d
+        s, z = asym_params(W0[:, g0:g1], bits)
+        c = asym_code(W0[:, g0:g1], s[:, None], z[:, None], bits)
+        codes_q[:, g0:g1] = c.astype(np.int64)
+        Qq[:, g0:g1] = asym_value(c, s[:, None], z[:, None])
+    codes = np.empty_like(codes_q)
+    Q = np.empty_like(Qq)
+    codes[:, perm] = codes_q
+    Q[:, perm] = Qq
+    return codes, Q
+
+
+def forced_replay_asym(W0: np.ndarray, U: np.ndarray, bits: int, group: int, forced_codes_q: np.ndarray):
+    """forced_replay with the asymmetric grid: dist = |clip(w / scale + zero, 0, levels) - c|."""
+    levels = asym_levels(bits)
+    W = np.array(W0, dtype=np.float64, copy=True)
+    out, d = W.shape
+    dist = np.zeros((out, d))
+    scale, zero = asym_params(W, bits)
+    for j in range(d):
+        if group and j % group == 0:
+            scale, zero = asym_params(W[:, j:j + group], bits)
+        w = W[:, j]
+        c = forced_codes_q[:, j].astype(np.float64)
+        dist[:, j] = np.abs(np.clip(w / scale + zero, 0, levels) - c)
+        e = (w - asym_value(c, scale, zero)) / U[j, j]
+        if j + 1 < d:
+            W[:, j + 1:] -= np.outer(e, U[j, j + 1:])
+    return dist
 
 
 # ---------------------------------------------------------------------------------------------

@@ -16,7 +16,10 @@ namespace gptq {
 
 namespace {
 
-constexpr int TK = 16;
+#ifndef GPTQ_DGEMM_TK
+#define GPTQ_DGEMM_TK 16
+#endif
+constexpr int TK = GPTQ_DGEMM_TK;  // K per LDS chunk
 
 // LDS layouts. An operand whose rows run along the tile's M (or N) dimension in memory (A^T, B) is kept
 // as [k][i] with rows padded to T + 16 doubles: the 16 consecutive i that a 16-lane group reads sit on
@@ -27,7 +30,7 @@ constexpr int TK = 16;
 template <int T>
 struct Lds {
   static constexpr int KI = T + 16;  // [k][i] row stride
-  static constexpr int IK = TK + 2;  // [i][k] row stride
+  static constexpr int IK = TK + 2;  // [i][k] row stride (= 2 mod 32)
   static constexpr int SZ = (TK * KI > T * IK) ? TK * KI : T * IK;
 };
 
@@ -101,7 +104,7 @@ __global__ __launch_bounds__(256, (T == 128) ? 2 : 1) void k_dgemm(DgemmArgs a) 
     for (int q = 0; q < NV; ++q) {
       const int e = tid + 256 * q;
       if (!TA) {
-        const int ii = e >> 3, kk = (e & 7) * 2;
+        const int ii = e / (TK / 2), kk = (e % (TK / 2)) * 2;
         ra[q] = ld2(A, a.lda, i0 + ii, k0 + kk, M, klo, khi, a_vec);
       } else {
         const int kk = e / (T / 2), ii = (e % (T / 2)) * 2;
@@ -111,7 +114,7 @@ __global__ __launch_bounds__(256, (T == 128) ? 2 : 1) void k_dgemm(DgemmArgs a) 
         const int kk = e / (T / 2), jj = (e % (T / 2)) * 2;
         rb[q] = (k0 + kk < khi) ? ld2(B, a.ldb, k0 + kk, j0 + jj, K, 0, N, b_vec) : make_double2(0.0, 0.0);
       } else {
-        const int jj = e >> 3, kk = (e & 7) * 2;
+        const int jj = e / (TK / 2), kk = (e % (TK / 2)) * 2;
         rb[q] = ld2(B, a.ldb, j0 + jj, k0 + kk, N, klo, khi, b_vec);
       }
     }
@@ -120,15 +123,15 @@ __global__ __launch_bounds__(256, (T == 128) ? 2 : 1) void k_dgemm(DgemmArgs a) 
 #pragma unroll
     for (int q = 0; q < NV; ++q) {
       const int e = tid + 256 * q;
-      if (!TA) *reinterpret_cast<double2*>(&As[st][(e >> 3) * L::IK + (e & 7) * 2]) = ra[q];
+      if (!TA) *reinterpret_cast<double2*>(&As[st][(e / (TK / 2)) * L::IK + (e % (TK / 2)) * 2]) = ra[q];
       else *reinterpret_cast<double2*>(&As[st][(e / (T / 2)) * L::KI + (e % (T / 2)) * 2]) = ra[q];
       if (!TB) *reinterpret_cast<double2*>(&Bs[st][(e / (T / 2)) * L::KI + (e % (T / 2)) * 2]) = rb[q];
-      else *reinterpret_cast<double2*>(&Bs[st][(e >> 3) * L::IK + (e & 7) * 2]) = rb[q];
+      else *reinterpret_cast<double2*>(&Bs[st][(e / (TK / 2)) * L::IK + (e % (TK / 2)) * 2]) = rb[q];
     }
   };
 
-  // v_mfma_f64_4x4x4f64 runs four independent 4 x 4 x 4 products per instruction at the full fp64 rate
-  // (the 16 x 16 x 4 form runs at half of it). Block b of an instruction takes A[i][k] from lane
+  // v_mfma_f64_4x4x4f64 runs four independent 4 x 4 x 4 products per instruction at the fp64 rate.
+  // Block b of an instruction takes A[i][k] from lane
   // 16 k + 4 b + i, B[k][j] from lane 16 k + 4 b + j and leaves D[i][j] in lane 16 i + 4 b + j. Giving
   // all four blocks the same 4 rows of A and consecutive 4-column groups of B makes one instruction a
   // 4 x 16 tile of C: lane l supplies A[r0 + l % 4][k0 + l / 16] and B[k0 + l / 16][c0 + l % 16] and

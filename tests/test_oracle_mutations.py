@@ -134,3 +134,105 @@ def test_pins_catch_planted_mistake(monkeypatch, name, factory, kind):
         except (AssertionError, np.linalg.LinAlgError, FloatingPointError, ValueError, IndexError):
             caught.append(fn.__name__)
     assert caught, f"no pin caught mutation {name}:{kind}"
+
+
+# ------------------------------------------------------------------------------------------------
+# The asymmetric grid: mistakes in its parameters, its rounding or its loop
+# ------------------------------------------------------------------------------------------------
+import tests.test_oracle_pins_asym as PA  # noqa: E402
+
+
+def _asym_params_factory(kind):
+    def params(Wblock, bits):
+        levels = 2 ** bits - 1
+        if kind == "symmetric_levels":
+            levels = 2 ** (bits - 1) - 1
+        wmin = Wblock.min(axis=1)
+        wmax = Wblock.max(axis=1)
+        if kind == "levels_off_by_one":
+            scale = np.where(wmax > wmin, (wmax - wmin) / (levels + 1), 1.0)
+        else:
+            scale = np.where(wmax > wmin, (wmax - wmin) / levels, 1.0)
+        if kind == "zero_sign":
+            zero = np.clip(np.round(wmin / scale), 0, levels)
+        elif kind == "zero_unclipped":
+            zero = np.round(-wmin / scale)
+        else:
+            zero = np.clip(np.round(-wmin / scale), 0, levels)
+        return scale, zero
+    return params
+
+
+def _asym_value_factory(kind):
+    def value(c, scale, zero):
+        if kind == "no_zero_shift":
+            return scale * c
+        raise ValueError(kind)
+    return value
+
+
+def _asym_loop_factory(kind):
+    def loop(W0, U, bits, group=0):
+        W = np.array(W0, dtype=np.float64, copy=True)
+        orig = W.copy()
+        out, d = W.shape
+        n_groups = -(-d // group) if group else 1
+        codes = np.zeros((out, d), dtype=np.int64)
+        scales = np.zeros((out, n_groups))
+        zeros = np.zeros((out, n_groups))
+        errs = np.zeros((out, d))
+        scale, zero = O.asym_params(W, bits)
+        if not group:
+            scales[:, 0], zeros[:, 0] = scale, zero
+        for j in range(d):
+            if group and j % group == 0:
+                src = orig if kind == "group_from_original" else W
+                scale, zero = O.asym_params(src[:, j:j + group], bits)
+                scales[:, j // group], zeros[:, j // group] = scale, zero
+            w = W[:, j]
+            c = O.asym_code(w, scale, zero, bits)
+            q = O.asym_value(c, scale, zero)
+            e = (w - q) / U[j, j]
+            if kind == "error_before_clip":
+                e = (w - scale * (np.round(w / scale + zero) - zero)) / U[j, j]
+            codes[:, j] = c.astype(np.int64)
+            errs[:, j] = e
+            if j + 1 < d:
+                W[:, j + 1:] -= np.outer(e, U[j, j + 1:])
+        loss = np.einsum("rj,rj->r", errs, errs)
+        return codes, scales, zeros, errs, loss
+    return loop
+
+
+PINS_ASYM = [
+    (PA.test_grid_hand_values, ()),
+    (PA.test_grid_end_points_and_half_step_bound, (3,)),
+    (PA.test_loop_matches_exact_rational_obs_asym, (0,)),
+    (PA.test_loop_matches_exact_rational_obs_asym, (2,)),
+    (PA.test_loop_matches_exact_rational_obs_asym, (5,)),
+    (PA.test_heavy_damping_is_rtn_asym, (3, 32)),
+    (PA.test_loss_identity_asym, (4, True)),
+    (PA.test_outputs_consistent_asym, ()),
+    (PA.test_output_error_below_rtn_asym, (3,)),
+]
+
+MUTATIONS_ASYM = [
+    ("asym_params", _asym_params_factory, k) for k in
+    ["symmetric_levels", "levels_off_by_one", "zero_sign", "zero_unclipped"]
+] + [
+    ("asym_value", _asym_value_factory, "no_zero_shift"),
+] + [
+    ("compensation_loop_asym", _asym_loop_factory, k) for k in ["group_from_original", "error_before_clip"]
+]
+
+
+@pytest.mark.parametrize("name,factory,kind", MUTATIONS_ASYM, ids=[f"{m[0]}-{m[2]}" for m in MUTATIONS_ASYM])
+def test_asym_pins_catch_planted_mistake(monkeypatch, name, factory, kind):
+    monkeypatch.setattr(O, name, factory(kind))
+    caught = []
+    for fn, args in PINS_ASYM:
+        try:
+            fn(*args)
+        except (AssertionError, np.linalg.LinAlgError, FloatingPointError, ValueError, IndexError):
+            caught.append(fn.__name__)
+    assert caught, f"no pin caught mutation {name}:{kind}"
