@@ -113,8 +113,8 @@ int gptq_prepare_chol(const double* S, const double* colsq, int64_t n_total, int
  *    "The code, line by line" (per-row scales from the starting weights; with groups, scales from the
  *    already-updated weights at each group boundary; clip to +-qmax) and "When it breaks" (g_idx).
  *    The guide's "Simplifications" mentions lazy updates in 128-column blocks; this library quantizes
- *    128-column panels in registers and applies each panel's errors to the columns on its right as one
- *    matrix product, which computes the same loop.
+ *    128-column panels in registers and applies the panels' errors to the columns on their right as
+ *    matrix products (two levels of lazy updates), which computes the same loop.
  *
  *  W          out x in, leading dimension ld_w >= in, dtype w_dtype (GPTQ_F32 or GPTQ_BF16).
  *  U, perm, dead  as produced by gptq_prepare_chol (or supplied by the caller with the same meaning).
@@ -140,6 +140,34 @@ int gptq_quantize_layer(const void* W, int w_dtype, int64_t out, int64_t in, int
                         int bits, int group,
                         int8_t* codes, float* scales, int32_t* g_idx, double* row_loss,
                         void* ws, size_t ws_bytes, void* stream);
+
+/* Quantization grid for gptq_quantize_layer_ex (`grid`). */
+typedef enum { GPTQ_GRID_SYMMETRIC = 0, GPTQ_GRID_ASYMMETRIC = 1 } gptq_grid;
+
+/* ---------------------------------------------------------------------------------------------------
+ * 3'. The same loop on a chosen grid. GPTQ guide, "Simplifications": the paper's default quantizer is
+ *    asymmetric (min/max plus a zero point). Handbook page "GPTQ > Implementation with AutoGPTQ",
+ *    quantize_weight / dequantize_weight / gptq_quantize_row, gives the formulas used here.
+ *
+ *  grid       GPTQ_GRID_SYMMETRIC: exactly gptq_quantize_layer (zeros may be NULL and is not written).
+ *             GPTQ_GRID_ASYMMETRIC: levels 0..L, L = 2^bits - 1. For each row (group == 0, from the
+ *             starting weights) or each group (from the already-updated weights at the group's first
+ *             column): scale = (max - min) / L, or 1 when max == min; zero = round(-min / scale) clipped
+ *             to [0, L]. code = round(w / scale + zero) clipped to [0, L]; the loop's quantized value is
+ *             scale * (code - zero). Every rounding is to nearest, ties to even; divisions are correctly
+ *             rounded. min and max are of the weights themselves (0 is not added to the range).
+ *  codes      asymmetric: values 0..L stored as their uint8 bit pattern (read the buffer as uint8 when
+ *             bits == 8).
+ *  zeros      out (required for the asymmetric grid): int32, out x G, the same layout as scales.
+ *  Dequantized weights (asymmetric): Q[r][c] = scales[r][g] * (codes[r][c] - zeros[r][g]), g = g_idx[c].
+ *  Everything else (arguments, layouts, workspace, errors) is as for gptq_quantize_layer; an unknown grid,
+ *  or the asymmetric grid with zeros == NULL, is INVALID_ARG.
+ * ------------------------------------------------------------------------------------------------- */
+int gptq_quantize_layer_ex(const void* W, int w_dtype, int64_t out, int64_t in, int64_t ld_w,
+                           const double* U, const int32_t* perm, const uint8_t* dead,
+                           int bits, int group, int grid,
+                           int8_t* codes, float* scales, int32_t* zeros, int32_t* g_idx, double* row_loss,
+                           void* ws, size_t ws_bytes, void* stream);
 
 /* Human-readable name of a gptq_status value (static storage). */
 const char* gptq_status_string(int status);

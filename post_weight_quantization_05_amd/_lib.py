@@ -21,6 +21,9 @@ GPTQ_BF16 = 1
 GPTQ_FACTOR_INVERSE_RECHOL = 0
 GPTQ_FACTOR_REVERSED = 1
 
+GPTQ_GRID_SYMMETRIC = 0
+GPTQ_GRID_ASYMMETRIC = 1
+
 # every symbol the header declares, with its ctypes signature
 _c_int64 = ctypes.c_int64
 _vp = ctypes.c_void_p
@@ -37,6 +40,9 @@ SIGNATURES = {
     "gptq_quantize_layer": (ctypes.c_int, [_vp, ctypes.c_int, _c_int64, _c_int64, _c_int64, _vp, _vp, _vp,
                                            ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
                                            _vp]),
+    "gptq_quantize_layer_ex": (ctypes.c_int, [_vp, ctypes.c_int, _c_int64, _c_int64, _c_int64, _vp, _vp, _vp,
+                                              ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _vp, _vp,
+                                              _vp, ctypes.c_size_t, _vp]),
 }
 
 _lib = None

@@ -81,17 +81,27 @@ size_t gptq_quantize_workspace_bytes(int64_t out, int64_t in) {
   return quantize_ws_bytes(out, in);
 }
 
-int gptq_quantize_layer(const void* W, int w_dtype, int64_t out, int64_t in, int64_t ld_w, const double* U,
-                        const int32_t* perm, const uint8_t* dead, int bits, int group, int8_t* codes, float* scales,
-                        int32_t* g_idx, double* row_loss, void* ws, size_t ws_bytes, void* stream) {
+int gptq_quantize_layer_ex(const void* W, int w_dtype, int64_t out, int64_t in, int64_t ld_w, const double* U,
+                           const int32_t* perm, const uint8_t* dead, int bits, int group, int grid, int8_t* codes,
+                           float* scales, int32_t* zeros, int32_t* g_idx, double* row_loss, void* ws,
+                           size_t ws_bytes, void* stream) {
   if (!W || !U || !perm || !dead || !codes || !scales) return GPTQ_ERR_INVALID_ARG;
+  if (grid != GPTQ_GRID_SYMMETRIC && grid != GPTQ_GRID_ASYMMETRIC) return GPTQ_ERR_INVALID_ARG;
+  if (grid == GPTQ_GRID_ASYMMETRIC && !zeros) return GPTQ_ERR_INVALID_ARG;
   if (out < 1 || in < 1 || in > MAX_IN || out > MAX_OUT || ld_w < in || !valid_dtype(w_dtype))
     return GPTQ_ERR_INVALID_ARG;
   if (bits < 2 || bits > 8 || group < 0) return GPTQ_ERR_INVALID_ARG;
   if (group != 0 && !(128 % group == 0 || group % 128 == 0)) return GPTQ_ERR_UNSUPPORTED;
   if (!ws || ws_bytes < quantize_ws_bytes(out, in)) return GPTQ_ERR_WORKSPACE;
-  return hip_status(quantize_launch(W, w_dtype, out, in, ld_w, U, perm, dead, bits, group, codes, scales, g_idx,
-                                    row_loss, ws, reinterpret_cast<hipStream_t>(stream)));
+  return hip_status(quantize_launch(W, w_dtype, out, in, ld_w, U, perm, dead, bits, group, grid, codes, scales,
+                                    zeros, g_idx, row_loss, ws, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int gptq_quantize_layer(const void* W, int w_dtype, int64_t out, int64_t in, int64_t ld_w, const double* U,
+                        const int32_t* perm, const uint8_t* dead, int bits, int group, int8_t* codes, float* scales,
+                        int32_t* g_idx, double* row_loss, void* ws, size_t ws_bytes, void* stream) {
+  return gptq_quantize_layer_ex(W, w_dtype, out, in, ld_w, U, perm, dead, bits, group, GPTQ_GRID_SYMMETRIC, codes,
+                                scales, nullptr, g_idx, row_loss, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -9,7 +9,7 @@
 //
 // Schedule (right-looking, 128-column panels):
 //  k_rowprep   W (bf16/fp32) -> fp64 working copy in quantization order, dead columns zeroed, per-row
-//              start scale (block max reduction).
+//              start scale (block max reduction), or start scale and zero point (min and max).
 //  k_panel     per panel: 16 lanes per row (lane c holds columns c, c+16, ..., c+112 in registers), the
 //              128 x 128 block of U in LDS. Each step j broadcasts w_j from its owner lane with DPP
 //              (row_newbcast), every lane of the row rounds it (IEEE division, round-half-even), and
@@ -22,6 +22,12 @@
 //              U[block, ob1:] (K = OB). The products are the ones of the column-by-column loop; only
 //              their grouping (and so the floating-point summation order) changes, and the fp64 W is
 //              read and written a few times instead of once per panel.
+// Grids. Symmetric ([guide] "The code, line by line"): codes -qmax..qmax, qmax = 2^(b-1) - 1, scale =
+// max(max|w|, 1e-12) / qmax, code = clip(round(w / scale)), value = code * scale. Asymmetric ([handbook]
+// quantize_weight, dequantize_weight, gptq_quantize_row; the paper's default per the guide's
+// "Simplifications"): codes 0..L, L = 2^b - 1, scale = (max - min) / L (1 when max = min), zero =
+// clip(round(-min / scale), 0, L), code = clip(round(w / scale + zero), 0, L), value = scale (code - zero).
+// Every division is correctly rounded and every rounding is to nearest even, as in the definition.
 #include <type_traits>
 #include <utility>
 
@@ -73,6 +79,14 @@ __device__ __forceinline__ double max16(double v) {
   return v;
 }
 
+__device__ __forceinline__ double min16(double v) {
+  v = fmin(v, ror16<8>(v));
+  v = fmin(v, ror16<4>(v));
+  v = fmin(v, ror16<2>(v));
+  v = fmin(v, ror16<1>(v));
+  return v;
+}
+
 __device__ __forceinline__ double sum16(double v) {
   v += ror16<8>(v);
   v += ror16<4>(v);
@@ -99,35 +113,58 @@ __device__ __forceinline__ double to_f64<uint16_t>(uint16_t v) {
   return (double)__uint_as_float(((uint32_t)v) << 16);
 }
 
-// One workgroup per row: Wq[r][j] = W[r][perm[j]] (0 for dead inputs), scale_row[r] = max(max|w|,
-// 1e-12) / qmax; per-row scales are also the output scales when group == 0.
-template <typename T>
+// One workgroup per row: Wq[r][j] = W[r][perm[j]] (0 for dead inputs). Symmetric: scale_row[r] =
+// max(max|w|, 1e-12) / qmax. Asymmetric: scale_row[r] and zero_row[r] from the row's min and max. With
+// group == 0 these are also the outputs.
+template <typename T, bool ASYM>
 __global__ __launch_bounds__(256) void k_rowprep(const T* __restrict__ W, int64_t ld_w, int in,
                                                  const int32_t* __restrict__ perm, const uint8_t* __restrict__ dead,
                                                  double qmax, int group, double* __restrict__ Wq,
-                                                 double* __restrict__ scale_row, float* __restrict__ scales,
+                                                 double* __restrict__ scale_row, double* __restrict__ zero_row,
+                                                 float* __restrict__ scales, int32_t* __restrict__ zeros,
                                                  double* __restrict__ row_loss) {
   __shared__ double red[256];
+  __shared__ double red2[256];
   const int r = blockIdx.x;
   const T* wr = W + (int64_t)r * ld_w;
   double* q = Wq + (int64_t)r * in;
-  double mx = 0.0;
+  double mx = ASYM ? -INFINITY : 0.0, mn = INFINITY;
   for (int j = threadIdx.x; j < in; j += 256) {
     const int p = min(max(perm[j], 0), in - 1);
     const double v = dead[p] ? 0.0 : to_f64<T>(wr[p]);
     q[j] = v;
-    mx = fmax(mx, fabs(v));
+    if (ASYM) {
+      mx = fmax(mx, v);
+      mn = fmin(mn, v);
+    } else {
+      mx = fmax(mx, fabs(v));
+    }
   }
   red[threadIdx.x] = mx;
+  red2[threadIdx.x] = mn;
   __syncthreads();
   for (int s = 128; s > 0; s >>= 1) {
-    if (threadIdx.x < s) red[threadIdx.x] = fmax(red[threadIdx.x], red[threadIdx.x + s]);
+    if (threadIdx.x < s) {
+      red[threadIdx.x] = fmax(red[threadIdx.x], red[threadIdx.x + s]);
+      red2[threadIdx.x] = fmin(red2[threadIdx.x], red2[threadIdx.x + s]);
+    }
     __syncthreads();
   }
   if (threadIdx.x == 0) {
-    const double s = fmax(red[0], SCALE_FLOOR) / qmax;
+    double s, z = 0.0;
+    if (ASYM) {
+      const double hi = red[0], lo = red2[0];
+      s = (hi > lo) ? (hi - lo) / qmax : 1.0;
+      z = fmin(fmax(rint(-lo / s), 0.0), qmax);
+    } else {
+      s = fmax(red[0], SCALE_FLOOR) / qmax;
+    }
     scale_row[r] = s;
-    if (group == 0) scales[r] = (float)s;
+    if (ASYM) zero_row[r] = z;
+    if (group == 0) {
+      scales[r] = (float)s;
+      if (ASYM) zeros[r] = (int32_t)z;
+    }
     if (row_loss) row_loss[r] = 0.0;
   }
 }
@@ -135,13 +172,13 @@ __global__ __launch_bounds__(256) void k_rowprep(const T* __restrict__ W, int64_
 // INPANEL = false: one scale per row, or groups that are multiples of 128 (the scale is recomputed at
 // panels where b0 % group == 0 and carried across panels in scale_row); INPANEL = true: groups dividing
 // 128 (boundaries inside the panel at j % group == 0).
-template <bool INPANEL>
+template <bool INPANEL, bool ASYM>
 __global__ __launch_bounds__(256) void k_panel(double* __restrict__ Wq, int out, int in, int b0,
                                                const double* __restrict__ U, const int32_t* __restrict__ perm,
-                                               double* __restrict__ scale_row, double qmax, int group,
-                                               int n_groups, int8_t* __restrict__ codes,
-                                               float* __restrict__ scales, double* __restrict__ Err,
-                                               int ld_err, double* __restrict__ row_loss) {
+                                               double* __restrict__ scale_row, double* __restrict__ zero_row,
+                                               double qmax, int group, int n_groups, int8_t* __restrict__ codes,
+                                               float* __restrict__ scales, int32_t* __restrict__ zeros,
+                                               double* __restrict__ Err, int ld_err, double* __restrict__ row_loss) {
   __shared__ double Us[PW][PW];
   __shared__ double rdiag[PW];
   __shared__ int pidx[PW];
@@ -182,22 +219,45 @@ __global__ __launch_bounds__(256) void k_panel(double* __restrict__ Wq, int out,
 
   double s = 1.0;
   double sy = 1.0;  // RN(1 / s)
+  double z = 0.0;   // zero point (asymmetric grid)
+  // grid parameters of a group from the current weights: lo/hi are the group's min and max (asymmetric)
+  // or 0 and max|w| (symmetric)
+  auto set_params = [&](double lo, double hi) {
+    if (ASYM) {
+      s = (hi > lo) ? (hi - lo) / qmax : 1.0;
+      sy = 1.0 / s;
+      z = fmin(fmax(rint(div_rn(-lo, s, sy)), 0.0), qmax);
+    } else {
+      s = fmax(hi, SCALE_FLOOR) / qmax;
+      sy = 1.0 / s;
+    }
+  };
   if (!INPANEL) {
     if (group != 0 && b0 % group == 0) {
       const int glen = min(group, in - b0);
-      double lm = 0.0;
+      double hi = ASYM ? -INFINITY : 0.0, lo = INFINITY;
       if (rok)
-        for (int col = c; col < glen; col += 16) lm = fmax(lm, fabs(wrow[b0 + col]));
-      lm = max16(lm);
-      s = fmax(lm, SCALE_FLOOR) / qmax;
+        for (int col = c; col < glen; col += 16) {
+          const double v = wrow[b0 + col];
+          hi = ASYM ? fmax(hi, v) : fmax(hi, fabs(v));
+          lo = fmin(lo, v);
+        }
+      hi = max16(hi);
+      if (ASYM) lo = min16(lo);
+      set_params(lo, hi);
       if (rok && c == 0) {
         scale_row[r] = s;
         scales[(int64_t)r * n_groups + b0 / group] = (float)s;
+        if (ASYM) {
+          zero_row[r] = z;
+          zeros[(int64_t)r * n_groups + b0 / group] = (int32_t)z;
+        }
       }
     } else {
       s = rok ? scale_row[r] : 1.0;
+      sy = 1.0 / s;
+      if (ASYM) z = rok ? zero_row[r] : 0.0;
     }
-    sy = 1.0 / s;
   }
 
   int code_m[8];
@@ -217,22 +277,34 @@ __global__ __launch_bounds__(256) void k_panel(double* __restrict__ Wq, int out,
       const int j = jm * 16 + jl;
       {
         if (INPANEL && (j % group) == 0) {
-          double lm = 0.0;
+          double hi = ASYM ? -INFINITY : 0.0, lo = INFINITY;
 #pragma unroll
           for (int m = 0; m < 8; ++m) {
             const int col = c + 16 * m;
-            lm = (col >= j && col < j + group) ? fmax(lm, fabs(w[m])) : lm;
+            const bool in_g = col >= j && col < j + group && col < pw;
+            hi = in_g ? (ASYM ? fmax(hi, w[m]) : fmax(hi, fabs(w[m]))) : hi;
+            lo = in_g ? fmin(lo, w[m]) : lo;
           }
-          lm = max16(lm);
-          s = fmax(lm, SCALE_FLOOR) / qmax;
-          sy = 1.0 / s;
-          if (rok && c == 0 && j < pw) scales[(int64_t)r * n_groups + (b0 + j) / group] = (float)s;
+          hi = max16(hi);
+          if (ASYM) lo = min16(lo);
+          set_params(lo, hi);
+          if (rok && c == 0 && j < pw) {
+            scales[(int64_t)r * n_groups + (b0 + j) / group] = (float)s;
+            if (ASYM) zeros[(int64_t)r * n_groups + (b0 + j) / group] = (int32_t)z;
+          }
         }
         const double wj = bcast16<jl>(w[jm]);
-        // q = c * scale and err = (w - q) / U[j][j] with the rounding steps of the definition (no fused
+        // the code and err = (w - q) / U[j][j] with the rounding steps of the definition (no fused
         // multiply-add): a weight that sits exactly on the grid leaves err = 0
-        const double cq = fmin(fmax(rint(div_rn(wj, s, sy)), -qmax), qmax);
-        const double e = __dmul_rn(__dsub_rn(wj, __dmul_rn(cq, s)), rdiag[j]);
+        double cq, qv;
+        if (ASYM) {
+          cq = fmin(fmax(rint(__dadd_rn(div_rn(wj, s, sy), z)), 0.0), qmax);
+          qv = __dmul_rn(s, __dsub_rn(cq, z));
+        } else {
+          cq = fmin(fmax(rint(div_rn(wj, s, sy)), -qmax), qmax);
+          qv = __dmul_rn(cq, s);
+        }
+        const double e = __dmul_rn(__dsub_rn(wj, qv), rdiag[j]);
         if (c == jl) {
           code_m[jm] = (int)cq;
           err_m[jm] = e;
@@ -279,43 +351,76 @@ size_t quantize_ws_bytes(int64_t out, int64_t in) {
   b += align_up((size_t)out * in * sizeof(double), 256);  // working copy
   b += align_up((size_t)out * OB * sizeof(double), 256);  // errors of one outer block
   b += align_up((size_t)out * sizeof(double), 256);       // current fp64 scale per row
+  b += align_up((size_t)out * sizeof(double), 256);       // current zero point per row (asymmetric grid)
   return b;
 }
 
+template <bool ASYM>
+static hipError_t launch_rowprep(const void* W, int w_dtype, int out, int in, int64_t ld_w, const int32_t* perm,
+                                 const uint8_t* dead, double qmax, int group, double* Wq, double* scale_row,
+                                 double* zero_row, float* scales, int32_t* zeros, double* row_loss,
+                                 hipStream_t stream) {
+  if (w_dtype == GPTQ_BF16)
+    hipLaunchKernelGGL((k_rowprep<uint16_t, ASYM>), dim3(out), dim3(256), 0, stream, (const uint16_t*)W, ld_w, in,
+                       perm, dead, qmax, group, Wq, scale_row, zero_row, scales, zeros, row_loss);
+  else
+    hipLaunchKernelGGL((k_rowprep<float, ASYM>), dim3(out), dim3(256), 0, stream, (const float*)W, ld_w, in, perm,
+                       dead, qmax, group, Wq, scale_row, zero_row, scales, zeros, row_loss);
+  return hipGetLastError();
+}
+
+template <bool ASYM>
+static hipError_t launch_panel(bool inpanel, dim3 grid, double* Wq, int out, int in, int b0, const double* U,
+                               const int32_t* perm, double* scale_row, double* zero_row, double qmax, int group,
+                               int n_groups, int8_t* codes, float* scales, int32_t* zeros, double* errp,
+                               int ld_err, double* row_loss, hipStream_t stream) {
+  if (inpanel)
+    k_panel<true, ASYM><<<grid, dim3(256), 0, stream>>>(Wq, out, in, b0, U, perm, scale_row, zero_row, qmax, group,
+                                                        n_groups, codes, scales, zeros, errp, ld_err, row_loss);
+  else
+    k_panel<false, ASYM><<<grid, dim3(256), 0, stream>>>(Wq, out, in, b0, U, perm, scale_row, zero_row, qmax, group,
+                                                         n_groups, codes, scales, zeros, errp, ld_err, row_loss);
+  return hipGetLastError();
+}
+
 hipError_t quantize_launch(const void* W, int w_dtype, int64_t out64, int64_t in64, int64_t ld_w, const double* U,
-                           const int32_t* perm, const uint8_t* dead, int bits, int group, int8_t* codes,
-                           float* scales, int32_t* g_idx, double* row_loss, void* ws, hipStream_t stream) {
+                           const int32_t* perm, const uint8_t* dead, int bits, int group, int grid, int8_t* codes,
+                           float* scales, int32_t* zeros, int32_t* g_idx, double* row_loss, void* ws,
+                           hipStream_t stream) {
   const int out = (int)out64, in = (int)in64;
+  const bool asym = (grid == GPTQ_GRID_ASYMMETRIC);
   char* w = reinterpret_cast<char*>(ws);
   double* Wq = reinterpret_cast<double*>(w);
   w += align_up((size_t)out * in * sizeof(double), 256);
   double* Err = reinterpret_cast<double*>(w);
   w += align_up((size_t)out * OB * sizeof(double), 256);
   double* scale_row = reinterpret_cast<double*>(w);
-  const double qmax = (double)((1 << (bits - 1)) - 1);
+  w += align_up((size_t)out * sizeof(double), 256);
+  double* zero_row = reinterpret_cast<double*>(w);
+  // largest code: qmax of the symmetric grid, or the top level 2^b - 1 of the asymmetric one
+  const double qmax = asym ? (double)((1 << bits) - 1) : (double)((1 << (bits - 1)) - 1);
   const int n_groups = group ? (int)ceil_div(in, group) : 1;
+  // outer blocks must not split a group whose parameters come from columns beyond the current panel:
+  // groups that are multiples of the panel width but neither divide nor are multiples of OB fall back
+  // to one panel per outer block (every later column updated after every panel)
+  const int ob = (group > PW && OB % group != 0 && group % OB != 0) ? PW : OB;
 
-  if (w_dtype == GPTQ_BF16)
-    hipLaunchKernelGGL(k_rowprep<uint16_t>, dim3(out), dim3(256), 0, stream, (const uint16_t*)W, ld_w, in, perm, dead,
-                       qmax, group, Wq, scale_row, scales, row_loss);
-  else
-    hipLaunchKernelGGL(k_rowprep<float>, dim3(out), dim3(256), 0, stream, (const float*)W, ld_w, in, perm, dead, qmax,
-                       group, Wq, scale_row, scales, row_loss);
-  hipError_t e = hipGetLastError();
+  hipError_t e = asym ? launch_rowprep<true>(W, w_dtype, out, in, ld_w, perm, dead, qmax, group, Wq, scale_row,
+                                             zero_row, scales, zeros, row_loss, stream)
+                      : launch_rowprep<false>(W, w_dtype, out, in, ld_w, perm, dead, qmax, group, Wq, scale_row,
+                                              zero_row, scales, zeros, row_loss, stream);
   if (e != hipSuccess) return e;
 
   const dim3 pgrid((unsigned)ceil_div(out, 16));
-  for (int ob0 = 0; ob0 < in; ob0 += OB) {
-    const int ob1 = min(in, ob0 + OB);
+  for (int ob0 = 0; ob0 < in; ob0 += ob) {
+    const int ob1 = min(in, ob0 + ob);
     for (int b0 = ob0; b0 < ob1; b0 += PW) {
       double* errp = Err + (b0 - ob0);  // this panel's columns of the outer block's error matrix
-      if (group != 0 && PW % group == 0)
-        k_panel<true><<<pgrid, dim3(256), 0, stream>>>(Wq, out, in, b0, U, perm, scale_row, qmax, group, n_groups,
-                                                       codes, scales, errp, OB, row_loss);
-      else
-        k_panel<false><<<pgrid, dim3(256), 0, stream>>>(Wq, out, in, b0, U, perm, scale_row, qmax, group, n_groups,
-                                                        codes, scales, errp, OB, row_loss);
-      e = hipGetLastError();
+      const bool inpanel = group != 0 && PW % group == 0;
+      e = asym ? launch_panel<true>(inpanel, pgrid, Wq, out, in, b0, U, perm, scale_row, zero_row, qmax, group,
+                                    n_groups, codes, scales, zeros, errp, OB, row_loss, stream)
+               : launch_panel<false>(inpanel, pgrid, Wq, out, in, b0, U, perm, scale_row, zero_row, qmax, group,
+                                     n_groups, codes, scales, zeros, errp, OB, row_loss, stream);
       if (e != hipSuccess) return e;
       const int b1 = b0 + PW;
       if (b1 < ob1) {  // the rest of the outer block: W[:, b1:ob1] -= Err[:, panel] U[b0:b1, b1:ob1]

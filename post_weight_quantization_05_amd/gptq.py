@@ -115,21 +115,28 @@ def prepare_chol(S: torch.Tensor, colsq: torch.Tensor, n_total: int, damp: float
 
 @dataclass
 class QuantResult:
-    codes: torch.Tensor      # int8, out x in, original column order
+    codes: torch.Tensor      # out x in, original column order: int8 (symmetric) or uint8 0..2^b-1 (asymmetric)
     scales: torch.Tensor     # fp32, out x G
     g_idx: torch.Tensor      # int32[in]
     row_loss: torch.Tensor   # fp64[out]
     perm: torch.Tensor | None = None
     dead: torch.Tensor | None = None
     U: torch.Tensor | None = None
+    zeros: torch.Tensor | None = None  # int32, out x G (asymmetric grid only)
 
     def dequantize(self) -> torch.Tensor:
-        return self.codes.to(torch.float64) * self.scales.to(torch.float64)[:, self.g_idx.long()]
+        g = self.g_idx.long()
+        c = self.codes.to(torch.float64)
+        if self.zeros is not None:
+            c = c - self.zeros.to(torch.float64)[:, g]
+        return c * self.scales.to(torch.float64)[:, g]
 
 
 def quantize_layer(W: torch.Tensor, U: torch.Tensor, perm: torch.Tensor, dead: torch.Tensor, bits: int = 4,
-                   group: int | None = None, stream=None, ws: torch.Tensor | None = None) -> QuantResult:
-    """The column-by-column error-compensation loop; W (out x in) bf16 or fp32 is only read."""
+                   group: int | None = None, stream=None, ws: torch.Tensor | None = None,
+                   asymmetric: bool = False) -> QuantResult:
+    """The column-by-column error-compensation loop; W (out x in) bf16 or fp32 is only read.
+    asymmetric=True uses the min/max grid with a zero point (gptq_quantize_layer_ex)."""
     _req_cuda(W, "W")
     ld = _ld(W, "W")
     out, d = W.shape
@@ -147,17 +154,23 @@ def quantize_layer(W: torch.Tensor, U: torch.Tensor, perm: torch.Tensor, dead: t
     need = lib.gptq_quantize_workspace_bytes(out, d)
     if ws is None or ws.numel() < need:
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    st = lib.gptq_quantize_layer(W.data_ptr(), _dtype_code(W), out, d, ld, U.data_ptr(), perm.data_ptr(),
-                                 dead.data_ptr(), int(bits), group, codes.data_ptr(), scales.data_ptr(),
-                                 g_idx.data_ptr(), row_loss.data_ptr(), ws.data_ptr(), ws.numel(), _stream(stream))
-    check(st, "gptq_quantize_layer")
-    return QuantResult(codes, scales, g_idx, row_loss, perm, dead, U)
+    zeros = torch.empty((out, n_groups), dtype=torch.int32, device=dev) if asymmetric else None
+    grid = _lib.GPTQ_GRID_ASYMMETRIC if asymmetric else _lib.GPTQ_GRID_SYMMETRIC
+    st = lib.gptq_quantize_layer_ex(W.data_ptr(), _dtype_code(W), out, d, ld, U.data_ptr(), perm.data_ptr(),
+                                    dead.data_ptr(), int(bits), group, grid, codes.data_ptr(), scales.data_ptr(),
+                                    zeros.data_ptr() if zeros is not None else None, g_idx.data_ptr(),
+                                    row_loss.data_ptr(), ws.data_ptr(), ws.numel(), _stream(stream))
+    check(st, "gptq_quantize_layer_ex")
+    if asymmetric:
+        codes = codes.view(torch.uint8)
+    return QuantResult(codes, scales, g_idx, row_loss, perm, dead, U, zeros)
 
 
 def gptq_quantize(W: torch.Tensor, X: torch.Tensor, bits: int = 4, group: int | None = None, damp: float = 0.01,
-                  act_order: bool = False, flags: int = GPTQ_FACTOR_INVERSE_RECHOL, stream=None) -> QuantResult:
+                  act_order: bool = False, flags: int = GPTQ_FACTOR_INVERSE_RECHOL, stream=None,
+                  asymmetric: bool = False) -> QuantResult:
     """The whole per-layer path: accumulate the Hessian over X, prepare U, quantize W."""
     state = HessianState(W.shape[1], device=W.device)
     hessian_accumulate(X, state, stream)
     U, perm, dead = prepare_chol(state.S, state.colsq, state.n_total, damp, act_order, flags, stream)
-    return quantize_layer(W, U, perm, dead, bits, group, stream)
+    return quantize_layer(W, U, perm, dead, bits, group, stream, asymmetric=asymmetric)

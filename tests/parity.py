@@ -56,6 +56,26 @@ def compare(res_gpu, ref: dict, W64: np.ndarray, bits: int, group: int, tau: flo
                 gidx_ok=bool(np.array_equal(g_idx, ref["g_idx"])))
 
 
+def compare_asym(res_gpu, ref: dict, W64: np.ndarray, bits: int, group: int, tau: float = TAU) -> dict:
+    """The same gates on the asymmetric grid: Q = scale (code - zero), replay distance on that grid."""
+    codes = res_gpu.codes.cpu().numpy().astype(np.int64)
+    scales = res_gpu.scales.cpu().numpy().astype(np.float64)
+    zeros = res_gpu.zeros.cpu().numpy().astype(np.float64)
+    g_idx = res_gpu.g_idx.cpu().numpy().astype(np.int64)
+    perm = ref["perm"]
+    agree = float(np.mean(codes == ref["codes"]))
+    Q_gpu = scales[:, g_idx] * (codes - zeros[:, g_idx])
+    Q_ref = ref["Q"]
+    q_rel = float(np.linalg.norm(Q_gpu - Q_ref) / max(np.linalg.norm(Q_ref), 1e-300))
+    e_gpu = O.output_error(W64, Q_gpu, ref["S"])
+    e_ref = O.output_error(W64, Q_ref, ref["S"])
+    out_rel = abs(e_gpu - e_ref) / max(e_ref, 1e-300)
+    dist = O.forced_replay_asym(ref["W0"], ref["U"], bits, group, codes[:, perm])
+    return dict(agree=agree, mismatches=int(np.sum(codes != ref["codes"])), q_rel=q_rel, out_rel=out_rel,
+                replay_excess=float(dist.max() - 0.5), e_gpu=e_gpu, e_ref=e_ref,
+                gidx_ok=bool(np.array_equal(g_idx, ref["g_idx"])))
+
+
 def assert_gates(m: dict, tau: float = TAU, q_gate: float = 1e-3):
     assert m["gidx_ok"], m
     assert m["agree"] >= 0.999, m

@@ -23,7 +23,7 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     lib = _lib.load()
     names = declared_functions()
-    assert len(names) == 8, names
+    assert len(names) == 9, names
     for n in names:
         assert hasattr(lib, n), n
         assert n in _lib.SIGNATURES, n
@@ -122,6 +122,26 @@ def test_quantize_argument_errors():
         assert call(group=g) == _lib.GPTQ_ERR_UNSUPPORTED
     assert call(ws=None) == _lib.GPTQ_ERR_WORKSPACE
     assert call(group=256, wsb=4) == _lib.GPTQ_ERR_WORKSPACE
+
+
+def test_quantize_ex_argument_errors():
+    """The grid-selecting entry point: unknown grid, or the asymmetric grid without a zeros buffer, are
+    argument errors; the other checks are those of gptq_quantize_layer."""
+    lib = _lib.load()
+    bad = _lib.GPTQ_ERR_INVALID_ARG
+
+    def call(grid=_lib.GPTQ_GRID_ASYMMETRIC, zeros=FAKE, W=FAKE, bits=4, group=0, ws=FAKE, wsb=1 << 30):
+        return lib.gptq_quantize_layer_ex(W, 1, 8, 256, 256, FAKE, FAKE, FAKE, bits, group, grid, FAKE, FAKE, zeros,
+                                          None, None, ws, wsb, None)
+
+    assert call(grid=2) == bad
+    assert call(grid=-1) == bad
+    assert call(zeros=None) == bad
+    assert call(W=None) == bad
+    assert call(bits=9) == bad
+    assert call(group=48) == _lib.GPTQ_ERR_UNSUPPORTED
+    assert call(ws=None) == _lib.GPTQ_ERR_WORKSPACE
+    assert call(grid=_lib.GPTQ_GRID_SYMMETRIC, zeros=None, ws=None) == _lib.GPTQ_ERR_WORKSPACE
 
 
 def test_missing_library_fails_loudly(tmp_path):
