@@ -21,6 +21,9 @@ What is computed (the method is a greedy sequential rounding heuristic, so the o
   7. codes back to the original column order, g_idx for act_order+groups ([guide] "When it breaks")
   8. the same loop on the asymmetric grid: levels 0..2^b-1, (scale, zero) from min/max of the row or group
      ([guide] "Simplifications": the paper's default; [handbook] quantize_weight, gptq_quantize_row)
+  9. storage and use: codes packed into 32-bit words, Q from codes, scales (zeros) and g_idx, and the
+     layer-wise driver that calibrates each layer on the already-quantized layers' outputs
+     ([guide] "When it breaks", "How it works" apply_layerwise; [handbook] int4 storage)
 
 Readings where the pages leave a detail open (each is also listed with the build's design notes):
   * qmax for b bits is 2^(b-1) - 1 (the lesson's starter code; "2-bit" = ternary {-s, 0, s} in the guide).
@@ -35,6 +38,9 @@ Readings where the pages leave a detail open (each is also listed with the build
     is clipped to the levels, so a group of all-positive (or all-negative) weights saturates at one end,
     as the handbook's formulas do. Per-row mode takes (scale, zero) from the starting weights, groups
     from the current weights at the group start (the handbook's per-column loop does the latter).
+  * Packed layout (the pages fix none): per row a little-endian bit stream of b-bit codes in 32-bit
+    words, symmetric codes offset by 2^(b-1). The driver's F is float32; an MLP layer is affine + ReLU
+    (no ReLU on the output layer); layer outputs are the exact values rounded once to fp32.
 """
 from __future__ import annotations
 
@@ -393,6 +399,100 @@ def forced_replay_asym(W0: np.ndarray, U: np.ndarray, bits: int, group: int, for
         if j + 1 < d:
             W[:, j + 1:] -= np.outer(e, U[j, j + 1:])
     return dist
+
+
+# ---------------------------------------------------------------------------------------------
+# Step 9: storage of the codes and their consumer ([guide] "When it breaks": integer codes with
+# per-group scales, g_idx for act_order groups; [handbook] "int4" storage of 4-bit codes)
+# ---------------------------------------------------------------------------------------------
+def stored_code_offset(bits: int, asymmetric: bool) -> int:
+    """Symmetric codes -qmax..qmax are stored as code + 2^(bits-1) (non-negative, below 2^bits); asymmetric
+    codes 0..2^bits-1 are stored as they are. (The pages do not fix a packed layout; this is the reading.)"""
+    return 0 if asymmetric else 2 ** (bits - 1)
+
+
+def pack_rows(codes: np.ndarray, bits: int, asymmetric: bool = False) -> np.ndarray:
+    """One little-endian bit stream per row: stored code j occupies stream bits [bits*j, bits*(j+1)), and
+    stream bit k is bit k % 32 of 32-bit word k // 32. Unused high bits of the last word are 0."""
+    if not 2 <= bits <= 8:
+        raise ValueError("bits must be in 2..8")
+    v = np.asarray(codes, dtype=np.int64) + stored_code_offset(bits, asymmetric)
+    if v.size and (v.min() < 0 or v.max() >= 2 ** bits):
+        raise ValueError("code outside the stored range")
+    out, d = v.shape
+    words = np.zeros((out, (d * bits + 31) // 32), dtype=np.int64)
+    for j in range(d):
+        bit = j * bits
+        w, sh = bit // 32, bit % 32
+        words[:, w] |= (v[:, j] << sh) & 0xFFFFFFFF
+        if sh + bits > 32:  # the code straddles into the next word
+            words[:, w + 1] |= v[:, j] >> (32 - sh)
+    return words.astype(np.uint32)
+
+
+def unpack_rows(words: np.ndarray, d: int, bits: int, asymmetric: bool = False) -> np.ndarray:
+    """Inverse of pack_rows: (out x words) uint32 -> codes (out x d, int64)."""
+    w64 = np.asarray(words, dtype=np.uint32).astype(np.int64)
+    codes = np.zeros((w64.shape[0], d), dtype=np.int64)
+    for j in range(d):
+        bit = j * bits
+        w, sh = bit // 32, bit % 32
+        v = w64[:, w] >> sh
+        if sh + bits > 32:
+            v = v | (w64[:, w + 1] << (32 - sh))
+        codes[:, j] = v & (2 ** bits - 1)
+    return codes - stored_code_offset(bits, asymmetric)
+
+
+def dequantize(codes: np.ndarray, scales: np.ndarray, g_idx: np.ndarray, zeros: np.ndarray | None = None):
+    """Q[r, c] = scales[r, g] * (codes[r, c] - zeros[r, g]) with g = g_idx[c] (zero 0 on the symmetric
+    grid), in fp64."""
+    g = np.asarray(g_idx, dtype=np.int64)
+    c = np.asarray(codes, dtype=np.float64)
+    if zeros is not None:
+        c = c - np.asarray(zeros, dtype=np.float64)[:, g]
+    return np.asarray(scales, dtype=np.float64)[:, g] * c
+
+
+def linear_forward(h: np.ndarray, Wl: np.ndarray, b: np.ndarray | None, relu: bool) -> np.ndarray:
+    """One MLP layer, h W^T + b, then ReLU on hidden layers, exact in fp64 and rounded once to fp32.
+
+    [guide] apply_layerwise (its source, in "Source code") stores layer weights and outputs in a float
+    type it calls F and never defines, with a layer_forward it does not define either. Readings: F is
+    float32; a layer is affine (weights and a bias) followed by ReLU, except the output layer, which has
+    no activation; the fp32 result is the exact value rounded to nearest."""
+    y = np.asarray(h, dtype=np.float64) @ np.asarray(Wl, dtype=np.float64).T
+    if b is not None:
+        y = y + np.asarray(b, dtype=np.float64)[None, :]
+    if relu:
+        y = np.maximum(y, 0.0)
+    return y.astype(np.float32).astype(np.float64)
+
+
+def apply_layerwise(weights, biases, X64: np.ndarray, quantize, skip_last: bool = False):
+    """[guide] "How it works", apply_layerwise: quantize the layers in order, each one calibrated on the
+    outputs of the layers before it AFTER those were quantized (the inputs it will see in use).
+
+    weights[i]: out_i x in_i (in_0 = X's width); biases[i]: out_i or None; quantize(W64, h64) -> dict
+    with "Q" (e.g. a partial of gptq_oracle). The quantized weights are kept in float32, as the driver
+    stores them. Returns (results, inputs, h): results[i] is quantize's dict (None for a skipped last
+    layer), inputs[i] the fp64 array layer i was calibrated on, h the network's output."""
+    h = np.asarray(X64, dtype=np.float64)
+    results, inputs = [], []
+    L = len(weights)
+    for i in range(L):
+        last = i == L - 1
+        W64 = np.asarray(weights[i], dtype=np.float64)
+        inputs.append(h)
+        if skip_last and last:
+            results.append(None)
+            Wl = W64
+        else:
+            r = quantize(W64, h)
+            results.append(r)
+            Wl = r["Q"].astype(np.float32)
+        h = linear_forward(h.astype(np.float32), Wl, biases[i], relu=not last)
+    return results, inputs, h
 
 
 # ---------------------------------------------------------------------------------------------

@@ -14,4 +14,8 @@ from .workloads import (  # noqa: F401
     gen_x,
     gen_layer,
     custom_config,
+    MLPConfig,
+    MLP_CONFIGS,
+    mlp_config_by_name,
+    gen_mlp,
 )

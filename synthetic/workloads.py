@@ -178,3 +178,51 @@ def gen_x(cfg: LayerConfig, row_start: int = 0, row_stop: int | None = None,
 def gen_layer(cfg: LayerConfig):
     """(W, X) for a config, both encoded per cfg.dtype."""
     return gen_w(cfg), gen_x(cfg)
+
+
+# ------------------------------------------------------------------------------------------------
+# A small MLP for the layer-wise driver (the guide's "3x256 teacher": 12 raw inputs, three hidden
+# layers of 256 with ReLU, an output layer; 512 calibration inputs). The trained teacher is not
+# available, so its weights are drawn:
+#   * layer i (out_i x in_i): default_rng([seed, 1 + i]) draws W ~ N(0, 2 / in_i) (fp32), then the
+#     bias ~ N(0, 0.1^2) (fp32); in hidden layers the first `dead` entries of permutation(out_i) get
+#     bias -50, so those ReLU units never fire (the guide's dead inputs of the next layer).
+#   * X: default_rng([seed, 0]).standard_normal((n, sizes[0]), float32).
+# ------------------------------------------------------------------------------------------------
+@dataclass(frozen=True)
+class MLPConfig:
+    name: str
+    sizes: tuple
+    n: int
+    dead: int = 0
+    seed: int = 0
+
+
+MLP_CONFIGS = (
+    MLPConfig("teacher_mlp", (12, 256, 256, 256, 2), 512, dead=6, seed=6006),
+    MLPConfig("wide_mlp", (200, 640, 640, 10), 2048, dead=16, seed=7007),
+)
+
+
+def mlp_config_by_name(name: str) -> MLPConfig:
+    for c in MLP_CONFIGS:
+        if c.name == name:
+            return c
+    raise KeyError(name)
+
+
+def gen_mlp(cfg: MLPConfig):
+    """(weights, biases, X): fp32 arrays, weights[i] out_i x in_i, biases[i] out_i, X n x sizes[0]."""
+    weights, biases = [], []
+    L = len(cfg.sizes) - 1
+    for i in range(L):
+        d_in, d_out = cfg.sizes[i], cfg.sizes[i + 1]
+        rng = np.random.default_rng([cfg.seed, 1 + i])
+        w = rng.standard_normal((d_out, d_in), dtype=np.float32) * np.float32(np.sqrt(2.0 / d_in))
+        b = rng.standard_normal(d_out, dtype=np.float32) * np.float32(0.1)
+        if cfg.dead and i < L - 1:
+            b[rng.permutation(d_out)[: cfg.dead]] = np.float32(-50.0)
+        weights.append(w)
+        biases.append(b)
+    X = np.random.default_rng([cfg.seed, 0]).standard_normal((cfg.n, cfg.sizes[0]), dtype=np.float32)
+    return weights, biases, X

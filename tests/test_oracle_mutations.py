@@ -236,3 +236,109 @@ def test_asym_pins_catch_planted_mistake(monkeypatch, name, factory, kind):
         except (AssertionError, np.linalg.LinAlgError, FloatingPointError, ValueError, IndexError):
             caught.append(fn.__name__)
     assert caught, f"no pin caught mutation {name}:{kind}"
+
+
+# ------------------------------------------------------------------------------------------------
+# Storage and the layer-wise driver: a wrong bit order, a lost straddle, g_idx ignored, a missing
+# bias, the classic mistake of calibrating on full-precision outputs
+# ------------------------------------------------------------------------------------------------
+import tests.test_oracle_pins_storage as PS  # noqa: E402
+
+
+def _pack_factory(kind):
+    def pack(codes, bits, asymmetric=False):
+        v = np.asarray(codes, dtype=np.int64) + O.stored_code_offset(bits, asymmetric)
+        if v.size and (v.min() < 0 or v.max() >= 2 ** bits):
+            raise ValueError("range")
+        out, d = v.shape
+        words = np.zeros((out, (d * bits + 31) // 32), dtype=np.int64)
+        for j in range(d):
+            bit = j * bits
+            w, sh = bit // 32, bit % 32
+            if kind == "msb_first":
+                sh = 32 - bits - sh if sh + bits <= 32 else sh
+            words[:, w] |= (v[:, j] << sh) & 0xFFFFFFFF
+            if sh + bits > 32 and kind != "no_straddle":
+                words[:, w + 1] |= v[:, j] >> (32 - sh)
+        return words.astype(np.uint32)
+    return pack
+
+
+def _dequant_factory(kind):
+    def deq(codes, scales, g_idx, zeros=None):
+        d = np.asarray(codes).shape[1]
+        G = np.asarray(scales).shape[1]
+        g = np.minimum(np.arange(d) * G // d, G - 1) if kind == "positional_groups" else np.asarray(g_idx)
+        c = np.asarray(codes, dtype=np.float64)
+        if zeros is not None and kind != "drop_zero":
+            c = c - np.asarray(zeros, dtype=np.float64)[:, g]
+        return np.asarray(scales, dtype=np.float64)[:, g] * c
+    return deq
+
+
+def _forward_factory(kind):
+    def fwd(h, Wl, b, relu):
+        y = np.asarray(h, dtype=np.float64) @ np.asarray(Wl, dtype=np.float64).T
+        if b is not None and kind != "no_bias":
+            y = y + np.asarray(b, dtype=np.float64)[None, :]
+        if relu or kind == "relu_on_last":
+            y = np.maximum(y, 0.0)
+        return y.astype(np.float32).astype(np.float64)
+    return fwd
+
+
+def _layerwise_factory(kind):
+    def drive(weights, biases, X64, quantize, skip_last=False):
+        h = np.asarray(X64, dtype=np.float64)
+        results, inputs = [], []
+        L = len(weights)
+        for i in range(L):
+            last = i == L - 1
+            W64 = np.asarray(weights[i], dtype=np.float64)
+            inputs.append(h)
+            if skip_last and last:
+                results.append(None)
+                Wl = W64
+            else:
+                r = quantize(W64, h)
+                results.append(r)
+                Wl = W64 if kind == "full_precision_inputs" else r["Q"].astype(np.float32)
+            h = O.linear_forward(h.astype(np.float32), Wl, biases[i], relu=not last)
+        return results, inputs, h
+    return drive
+
+
+PINS_STORAGE = [
+    (PS.test_pack_hand_word_4bit, ()),
+    (PS.test_pack_hand_words_3bit_straddle, ()),
+    (PS.test_pack_equals_bigint_stream_and_round_trips, (3, False)),
+    (PS.test_dequantize_hand_values, ()),
+    (PS.test_dequantize_reproduces_quantizer_q, (True,)),
+    (PS.test_linear_forward_hand_values, ()),
+    (PS.test_layerwise_identity_quantizer_is_the_plain_forward, ()),
+    (PS.test_layerwise_calibrates_on_quantized_outputs, ()),
+    (PS.test_layerwise_skip_last_keeps_output_layer, ()),
+]
+
+MUTATIONS_STORAGE = [
+    ("pack_rows", _pack_factory, k) for k in ["msb_first", "no_straddle"]
+] + [
+    ("dequantize", _dequant_factory, k) for k in ["positional_groups", "drop_zero"]
+] + [
+    ("linear_forward", _forward_factory, k) for k in ["no_bias", "relu_on_last"]
+] + [
+    ("apply_layerwise", _layerwise_factory, "full_precision_inputs"),
+]
+
+
+@pytest.mark.parametrize("name,factory,kind", MUTATIONS_STORAGE,
+                         ids=[f"{m[0]}-{m[2]}" for m in MUTATIONS_STORAGE])
+def test_storage_pins_catch_planted_mistake(monkeypatch, name, factory, kind):
+    monkeypatch.setattr(O, name, factory(kind))
+    caught = []
+    for fn, args in PINS_STORAGE:
+        try:
+            fn(*args)
+        except (AssertionError, ValueError, IndexError):
+            caught.append(fn.__name__)
+    assert caught, f"no pin caught mutation {name}:{kind}"
