@@ -169,6 +169,37 @@ int gptq_quantize_layer_ex(const void* W, int w_dtype, int64_t out, int64_t in, 
                            int8_t* codes, float* scales, int32_t* zeros, int32_t* g_idx, double* row_loss,
                            void* ws, size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------------------------------
+ * 4. Packed codes and a consumer of the outputs. GPTQ guide, "When it breaks": the layer is stored as
+ *    integer codes with per-group scales, and with act_order a consumer finds a column's group through
+ *    g_idx. Handbook page "GPTQ > Implementation with AutoGPTQ": codes are stored packed at 4 bits each.
+ *
+ *  gptq_packed_words_per_row  ceil(in * bits / 32), the uint32 words of one packed row (0 for bad sizes).
+ *  gptq_pack_codes   codes (int8, out x in, as gptq_quantize_layer[_ex] writes them) -> packed (uint32,
+ *                    out x words_per_row, caller-allocated). Row r is a little-endian bit stream: code j
+ *                    occupies bits [bits*j, bits*(j+1)), bit k of the stream being bit k % 32 of word
+ *                    k / 32. Symmetric codes are stored as code + 2^(bits-1); asymmetric codes (0..2^b-1)
+ *                    as they are. Unused high bits of a row's last word are 0.
+ *  gptq_dequant_matmul  Y = X Q^T, Y n x out fp32 (leading dimension ld_y >= out), X n x in (GPTQ_BF16 or
+ *                    GPTQ_F32, ld_x >= in). Q[r][c] = scales[r][g] * (code(r, c) - zero(r, g)) with
+ *                    g = g_idx[c]; zero = zeros[r][g] on the asymmetric grid, 0 on the symmetric one.
+ *                    scales / zeros are out x G as the quantize call writes them, G = group ?
+ *                    ceil(in/group) : 1; g_idx is required (all zeros when group == 0). Q is formed in
+ *                    fp32 (one rounding per element) and the products accumulate in fp32. Then, in the
+ *                    same pass, Y += bias (fp32[out], nullable) and, when relu == 1, Y = max(Y, 0): the
+ *                    forward of a quantized MLP layer, as the guide's layer-wise driver needs it to feed
+ *                    the next layer ("How it works", apply_layerwise). relu must be 0 or 1.
+ *  Errors: INVALID_ARG (NULL pointer, sizes, ld, dtype, bits outside 2..8, unknown grid, asymmetric grid
+ *  without zeros), HIP. Both calls are asynchronous on `stream`.
+ * ------------------------------------------------------------------------------------------------- */
+int64_t gptq_packed_words_per_row(int64_t in, int bits);
+int gptq_pack_codes(const int8_t* codes, int64_t out, int64_t in, int bits, int grid, uint32_t* packed,
+                    void* stream);
+int gptq_dequant_matmul(const void* X, int x_dtype, int64_t n, int64_t in, int64_t ld_x,
+                        const uint32_t* packed, const float* scales, const int32_t* zeros,
+                        const int32_t* g_idx, int64_t out, int bits, int grid, int group,
+                        const float* bias, int relu, float* Y, int64_t ld_y, void* stream);
+
 /* Human-readable name of a gptq_status value (static storage). */
 const char* gptq_status_string(int status);
 

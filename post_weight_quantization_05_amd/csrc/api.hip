@@ -104,4 +104,33 @@ int gptq_quantize_layer(const void* W, int w_dtype, int64_t out, int64_t in, int
                                 scales, nullptr, g_idx, row_loss, ws, ws_bytes, stream);
 }
 
+int64_t gptq_packed_words_per_row(int64_t in, int bits) {
+  if (in < 1 || bits < 2 || bits > 8) return 0;
+  return packed_words_per_row(in, bits);
+}
+
+int gptq_pack_codes(const int8_t* codes, int64_t out, int64_t in, int bits, int grid, uint32_t* packed,
+                    void* stream) {
+  if (!codes || !packed) return GPTQ_ERR_INVALID_ARG;
+  if (out < 1 || in < 1 || in > MAX_IN || out > MAX_OUT || bits < 2 || bits > 8) return GPTQ_ERR_INVALID_ARG;
+  if (grid != GPTQ_GRID_SYMMETRIC && grid != GPTQ_GRID_ASYMMETRIC) return GPTQ_ERR_INVALID_ARG;
+  return hip_status(pack_launch(codes, out, in, bits, grid, packed, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int gptq_dequant_matmul(const void* X, int x_dtype, int64_t n, int64_t in, int64_t ld_x, const uint32_t* packed,
+                        const float* scales, const int32_t* zeros, const int32_t* g_idx, int64_t out, int bits,
+                        int grid, int group, const float* bias, int relu, float* Y, int64_t ld_y, void* stream) {
+  if (!X || !packed || !scales || !g_idx || !Y) return GPTQ_ERR_INVALID_ARG;
+  if (grid != GPTQ_GRID_SYMMETRIC && grid != GPTQ_GRID_ASYMMETRIC) return GPTQ_ERR_INVALID_ARG;
+  if (grid == GPTQ_GRID_ASYMMETRIC && !zeros) return GPTQ_ERR_INVALID_ARG;
+  if (n < 1 || in < 1 || out < 1 || in > MAX_IN || out > MAX_OUT || n > ((int64_t)1 << 31) - 1)
+    return GPTQ_ERR_INVALID_ARG;
+  if (ld_x < in || ld_y < out || !valid_dtype(x_dtype) || bits < 2 || bits > 8 || group < 0 || (relu != 0 && relu != 1))
+    return GPTQ_ERR_INVALID_ARG;
+  if (((n + 63) / 64) * ((out + 63) / 64) > (int64_t)INT32_MAX) return GPTQ_ERR_INVALID_ARG;  // one workgroup per 64 x 64 tile
+  const int n_groups = group ? (int)((in + group - 1) / group) : 1;
+  return hip_status(dequant_matmul_launch(X, x_dtype, n, in, ld_x, packed, scales, zeros, g_idx, out, bits, grid,
+                                          n_groups, bias, relu, Y, ld_y, reinterpret_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -55,4 +55,13 @@ hipError_t quantize_launch(const void* W, int w_dtype, int64_t out, int64_t in, 
                            float* scales, int32_t* zeros, int32_t* g_idx, double* row_loss, void* ws,
                            hipStream_t stream);
 
+// Packed codes and the dequantizing matmul (pack.hip)
+int64_t packed_words_per_row(int64_t in, int bits);
+hipError_t pack_launch(const int8_t* codes, int64_t out, int64_t in, int bits, int grid, uint32_t* packed,
+                       hipStream_t stream);
+hipError_t dequant_matmul_launch(const void* X, int x_dtype, int64_t n, int64_t in, int64_t ld_x,
+                                 const uint32_t* packed, const float* scales, const int32_t* zeros,
+                                 const int32_t* g_idx, int64_t out, int bits, int grid, int n_groups,
+                                 const float* bias, int relu, float* Y, int64_t ld_y, hipStream_t stream);
+
 }  // namespace gptq

@@ -16,6 +16,7 @@ from ._lib import GPTQ_BF16, GPTQ_F32, GPTQ_FACTOR_INVERSE_RECHOL, GPTQ_FACTOR_R
 
 __all__ = [
     "HessianState", "hessian_accumulate", "prepare_chol", "quantize_layer", "gptq_quantize", "QuantResult",
+    "pack_codes", "dequant_matmul", "apply_layerwise", "QuantizedLayer",
     "GPTQ_FACTOR_INVERSE_RECHOL", "GPTQ_FACTOR_REVERSED",
 ]
 
@@ -166,6 +167,56 @@ def quantize_layer(W: torch.Tensor, U: torch.Tensor, perm: torch.Tensor, dead: t
     return QuantResult(codes, scales, g_idx, row_loss, perm, dead, U, zeros)
 
 
+def pack_codes(codes: torch.Tensor, bits: int, asymmetric: bool = False, stream=None) -> torch.Tensor:
+    """Codes (out x in, as quantize_layer returns them) -> uint32 bit streams, out x ceil(in*bits/32)."""
+    _req_cuda(codes, "codes")
+    if codes.dim() != 2 or not codes.is_contiguous() or codes.element_size() != 1:
+        raise ValueError("codes must be a contiguous 2-D int8/uint8 tensor")
+    out, d = codes.shape
+    lib = _lib.load()
+    wpr = lib.gptq_packed_words_per_row(d, int(bits))
+    if wpr <= 0:
+        raise ValueError("bad in/bits")
+    packed = torch.empty((out, wpr), dtype=torch.int32, device=codes.device)
+    grid = _lib.GPTQ_GRID_ASYMMETRIC if asymmetric else _lib.GPTQ_GRID_SYMMETRIC
+    check(lib.gptq_pack_codes(codes.data_ptr(), out, d, int(bits), grid, packed.data_ptr(), _stream(stream)),
+          "gptq_pack_codes")
+    return packed
+
+
+def dequant_matmul(X: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, g_idx: torch.Tensor, bits: int,
+                   group: int | None = None, zeros: torch.Tensor | None = None, bias: torch.Tensor | None = None,
+                   relu: bool = False, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Y = X Q^T (+ bias, then ReLU when asked), fp32 n x out, with Q dequantized from packed codes, scales
+    (and zeros) through g_idx."""
+    _req_cuda(X, "X")
+    ldx = _ld(X, "X")
+    n, d = X.shape
+    n_out = packed.shape[0]
+    group = int(group or 0)
+    n_groups = -(-d // group) if group else 1
+    _contig(scales, "scales", torch.float32, (n_out, n_groups))
+    _contig(g_idx, "g_idx", torch.int32, (d,))
+    if zeros is not None:
+        _contig(zeros, "zeros", torch.int32, (n_out, n_groups))
+    if bias is not None:
+        _contig(bias, "bias", torch.float32, (n_out,))
+    lib = _lib.load()
+    wpr = lib.gptq_packed_words_per_row(d, int(bits))
+    _contig(packed, "packed", torch.int32, (n_out, wpr))
+    if out is None:
+        out = torch.empty((n, n_out), dtype=torch.float32, device=X.device)
+    else:
+        _contig(out, "out", torch.float32, (n, n_out))
+    grid = _lib.GPTQ_GRID_ASYMMETRIC if zeros is not None else _lib.GPTQ_GRID_SYMMETRIC
+    st = lib.gptq_dequant_matmul(X.data_ptr(), _dtype_code(X), n, d, ldx, packed.data_ptr(), scales.data_ptr(),
+                                 zeros.data_ptr() if zeros is not None else None, g_idx.data_ptr(), n_out, int(bits),
+                                 grid, group, bias.data_ptr() if bias is not None else None, int(bool(relu)),
+                                 out.data_ptr(), n_out, _stream(stream))
+    check(st, "gptq_dequant_matmul")
+    return out
+
+
 def gptq_quantize(W: torch.Tensor, X: torch.Tensor, bits: int = 4, group: int | None = None, damp: float = 0.01,
                   act_order: bool = False, flags: int = GPTQ_FACTOR_INVERSE_RECHOL, stream=None,
                   asymmetric: bool = False) -> QuantResult:
@@ -174,3 +225,49 @@ def gptq_quantize(W: torch.Tensor, X: torch.Tensor, bits: int = 4, group: int | 
     hessian_accumulate(X, state, stream)
     U, perm, dead = prepare_chol(state.S, state.colsq, state.n_total, damp, act_order, flags, stream)
     return quantize_layer(W, U, perm, dead, bits, group, stream, asymmetric=asymmetric)
+
+
+@dataclass
+class QuantizedLayer:
+    """One layer of a layer-wise quantized MLP: the quantizer's outputs and the packed codes the forward
+    reads. result and packed are None for a layer kept at full precision (skip_last)."""
+    result: QuantResult | None
+    packed: torch.Tensor | None
+    bias: torch.Tensor | None
+    bits: int
+    group: int
+
+
+def apply_layerwise(weights, biases, X: torch.Tensor, bits: int = 4, group: int | None = None, damp: float = 0.01,
+                    act_order: bool = False, asymmetric: bool = False, skip_last: bool = False,
+                    flags: int = GPTQ_FACTOR_REVERSED, keep_inputs: bool = False, stream=None):
+    """Quantize an MLP layer by layer, calibrating each layer on the outputs of the layers before it after
+    they were quantized (GPTQ guide, "How it works", apply_layerwise).
+
+    weights[i]: out_i x in_i CUDA tensor (fp32 or bf16); biases[i]: fp32 [out_i] or None; X: n x in_0.
+    Each layer: Hessian of its input, U, the compensation loop, packed codes; then its forward
+    relu(h Q^T + b) (no ReLU on the last layer) by the dequantizing matmul, in fp32, is the next layer's
+    input. Returns (layers, inputs, h): inputs[i] the tensor layer i was calibrated on (only with
+    keep_inputs), h the network output, or None when the last layer is kept at full precision (its
+    forward feeds nothing here)."""
+    L = len(weights)
+    if len(biases) != L or L == 0:
+        raise ValueError("weights and biases must be non-empty lists of the same length")
+    group = int(group or 0)
+    h = X
+    layers, inputs = [], []
+    for i, W in enumerate(weights):
+        last = i == L - 1
+        if W.dim() != 2 or W.shape[1] != h.shape[1]:
+            raise ValueError(f"layer {i}: weight shape {tuple(W.shape)} does not take inputs of width {h.shape[1]}")
+        if keep_inputs:
+            inputs.append(h)
+        if skip_last and last:
+            layers.append(QuantizedLayer(None, None, biases[i], bits, group))
+            return layers, inputs, None
+        res = gptq_quantize(W, h, bits, group, damp, act_order, flags, stream, asymmetric=asymmetric)
+        packed = pack_codes(res.codes, bits, asymmetric, stream)
+        layers.append(QuantizedLayer(res, packed, biases[i], bits, group))
+        h = dequant_matmul(h, packed, res.scales, res.g_idx, bits, group, res.zeros, biases[i], relu=not last,
+                           stream=stream)
+    return layers, inputs, h

@@ -23,7 +23,7 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     lib = _lib.load()
     names = declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 12, names
     for n in names:
         assert hasattr(lib, n), n
         assert n in _lib.SIGNATURES, n
@@ -142,6 +142,38 @@ def test_quantize_ex_argument_errors():
     assert call(group=48) == _lib.GPTQ_ERR_UNSUPPORTED
     assert call(ws=None) == _lib.GPTQ_ERR_WORKSPACE
     assert call(grid=_lib.GPTQ_GRID_SYMMETRIC, zeros=None, ws=None) == _lib.GPTQ_ERR_WORKSPACE
+
+
+def test_pack_and_dequant_argument_errors():
+    lib = _lib.load()
+    bad = _lib.GPTQ_ERR_INVALID_ARG
+    assert lib.gptq_packed_words_per_row(256, 4) == 32
+    assert lib.gptq_packed_words_per_row(300, 3) == 29   # ceil(900 / 32)
+    assert lib.gptq_packed_words_per_row(1, 8) == 1
+    assert lib.gptq_packed_words_per_row(0, 4) == 0
+    assert lib.gptq_packed_words_per_row(16, 9) == 0
+    assert lib.gptq_pack_codes(None, 4, 16, 4, 0, FAKE, None) == bad
+    assert lib.gptq_pack_codes(FAKE, 4, 16, 4, 0, None, None) == bad
+    assert lib.gptq_pack_codes(FAKE, 0, 16, 4, 0, FAKE, None) == bad
+    assert lib.gptq_pack_codes(FAKE, 4, 16, 1, 0, FAKE, None) == bad
+    assert lib.gptq_pack_codes(FAKE, 4, 16, 4, 3, FAKE, None) == bad
+
+    def mm(X=FAKE, dt=1, n=8, d=16, ldx=16, P=FAKE, sc=FAKE, z=FAKE, gi=FAKE, out=4, bits=4, grid=1, group=0,
+           relu=0, Y=FAKE, ldy=4):
+        return lib.gptq_dequant_matmul(X, dt, n, d, ldx, P, sc, z, gi, out, bits, grid, group, None, relu, Y, ldy,
+                                       None)
+
+    assert mm(X=None) == bad
+    assert mm(P=None) == bad
+    assert mm(gi=None) == bad
+    assert mm(z=None) == bad               # asymmetric grid needs zeros
+    assert mm(grid=7) == bad
+    assert mm(ldx=15) == bad
+    assert mm(ldy=3) == bad
+    assert mm(dt=9) == bad
+    assert mm(bits=9) == bad
+    assert mm(n=0) == bad
+    assert mm(relu=2) == bad
 
 
 def test_missing_library_fails_loudly(tmp_path):
