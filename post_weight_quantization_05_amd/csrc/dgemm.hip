@@ -38,7 +38,7 @@ struct Lds {
 // T x 16 are fetched as 16-byte vectors into registers while the MFMAs of the previous chunk run, then
 // stored to the other LDS buffer.
 template <bool TA, bool TB, int T>
-__global__ __launch_bounds__(256, (T == 128) ? 2 : 1) void k_dgemm(DgemmArgs a) {
+__global__ __launch_bounds__(256) void k_dgemm(DgemmArgs a) {
   constexpr int NV = T * TK / 2 / 256;   // 16-byte loads per thread per operand and chunk
   using L = Lds<T>;
   __shared__ __attribute__((aligned(16))) double As[2][L::SZ];
@@ -57,6 +57,20 @@ __global__ __launch_bounds__(256, (T == 128) ? 2 : 1) void k_dgemm(DgemmArgs a) 
     const int ntn = (a.N + T - 1) / T;
     I = blockIdx.x / ntn;
     J = blockIdx.x - I * ntn;
+    // Triangular K-ranges make a tile's work depend on J (KMODE_GE_J) or on I (the other modes). The
+    // workgroups that share a CU are about 256 apart in dispatch order (8 XCDs x 32 CUs), so in every
+    // other run of 256 workgroups the K-determining coordinate is mirrored: long and short tiles then
+    // share CUs instead of piling up on the same ones. Both maps are permutations of the tile set.
+    if (a.kmode == KMODE_GE_J) {
+      const int64_t first = (int64_t)blockIdx.y * gridDim.x + (int64_t)I * ntn;  // this row's first tile
+      if ((first / 256) & 1) J = ntn - 1 - J;
+    } else if (a.kmode != KMODE_FULL) {
+      const int nti = (int)(gridDim.x / ntn);
+      const int R = max(1, 256 / ntn);  // tile rows per run of 256 workgroups
+      const int G = (nti + R - 1) / R;
+      const int g = I / R;
+      if ((((int)blockIdx.y * G + g) & 1) && (g + 1) * R <= nti) I = g * R + (R - 1 - (I - g * R));
+    }
   }
   const int M = (a.m_step != 0) ? min(a.M, a.m_lim - batch * a.m_step) : a.M;
   const int N = a.N;
@@ -212,14 +226,8 @@ static hipError_t dgemm_launch_t(const DgemmArgs& a, bool ta, bool tb, int batch
 
 hipError_t dgemm_launch(const DgemmArgs& a, bool ta, bool tb, int batches, hipStream_t stream) {
   if (a.M <= 0 || a.N <= 0 || batches <= 0) return hipSuccess;
-  // 128 x 128 tiles when they still give at least one workgroup per CU; 64 x 64 for small products
-  const int64_t t128 = a.tri_tiles ? (int64_t)((a.M + 127) / 128) * ((a.M + 127) / 128 + 1) / 2
-                                   : (int64_t)((a.M + 127) / 128) * ((a.N + 127) / 128);
-#ifdef GPTQ_DGEMM_T128
-  if (t128 * batches >= 256) return dgemm_launch_t<128>(a, ta, tb, batches, stream);
-#else
-  (void)t128;
-#endif
+  // 64 x 64 tiles only: the triangular K-ranges rely on zeros above the diagonal inside the
+  // factorization's 64 x 64 diagonal blocks, which is exactly one tile
   return dgemm_launch_t<64>(a, ta, tb, batches, stream);
 }
 
