@@ -21,9 +21,18 @@ struct DgemmArgs {
   int M, N, K;
   double alpha, beta;
   int tri_tiles;  // only tiles with I >= J (square C)
+  int lower_only; // rectangular C whose origin lies on a diagonal: tiles with I < J are skipped
   int kmode;
   int m_lim, m_step;  // when m_step != 0: rows of batch b = min(M, m_lim - b * m_step)
   int k_by_m;         // K of each batch equals its row count (square triangular A)
+  // When fuse_diag is set (A B^T products only), the workgroup of tile (0, 0) then factors the 64 x 64
+  // diagonal block diag_kb of diag_A (which that tile has just written) and stores its inverse in
+  // diag_Dinv, flagging bad pivots in diag_status, while the other tiles are still being computed.
+  int fuse_diag;
+  double* diag_A;
+  int diag_d, diag_kb;
+  double* diag_Dinv;
+  unsigned* diag_status;
 };
 
 hipError_t dgemm_launch(const DgemmArgs& a, bool ta, bool tb, int batches, hipStream_t stream);

@@ -1,4 +1,4 @@
-// fp64 tiled GEMM on gfx950 matrix cores (v_mfma_f64_4x4x4_f64, four 4x4x4 blocks per instruction), the
+// fp64 tiled GEMM on gfx950 matrix cores (v_mfma_f64_16x16x4_f64), the
 // shared core of the blocked factorization (trailing SYRK updates, triangular-inverse levels) and of the
 // quantize loop's trailing update W[:, b1:] -= Err U[b0:b1, b1:].
 //
@@ -6,11 +6,15 @@
 //   opA(A)[i][k] = TA ? A[k][i] : A[i][k],  opB(B)[k][j] = TB ? B[j][k] : B[k][j]  (row-major storage)
 //
 // Tiles are T x T (T = 64: 256 threads, 4 waves of 32 x 32); K runs in chunks of 16 through
-// double-buffered LDS. Options: only lower-triangle tiles (I >= J) of a square C; per-tile K-range
+// double-buffered LDS, fed from a register ring that keeps PD chunks of global loads in flight.
+// Options: only lower-triangle tiles (I >= J) of a square C; per-tile K-range
 // restrictions for triangular operands (their zero triangle is then never multiplied); and a batch index
 // (blockIdx.y) with per-operand strides and a per-batch row limit.
+#include <type_traits>
+
 #include "common.h"
 #include "dgemm.h"
+#include "diagblock.h"
 
 namespace gptq {
 
@@ -20,24 +24,32 @@ namespace {
 #define GPTQ_DGEMM_TK 16
 #endif
 constexpr int TK = GPTQ_DGEMM_TK;  // K per LDS chunk
+constexpr int PD = 3;  // operand chunks in flight (register ring)
+
+template <int K, int N, typename F>
+__device__ __forceinline__ void static_for_d(F&& f) {
+  if constexpr (K < N) {
+    f(std::integral_constant<int, K>{});
+    static_for_d<K + 1, N>(f);
+  }
+}
 
 // LDS layouts. An operand whose rows run along the tile's M (or N) dimension in memory (A^T, B) is kept
-// as [k][i] with rows padded to T + 16 doubles: the 16 consecutive i that a 16-lane group reads sit on
-// one half of the banks, the next k row on the other half. An operand whose rows run along k (A, B^T)
-// is kept as [i][k] with rows of 18 doubles: 16 lanes reading 16 rows at one k hit 16 distinct bank
-// pairs (9 i mod 16 is a permutation), and the next k shifts them by one pair. Both are filled with
-// 16-byte stores of two consecutive doubles.
+// as [k][i] with rows padded to T + 16 doubles; an operand whose rows run along k (A, B^T) is kept as
+// [i][k] with rows of TK + 4 doubles. A 16 x 4 fragment read (16 consecutive i, 4 consecutive k) then
+// touches every bank pair exactly twice in both layouts. Both are filled with 16-byte stores of two
+// consecutive doubles.
 template <int T>
 struct Lds {
   static constexpr int KI = T + 16;  // [k][i] row stride
-  static constexpr int IK = TK + 2;  // [i][k] row stride (= 2 mod 32)
+  static constexpr int IK = TK + 4;  // [i][k] row stride
   static constexpr int SZ = (TK * KI > T * IK) ? TK * KI : T * IK;
 };
 
 // T x T tile, 4 waves in 2 x 2, each (T/2) x (T/2). Operand chunks of
 // T x 16 are fetched as 16-byte vectors into registers while the MFMAs of the previous chunk run, then
 // stored to the other LDS buffer.
-template <bool TA, bool TB, int T>
+template <bool TA, bool TB, int T, bool DIAG>
 __global__ __launch_bounds__(256) void k_dgemm(DgemmArgs a) {
   constexpr int NV = T * TK / 2 / 256;   // 16-byte loads per thread per operand and chunk
   using L = Lds<T>;
@@ -72,6 +84,7 @@ __global__ __launch_bounds__(256) void k_dgemm(DgemmArgs a) {
       if ((((int)blockIdx.y * G + g) & 1) && (g + 1) * R <= nti) I = g * R + (R - 1 - (I - g * R));
     }
   }
+  if (a.lower_only && I < J) return;
   const int M = (a.m_step != 0) ? min(a.M, a.m_lim - batch * a.m_step) : a.M;
   const int N = a.N;
   const int K = a.k_by_m ? M : a.K;
@@ -112,97 +125,114 @@ __global__ __launch_bounds__(256) void k_dgemm(DgemmArgs a) {
   };
   // thread element e of a chunk: along-k operands (A, B^T) as rows x 8 pairs, along-tile operands as
   // 16 k-rows x T/2 pairs; both map 8 (resp. T/2) consecutive threads onto one contiguous row segment
-  double2 ra[NV], rb[NV];
-  auto gload = [&](int k0) {
+  // register ring: PD chunks of both operands in flight, so short-K and few-tile products (the panel
+  // solves and small updates of the factorization) wait for one global-memory latency, not one per chunk
+  double2 ra[PD][NV], rb[PD][NV];
+  auto gload = [&](auto slot_c, int k0) {
+    constexpr int slot = decltype(slot_c)::value;
 #pragma unroll
     for (int q = 0; q < NV; ++q) {
       const int e = tid + 256 * q;
       if (!TA) {
         const int ii = e / (TK / 2), kk = (e % (TK / 2)) * 2;
-        ra[q] = ld2(A, a.lda, i0 + ii, k0 + kk, M, klo, khi, a_vec);
+        ra[slot][q] = ld2(A, a.lda, i0 + ii, k0 + kk, M, klo, khi, a_vec);
       } else {
         const int kk = e / (T / 2), ii = (e % (T / 2)) * 2;
-        ra[q] = (k0 + kk < khi) ? ld2(A, a.lda, k0 + kk, i0 + ii, K, 0, M, a_vec) : make_double2(0.0, 0.0);
+        ra[slot][q] = (k0 + kk < khi) ? ld2(A, a.lda, k0 + kk, i0 + ii, K, 0, M, a_vec) : make_double2(0.0, 0.0);
       }
       if (!TB) {
         const int kk = e / (T / 2), jj = (e % (T / 2)) * 2;
-        rb[q] = (k0 + kk < khi) ? ld2(B, a.ldb, k0 + kk, j0 + jj, K, 0, N, b_vec) : make_double2(0.0, 0.0);
+        rb[slot][q] = (k0 + kk < khi) ? ld2(B, a.ldb, k0 + kk, j0 + jj, K, 0, N, b_vec) : make_double2(0.0, 0.0);
       } else {
         const int jj = e / (TK / 2), kk = (e % (TK / 2)) * 2;
-        rb[q] = ld2(B, a.ldb, j0 + jj, k0 + kk, N, klo, khi, b_vec);
+        rb[slot][q] = ld2(B, a.ldb, j0 + jj, k0 + kk, N, klo, khi, b_vec);
       }
     }
   };
-  auto lstore = [&](int st) {
+  auto lstore = [&](auto slot_c, int st) {
+    constexpr int slot = decltype(slot_c)::value;
 #pragma unroll
     for (int q = 0; q < NV; ++q) {
       const int e = tid + 256 * q;
-      if (!TA) *reinterpret_cast<double2*>(&As[st][(e / (TK / 2)) * L::IK + (e % (TK / 2)) * 2]) = ra[q];
-      else *reinterpret_cast<double2*>(&As[st][(e / (T / 2)) * L::KI + (e % (T / 2)) * 2]) = ra[q];
-      if (!TB) *reinterpret_cast<double2*>(&Bs[st][(e / (T / 2)) * L::KI + (e % (T / 2)) * 2]) = rb[q];
-      else *reinterpret_cast<double2*>(&Bs[st][(e / (TK / 2)) * L::IK + (e % (TK / 2)) * 2]) = rb[q];
+      if (!TA) *reinterpret_cast<double2*>(&As[st][(e / (TK / 2)) * L::IK + (e % (TK / 2)) * 2]) = ra[slot][q];
+      else *reinterpret_cast<double2*>(&As[st][(e / (T / 2)) * L::KI + (e % (T / 2)) * 2]) = ra[slot][q];
+      if (!TB) *reinterpret_cast<double2*>(&Bs[st][(e / (T / 2)) * L::KI + (e % (T / 2)) * 2]) = rb[slot][q];
+      else *reinterpret_cast<double2*>(&Bs[st][(e / (TK / 2)) * L::IK + (e % (TK / 2)) * 2]) = rb[slot][q];
     }
   };
 
-  // v_mfma_f64_4x4x4f64 runs four independent 4 x 4 x 4 products per instruction at the fp64 rate.
-  // Block b of an instruction takes A[i][k] from lane
-  // 16 k + 4 b + i, B[k][j] from lane 16 k + 4 b + j and leaves D[i][j] in lane 16 i + 4 b + j. Giving
-  // all four blocks the same 4 rows of A and consecutive 4-column groups of B makes one instruction a
-  // 4 x 16 tile of C: lane l supplies A[r0 + l % 4][k0 + l / 16] and B[k0 + l / 16][c0 + l % 16] and
-  // holds C[r0 + l / 16][c0 + l % 16]. A wave's (T/2) x (T/2) block is PR x PC such tiles.
-  constexpr int PR = T / 8;   // 4-row groups per wave
-  constexpr int PC = T / 32;  // 16-column groups per wave
-  double acc[PR][PC];
+  // v_mfma_f64_16x16x4f64: lane l supplies A[l % 16][l / 16] and B[l / 16][l % 16] of a 16 x 4 by
+  // 4 x 16 product and holds D[4 r + l / 16][l % 16] in register r. A wave's (T/2) x (T/2) block is
+  // FR x FC such 16 x 16 tiles.
+  constexpr int FR = T / 32;
+  constexpr int FC = T / 32;
+  f64x4 acc[FR][FC];
 #pragma unroll
-  for (int p = 0; p < PR; ++p)
+  for (int p = 0; p < FR; ++p)
 #pragma unroll
-    for (int q = 0; q < PC; ++q) acc[p][q] = 0.0;
+    for (int q = 0; q < FC; ++q) acc[p][q] = f64x4{0.0, 0.0, 0.0, 0.0};
 
   const int nk = (khi > klo) ? (khi - klo + TK - 1) / TK : 0;
-  if (nk > 0) {
-    gload(klo);
-    lstore(0);
-  }
+  static_for_d<0, PD>([&](auto pc) {
+    if (decltype(pc)::value < nk) gload(pc, klo + decltype(pc)::value * TK);
+  });
+  if (nk > 0) lstore(std::integral_constant<int, 0>{}, 0);
   __syncthreads();
-  const int lr = lane & 3, lk = lane >> 4, lc = lane & 15;
-  for (int kt = 0; kt < nk; ++kt) {
+  const int lk = lane >> 4, lc = lane & 15;
+  // chunk kt sits in ring slot kt % PD until it is stored to LDS buffer kt % 2
+  for (int kt0 = 0; kt0 < nk; kt0 += PD) {
+    static_for_d<0, PD>([&](auto pc) {
+    constexpr int p = decltype(pc)::value;
+    const int kt = kt0 + p;
+    if (kt >= nk) return;
     const int st = kt & 1;
-    if (kt + 1 < nk) gload(klo + (kt + 1) * TK);
+    if (kt + PD < nk) gload(pc, klo + (kt + PD) * TK);
 #pragma unroll
     for (int k4 = 0; k4 < TK; k4 += 4) {
       const int kr = k4 + lk;
-      double fa[PR], fb[PC];
+      double fa[FR], fb[FC];
 #pragma unroll
-      for (int p = 0; p < PR; ++p) {
-        const int i = wm * (T / 2) + p * 4 + lr;
-        fa[p] = TA ? As[st][kr * L::KI + i] : As[st][i * L::IK + kr];
+      for (int r = 0; r < FR; ++r) {
+        const int i = wm * (T / 2) + r * 16 + lc;
+        fa[r] = TA ? As[st][kr * L::KI + i] : As[st][i * L::IK + kr];
       }
 #pragma unroll
-      for (int q = 0; q < PC; ++q) {
+      for (int q = 0; q < FC; ++q) {
         const int j = wn * (T / 2) + q * 16 + lc;
         fb[q] = TB ? Bs[st][j * L::IK + kr] : Bs[st][kr * L::KI + j];
       }
 #pragma unroll
-      for (int p = 0; p < PR; ++p)
+      for (int r = 0; r < FR; ++r)
 #pragma unroll
-        for (int q = 0; q < PC; ++q) acc[p][q] = __builtin_amdgcn_mfma_f64_4x4x4f64(fa[p], fb[q], acc[p][q], 0, 0, 0);
+        for (int q = 0; q < FC; ++q) acc[r][q] = __builtin_amdgcn_mfma_f64_16x16x4f64(fa[r], fb[q], acc[r][q], 0, 0, 0);
     }
-    if (kt + 1 < nk) lstore(st ^ 1);
+    if (kt + 1 < nk) lstore(std::integral_constant<int, (p + 1) % PD>{}, st ^ 1);
     __syncthreads();
+    });
   }
 
+  const bool diag_tile = (a.tri_tiles || a.lower_only) && I == J;
 #pragma unroll
-  for (int p = 0; p < PR; ++p)
+  for (int r = 0; r < FR; ++r)
 #pragma unroll
-    for (int q = 0; q < PC; ++q) {
-      const int gi = i0 + wm * (T / 2) + p * 4 + lk;
-      const int gj = j0 + wn * (T / 2) + q * 16 + lc;
-      if (gi < M && gj < N) {
-        double* ptr = C + (int64_t)gi * a.ldc + gj;
-        const double v = a.alpha * acc[p][q];
-        *ptr = (a.beta == 0.0) ? v : fma(a.beta, *ptr, v);
+    for (int q = 0; q < FC; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int gi = i0 + wm * (T / 2) + r * 16 + 4 * e + lk;
+        const int gj = j0 + wn * (T / 2) + q * 16 + lc;
+        if (gi < M && gj < N) {
+          double* ptr = C + (int64_t)gi * a.ldc + gj;
+          const double v = a.alpha * acc[r][q][e];
+          // a diagonal tile of a triangular update writes its lower triangle only
+          if (!diag_tile || gj - j0 <= gi - i0) *ptr = (a.beta == 0.0) ? v : fma(a.beta, *ptr, v);
+        }
       }
+  if constexpr (DIAG) {
+    if (blockIdx.x == 0 && blockIdx.y == 0) {
+      __syncthreads();  // the tile's stores are visible to the whole workgroup
+      diagblock::factor_diag_block(a.diag_A, a.diag_d, a.diag_d, a.diag_kb, a.diag_Dinv, a.diag_status);
     }
+  }
 }
 
 }  // namespace
@@ -217,17 +247,21 @@ static hipError_t dgemm_launch_t(const DgemmArgs& a, bool ta, bool tb, int batch
     tiles = ((a.M + T - 1) / T) * ((a.N + T - 1) / T);
   }
   dim3 grid(tiles, batches);
-  if (!ta && !tb) k_dgemm<false, false, T><<<grid, dim3(256), 0, stream>>>(a);
-  else if (!ta && tb) k_dgemm<false, true, T><<<grid, dim3(256), 0, stream>>>(a);
-  else if (ta && !tb) k_dgemm<true, false, T><<<grid, dim3(256), 0, stream>>>(a);
-  else k_dgemm<true, true, T><<<grid, dim3(256), 0, stream>>>(a);
+  if (a.fuse_diag) {
+    // the fused diagonal factorization needs tile (0, 0) at the block's origin, unmirrored
+    if (ta || !tb || a.kmode != KMODE_FULL || a.tri_tiles || !a.diag_A) return hipErrorInvalidValue;
+    k_dgemm<false, true, T, true><<<grid, dim3(256), 0, stream>>>(a);
+  } else if (!ta && !tb) k_dgemm<false, false, T, false><<<grid, dim3(256), 0, stream>>>(a);
+  else if (!ta && tb) k_dgemm<false, true, T, false><<<grid, dim3(256), 0, stream>>>(a);
+  else if (ta && !tb) k_dgemm<true, false, T, false><<<grid, dim3(256), 0, stream>>>(a);
+  else k_dgemm<true, true, T, false><<<grid, dim3(256), 0, stream>>>(a);
   return hipGetLastError();
 }
 
 hipError_t dgemm_launch(const DgemmArgs& a, bool ta, bool tb, int batches, hipStream_t stream) {
   if (a.M <= 0 || a.N <= 0 || batches <= 0) return hipSuccess;
-  // 64 x 64 tiles only: the triangular K-ranges rely on zeros above the diagonal inside the
-  // factorization's 64 x 64 diagonal blocks, which is exactly one tile
+  // 64 x 64 tiles: the triangular K-ranges rely on zeros above the diagonal inside the factorization's
+  // 64 x 64 diagonal blocks, which is exactly one tile (128 x 128 tiles measured no faster here)
   return dgemm_launch_t<64>(a, ta, tb, batches, stream);
 }
 

@@ -1,0 +1,216 @@
+// Factorization of one 64 x 64 diagonal block (fp64, gfx950): Cholesky in place and the inverse of the
+// factor. Used by the stand-alone diagonal-block kernel and, fused, by the block-column update that
+// produces the next diagonal block (only the workgroup that owns that block runs it).
+//
+// GPTQ guide ("GPTQ", herodthegreater.github.io/pigeon/guide/gptq/), "GPTQ's two tricks", trick 2: U is
+// a Cholesky factor; these blocks are the diagonal steps of the blocked factorization that yields it.
+#pragma once
+#include <type_traits>
+
+#include "common.h"
+
+namespace gptq {
+namespace diagblock {
+
+constexpr int NB = 64;
+
+// compile-time loop (the 64-step elimination loops are too large for the unroller, and a runtime index
+// into the register-resident row would move it to scratch memory)
+template <int K, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (K < N) {
+    f(std::integral_constant<int, K>{});
+    static_for<K + 1, N>(f);
+  }
+}
+
+__device__ __forceinline__ double readlane_d(double v, int l) {
+  const long long x = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readlane((int)(x & 0xFFFFFFFFll), l);
+  const int hi = __builtin_amdgcn_readlane((int)(x >> 32), l);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+
+// 1/sqrt(a) for finite a > 0, to about 1 ulp without an IEEE square root or division: the hardware
+// estimate (about 2^-24 relative) refined by one third-order Newton step, y (1 + e/2 + 3e^2/8) with
+// e = 1 - a y^2 (truncation error about e^3, below 2^-70). Inputs below 2^-1000 are scaled by 2^1000
+// first so the estimate sees a normal number.
+__device__ __forceinline__ double rsqrt_refined(double a) {
+  const bool tiny = a < 0x1p-1000;
+  const double as = tiny ? a * 0x1p+1000 : a;
+  double y = __builtin_amdgcn_rsq(as);
+  const double e = fma(-(as * y), y, 1.0);
+  const double p = fma(e, 0.375, 0.5);
+  y = fma(y * e, p, y);
+  return tiny ? y * 0x1p+500 : y;
+}
+
+// v from lane 4q + R of each quad of lanes (DPP quad_perm [R, R, R, R]), both halves of the double
+template <int R>
+__device__ __forceinline__ double quad_bcast(double v) {
+  const long long x = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(x & 0xFFFFFFFFll), R * 0x55, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(x >> 32), R * 0x55, 0xF, 0xF, false);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+
+// Factor the diagonal block kb of A in place (lower, zeros above) and write its inverse to Dinv[kb].
+// 256 threads. The block is staged through LDS with coalesced loads and stores.
+//  Cholesky (wave 0): lane i holds row i in registers and eliminates right-looking. Pivot k is
+//  r_k[k]; 1/L[k][k] comes from rsqrt_refined, so no square root or division sits on the chain. After
+//  scaling column k, every lane updates its entries j > k with column k, which goes through LDS. The
+//  next pivot r_{k+1}[k+1] - L[k+1][k]^2 uses lane k+1's own registers only, so its square-root
+//  estimate overlaps the LDS round trip of the column.
+//  Inverse (all 4 waves): a quad of lanes owns column j of L^-1 (lane 4j + r holds rows i = r mod 4) and
+//  eliminates right-looking; the finished entry (L^-1)[k][j] reaches the other lanes of its quad by
+//  DPP. Column k of L is kept in LDS as Lc[k][r][m] = L[4m + r][k], with the four r-rows 144 bytes apart
+//  so a quad's four reads hit distinct banks.
+// Rows/columns past the matrix edge act as the identity. Pivots that are not > 0 or not finite set the
+// status bits and are replaced by 1 so the kernel still finishes.
+constexpr int LC_STRIDE = 18;  // doubles per (k, r) row of Lc
+
+__device__ __forceinline__ void factor_diag_block(double* __restrict__ A, int64_t lda, int d, int kb,
+                                                  double* __restrict__ Dinv, unsigned* status) {
+  __shared__ double Ls[NB][NB + 1];
+  __shared__ __attribute__((aligned(16))) double Lc[NB][4][LC_STRIDE];
+  __shared__ double col[NB];
+  __shared__ double rdg[NB];
+  const int o = kb * NB;
+  const int m = min(NB, d - o);
+  const int tid = threadIdx.x;
+  {
+    // all 16 loads of a thread in flight at once (addresses clamped into the block, values selected)
+    double v[NB * NB / 256];
+#pragma unroll
+    for (int t = 0; t < NB * NB / 256; ++t) {
+      const int e = tid + 256 * t, i = e / NB, j = e % NB;
+      const bool in = (i < m && j < m && j <= i);
+      const double x = A[(int64_t)(o + (in ? i : 0)) * lda + o + (in ? j : 0)];
+      v[t] = in ? x : ((i == j) ? 1.0 : 0.0);
+    }
+#pragma unroll
+    for (int t = 0; t < NB * NB / 256; ++t) {
+      const int e = tid + 256 * t;
+      Ls[e / NB][e % NB] = v[t];
+    }
+  }
+  __syncthreads();
+  if (tid < 64) {
+    const int i = tid;
+    unsigned flags = 0;
+    double r[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) r[j] = Ls[i][j];
+    // a pivot that is not > 0 or not finite is flagged and replaced by 1 (branch-free: it is uniform)
+    auto checked = [&](double p) {
+      const bool ok = (p > 0.0) && (p < INFINITY);
+      flags |= ok ? 0u : ((p <= 0.0) ? DEV_STATUS_NOT_SPD : DEV_STATUS_NONFINITE);
+      return ok ? p : 1.0;
+    };
+    double piv = checked(readlane_d(r[0], 0));
+    double y = rsqrt_refined(piv);
+    double ydiag = 0.0;
+    static_for<0, NB>([&](auto kc) {
+      constexpr int k = decltype(kc)::value;
+      r[k] = (i == k) ? piv * y : r[k] * y;
+      ydiag = (i == k) ? y : ydiag;
+      if constexpr (k + 1 < NB) {
+        // next pivot from lane k+1's own entries: r[k+1] - L[k+1][k]^2 (no LDS on this path)
+        const double pn = checked(readlane_d(fma(-r[k], r[k], r[k + 1]), k + 1));
+        col[i] = r[k];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        constexpr int F = ((k + 1) & ~7), NC = (NB - F) / 8;  // chunks of 8 holding the entries > k
+        double buf[4][8];
+        auto rd = [&](auto cc) {
+          constexpr int c = decltype(cc)::value;
+#pragma unroll
+          for (int q = 0; q < 8; ++q) buf[c & 3][q] = col[F + 8 * c + q];
+        };
+        static_for<0, (NC < 3 ? NC : 3)>(rd);
+        __builtin_amdgcn_sched_barrier(0);
+        // the next pivot's 1/sqrt runs while the column reads are in flight
+        const double yn = rsqrt_refined(pn);
+        __builtin_amdgcn_sched_barrier(0);
+        static_for<0, NC>([&](auto cc) {
+          constexpr int c = decltype(cc)::value;
+          if constexpr (c + 3 < NC) rd(std::integral_constant<int, c + 3>{});
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            if (F + 8 * c + q > k) r[F + 8 * c + q] = fma(-r[k], buf[c & 3][q], r[F + 8 * c + q]);
+          }
+        });
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int j = k + 1; j < NB; ++j) asm volatile("" : "+v"(r[j]));
+        piv = pn;
+        y = yn;
+      }
+    });
+    rdg[i] = ydiag;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      Ls[i][j] = (j <= i) ? r[j] : 0.0;
+      Lc[j][i & 3][i >> 2] = (j < i) ? r[j] : 0.0;
+    }
+    if (flags && i == 0) atomicOr(status, flags);
+  }
+  __syncthreads();
+  {
+    double v[NB * NB / 256];
+#pragma unroll
+    for (int t = 0; t < NB * NB / 256; ++t) {
+      const int e = tid + 256 * t;
+      v[t] = Ls[e / NB][e % NB];
+    }
+#pragma unroll
+    for (int t = 0; t < NB * NB / 256; ++t) {
+      const int e = tid + 256 * t, i = e / NB, j = e % NB;
+      if (i < m && j < m) A[(int64_t)(o + i) * lda + o + j] = v[t];
+    }
+  }
+  // inverse: lane 4j + r holds c[q] = (L^-1)[4q + r][j], starting from e_j
+  const int jc = tid >> 2, rr = tid & 3;
+  double c[16];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) c[q] = (4 * q + rr == jc) ? 1.0 : 0.0;
+  // column k of L and 1/L[k][k] are read one step ahead, so their LDS latency is off the chain
+  double lcur[16], lnext[16];
+  double dcur = rdg[0], dnext = 0.0;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) lcur[q] = Lc[0][rr][q];
+  static_for<0, NB>([&](auto kc) {
+    constexpr int k = decltype(kc)::value;
+    constexpr int mk = k >> 2, rk = k & 3;
+    if constexpr (k + 1 < NB) {
+#pragma unroll
+      for (int q = (k + 1) >> 2; q < 16; ++q) lnext[q] = Lc[k + 1][rr][q];
+      dnext = rdg[k + 1];
+    }
+    const double own = c[mk] * dcur;
+    c[mk] = (rr == rk) ? own : c[mk];
+    if constexpr (k + 1 < NB) {
+      const double b = quad_bcast<rk>(c[mk]);  // (L^-1)[k][j]
+#pragma unroll
+      for (int q = mk; q < 16; ++q) {
+        const double t = fma(-lcur[q], b, c[q]);
+        c[q] = (q > mk || rr > rk) ? t : c[q];
+      }
+#pragma unroll
+      for (int q = (k + 1) >> 2; q < 16; ++q) lcur[q] = lnext[q];
+      dcur = dnext;
+    }
+  });
+  double* D = Dinv + (int64_t)kb * NB * NB;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int row = 4 * q + rr;
+    D[row * NB + jc] = (row < m && jc < m) ? c[q] : ((row == jc) ? 1.0 : 0.0);
+  }
+}
+
+
+}  // namespace diagblock
+}  // namespace gptq

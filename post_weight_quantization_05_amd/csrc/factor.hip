@@ -12,8 +12,9 @@
 //                 non-finite check on colsq.
 //  k_perm         act_order permutation by ranks (descending key, ties by index): a stable sort.
 //  k_gather       H_p = P^T H P (optionally index-reversed) from S's lower triangle, lower part only.
-//  k_potrf_diag   one wave factors a 64 x 64 diagonal block in registers (lane = row) and inverts it
-//                 (lane = column); flags pivots that are not > 0 or not finite.
+//  k_potrf_diag   factors a 64 x 64 diagonal block (one wave, lane = row, rsqrt-refined pivots) and
+//                 inverts it (four waves, a quad of lanes per column); flags pivots that are not > 0
+//                 or not finite.
 //  panel / SYRK / triangular-inverse levels / H^-1 = L^-T L^-1 use the fp64 MFMA GEMM core (dgemm.hip).
 // Routes (flags): INVERSE_RECHOL = potrf, trtri, lauum, potrf, transpose (the guide's order);
 // REVERSED = potrf and trtri of J H J, then U = J L^-1 J (same unique U, half the work).
@@ -21,29 +22,13 @@
 
 #include "common.h"
 #include "dgemm.h"
+#include "diagblock.h"
 
 namespace gptq {
 
 namespace {
 
-constexpr int NB = 64;
-
-// compile-time loop (the 64-step elimination loops are too large for the unroller, and a runtime index
-// into the register-resident row would move it to scratch memory)
-template <int K, int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (K < N) {
-    f(std::integral_constant<int, K>{});
-    static_for<K + 1, N>(f);
-  }
-}
-
-__device__ __forceinline__ double readlane_d(double v, int l) {
-  const long long x = __double_as_longlong(v);
-  const int lo = __builtin_amdgcn_readlane((int)(x & 0xFFFFFFFFll), l);
-  const int hi = __builtin_amdgcn_readlane((int)(x >> 32), l);
-  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
-}
+using diagblock::NB;
 
 __global__ void k_zero_u32(unsigned* p) { *p = 0u; }
 
@@ -136,124 +121,9 @@ __global__ __launch_bounds__(256) void k_gather(const double* __restrict__ S, co
   }
   A[(int64_t)a * d + b] = v;
 }
-
-// Factor the diagonal block kb of A in place (lower, zeros above) and write its inverse to Dinv[kb].
-// One wave. Cholesky: lane i holds row i of the block in registers (right-looking: after pivot k every
-// lane updates its own entries j > k with column k, which goes through LDS). Inverse: lane j holds
-// column j of L^-1 and eliminates right-looking as well (c[i] -= L[i][k] c[k] for i > k). In both
-// phases a step's LDS values are read in chunks of 8 with three chunks in flight ahead of the
-// multiply-adds that use them, so a step waits for one LDS round trip, not one per chunk.
-// Rows/columns past the matrix edge act as the identity.
-template <int K>
-struct ChunkSpan {
-  static constexpr int first = ((K + 1) & ~7);                // first chunk start with entries > K
-  static constexpr int count = (NB - first) / 8;               // chunks of 8 from `first` to NB
-};
-
-__global__ __launch_bounds__(64) void k_potrf_diag(double* __restrict__ A, int64_t lda, int d, int kb,
-                                                   double* __restrict__ Dinv, unsigned* status) {
-  __shared__ double col[NB];
-  __shared__ double Ls[NB][NB + 1];
-  __shared__ double rdg[NB];
-  const int o = kb * NB;
-  const int m = min(NB, d - o);
-  const int i = threadIdx.x;
-  unsigned flags = 0;
-  {
-    double r[NB];
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      double v = (i == j) ? 1.0 : 0.0;
-      if (i < m && j < m && j <= i) v = A[(int64_t)(o + i) * lda + o + j];
-      r[j] = v;
-    }
-    static_for<0, NB>([&](auto kc) {
-      constexpr int k = decltype(kc)::value;
-      double piv = readlane_d(r[k], k);
-      if (!(piv > 0.0)) {
-        flags |= isfinite(piv) ? DEV_STATUS_NOT_SPD : DEV_STATUS_NONFINITE;
-        piv = 1.0;
-      } else if (!isfinite(piv)) {
-        flags |= DEV_STATUS_NONFINITE;
-        piv = 1.0;
-      }
-      const double lkk = sqrt(piv);
-      const double inv = 1.0 / lkk;
-      r[k] = (i == k) ? lkk : r[k] * inv;
-      if (i == k) rdg[k] = inv;  // 1 / L[k][k] for the inverse
-      if constexpr (k + 1 < NB) {
-        col[i] = r[k];
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        constexpr int F = ChunkSpan<k>::first, NC = ChunkSpan<k>::count;
-        double buf[4][8];
-        auto rd = [&](auto cc) {
-          constexpr int c = decltype(cc)::value;
-#pragma unroll
-          for (int q = 0; q < 8; ++q) buf[c & 3][q] = col[F + 8 * c + q];
-        };
-        static_for<0, (NC < 3 ? NC : 3)>(rd);
-        static_for<0, NC>([&](auto cc) {
-          constexpr int c = decltype(cc)::value;
-          if constexpr (c + 3 < NC) rd(std::integral_constant<int, c + 3>{});
-          __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-          for (int q = 0; q < 8; ++q) {
-            constexpr int dummy = 0;
-            (void)dummy;
-            const int jj = F + 8 * c + q;
-            if (jj > k) r[F + 8 * c + q] = fma(-r[k], buf[c & 3][q], r[F + 8 * c + q]);
-          }
-        });
-        __builtin_amdgcn_wave_barrier();
-#pragma unroll
-        for (int j = k + 1; j < NB; ++j) asm volatile("" : "+v"(r[j]));
-      }
-    });
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      const double v = (j <= i) ? r[j] : 0.0;
-      Ls[i][j] = v;
-      if (i < m && j < m) A[(int64_t)(o + i) * lda + o + j] = v;
-    }
-  }
-  if (flags && i == 0) atomicOr(status, flags);
-  __syncthreads();
-  // inverse: lane j holds column j of L^-1 (starts as e_j), right-looking elimination
-  const int jc = i;
-  double c[NB];
-#pragma unroll
-  for (int k = 0; k < NB; ++k) c[k] = (k == jc) ? 1.0 : 0.0;
-  static_for<0, NB>([&](auto kc) {
-    constexpr int k = decltype(kc)::value;
-    c[k] = c[k] * rdg[k];
-    if constexpr (k + 1 < NB) {
-      constexpr int F = ChunkSpan<k>::first, NC = ChunkSpan<k>::count;
-      double buf[4][8];
-      auto rd = [&](auto cc) {
-        constexpr int cb = decltype(cc)::value;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) buf[cb & 3][q] = Ls[F + 8 * cb + q][k];
-      };
-      static_for<0, (NC < 3 ? NC : 3)>(rd);
-      static_for<0, NC>([&](auto cc) {
-        constexpr int cb = decltype(cc)::value;
-        if constexpr (cb + 3 < NC) rd(std::integral_constant<int, cb + 3>{});
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const int r2 = F + 8 * cb + q;
-          if (r2 > k) c[F + 8 * cb + q] = fma(-buf[cb & 3][q], c[k], c[F + 8 * cb + q]);
-        }
-      });
-#pragma unroll
-      for (int j = k; j < NB; ++j) asm volatile("" : "+v"(c[j]));
-    }
-  });
-  double* D = Dinv + (int64_t)kb * NB * NB;
-#pragma unroll
-  for (int k = 0; k < NB; ++k) D[k * NB + jc] = (k < m && jc < m) ? c[k] : ((k == jc) ? 1.0 : 0.0);
+__global__ __launch_bounds__(256) void k_potrf_diag(double* __restrict__ A, int64_t lda, int d, int kb,
+                                                    double* __restrict__ Dinv, unsigned* status) {
+  diagblock::factor_diag_block(A, lda, d, kb, Dinv, status);
 }
 
 // Copy the inverted diagonal blocks into the diagonal of A (start of the triangular inverse).
@@ -310,38 +180,72 @@ __global__ __launch_bounds__(256) void k_reverse_to_upper(const double* __restri
   U[(int64_t)a * d + b] = (b >= a) ? Li[(int64_t)(d - 1 - a) * d + (d - 1 - b)] : 0.0;
 }
 
+// Blocked right-looking Cholesky in two levels. Inside an outer block column of NBO columns, each
+// 64-column step factors its diagonal block, solves its panel for every row below, and updates only the
+// remaining columns of the outer block (K = 64). After the outer block, one product with K = NBO updates
+// the whole trailing matrix. Same operations as the one-level form, in fewer and larger launches.
+constexpr int NBO = 256;
+
 hipError_t potrf_lower(double* A, int d, double* Dinv, unsigned* status, hipStream_t stream) {
-  const int nblk = (d + NB - 1) / NB;
-  for (int kb = 0; kb < nblk; ++kb) {
-    hipLaunchKernelGGL(k_potrf_diag, dim3(1), dim3(64), 0, stream, A, (int64_t)d, d, kb, Dinv, status);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const int o = kb * NB;
-    const int m = min(NB, d - o);
-    const int rest = d - o - m;
-    if (rest <= 0) break;
-    double* panel = A + (int64_t)(o + m) * d + o;
-    // panel <- panel * Dinv^T (solve X L_kk^T = panel)
-    DgemmArgs p{};
-    p.A = panel; p.lda = d;
-    p.B = Dinv + (int64_t)kb * NB * NB; p.ldb = NB;
-    p.C = panel; p.ldc = d;
-    p.M = rest; p.N = m; p.K = m;
-    p.alpha = 1.0; p.beta = 0.0;
-    p.kmode = KMODE_FULL;
-    e = dgemm_launch(p, false, true, 1, stream);
-    if (e != hipSuccess) return e;
-    // trailing update, lower tiles: A22 -= panel panel^T
-    DgemmArgs s{};
-    s.A = panel; s.lda = d;
-    s.B = panel; s.ldb = d;
-    s.C = A + (int64_t)(o + m) * d + (o + m); s.ldc = d;
-    s.M = rest; s.N = rest; s.K = m;
-    s.alpha = -1.0; s.beta = 1.0;
-    s.tri_tiles = 1;
-    s.kmode = KMODE_FULL;
-    e = dgemm_launch(s, false, true, 1, stream);
-    if (e != hipSuccess) return e;
+  bool diag_done = false;  // the previous block-column update already factored this diagonal block
+  for (int b0 = 0; b0 < d; b0 += NBO) {
+    const int b1 = min(d, b0 + NBO);
+    for (int o = b0; o < b1; o += NB) {
+      const int kb = o / NB;
+      hipError_t e;
+      if (!diag_done) {
+        hipLaunchKernelGGL(k_potrf_diag, dim3(1), dim3(256), 0, stream, A, (int64_t)d, d, kb, Dinv, status);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+      }
+      diag_done = false;
+      const int m = min(NB, d - o);
+      const int c1 = o + m;
+      const int rest = d - c1;
+      if (rest <= 0) return hipSuccess;
+      double* panel = A + (int64_t)c1 * d + o;
+      // panel <- panel * Dinv^T (solve X L_kk^T = panel)
+      DgemmArgs p{};
+      p.A = panel; p.lda = d;
+      p.B = Dinv + (int64_t)kb * NB * NB; p.ldb = NB;
+      p.C = panel; p.ldc = d;
+      p.M = rest; p.N = m; p.K = m;
+      p.alpha = 1.0; p.beta = 0.0;
+      p.kmode = KMODE_FULL;
+      e = dgemm_launch(p, false, true, 1, stream);
+      if (e != hipSuccess) return e;
+      if (c1 < b1) {
+        // the outer block's remaining columns: A[c1:, c1:b1] -= panel panel[c1:b1]^T (lower tiles);
+        // tile (0, 0) is the next diagonal block, which its workgroup factors right away
+        DgemmArgs s{};
+        s.A = panel; s.lda = d;
+        s.B = panel; s.ldb = d;
+        s.C = A + (int64_t)c1 * d + c1; s.ldc = d;
+        s.M = rest; s.N = b1 - c1; s.K = m;
+        s.alpha = -1.0; s.beta = 1.0;
+        s.lower_only = 1;
+        s.kmode = KMODE_FULL;
+        s.fuse_diag = 1;
+        s.diag_A = A; s.diag_d = d; s.diag_kb = kb + 1; s.diag_Dinv = Dinv; s.diag_status = status;
+        e = dgemm_launch(s, false, true, 1, stream);
+        if (e != hipSuccess) return e;
+        diag_done = true;
+      }
+    }
+    if (b1 < d) {
+      // trailing update with the whole outer panel: A22 -= Q Q^T, Q = A[b1:, b0:b1] (lower tiles)
+      const double* Q = A + (int64_t)b1 * d + b0;
+      DgemmArgs s{};
+      s.A = Q; s.lda = d;
+      s.B = Q; s.ldb = d;
+      s.C = A + (int64_t)b1 * d + b1; s.ldc = d;
+      s.M = d - b1; s.N = d - b1; s.K = b1 - b0;
+      s.alpha = -1.0; s.beta = 1.0;
+      s.tri_tiles = 1;
+      s.kmode = KMODE_FULL;
+      hipError_t e = dgemm_launch(s, false, true, 1, stream);
+      if (e != hipSuccess) return e;
+    }
   }
   return hipSuccess;
 }
