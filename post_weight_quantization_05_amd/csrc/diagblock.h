@@ -31,18 +31,14 @@ __device__ __forceinline__ double readlane_d(double v, int l) {
   return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
 }
 
-// 1/sqrt(a) for finite a > 0, to about 1 ulp without an IEEE square root or division: the hardware
-// estimate (about 2^-24 relative) refined by one third-order Newton step, y (1 + e/2 + 3e^2/8) with
-// e = 1 - a y^2 (truncation error about e^3, below 2^-70). Inputs below 2^-1000 are scaled by 2^1000
-// first so the estimate sees a normal number.
+// 1/sqrt(a) for finite a >= 2^-1000, to about 1 ulp without an IEEE square root or division: the
+// hardware estimate (about 2^-24 relative) refined by one third-order Newton step, y (1 + e/2 + 3e^2/8)
+// with e = 1 - a y^2 (truncation error about e^3, below 2^-70). Smaller pivots are flagged by the caller.
 __device__ __forceinline__ double rsqrt_refined(double a) {
-  const bool tiny = a < 0x1p-1000;
-  const double as = tiny ? a * 0x1p+1000 : a;
-  double y = __builtin_amdgcn_rsq(as);
-  const double e = fma(-(as * y), y, 1.0);
+  const double y = __builtin_amdgcn_rsq(a);
+  const double e = fma(-(a * y), y, 1.0);
   const double p = fma(e, 0.375, 0.5);
-  y = fma(y * e, p, y);
-  return tiny ? y * 0x1p+500 : y;
+  return fma(y * e, p, y);
 }
 
 // v from lane 4q + R of each quad of lanes (DPP quad_perm [R, R, R, R]), both halves of the double
@@ -65,8 +61,8 @@ __device__ __forceinline__ double quad_bcast(double v) {
 //  eliminates right-looking; the finished entry (L^-1)[k][j] reaches the other lanes of its quad by
 //  DPP. Column k of L is kept in LDS as Lc[k][r][m] = L[4m + r][k], with the four r-rows 144 bytes apart
 //  so a quad's four reads hit distinct banks.
-// Rows/columns past the matrix edge act as the identity. Pivots that are not > 0 or not finite set the
-// status bits and are replaced by 1 so the kernel still finishes.
+// Rows/columns past the matrix edge act as the identity. Pivots below 2^-1000 or not finite set the
+// status bits (and are treated as 1 from there on).
 constexpr int LC_STRIDE = 18;  // doubles per (k, r) row of Lc
 
 __device__ __forceinline__ void factor_diag_block(double* __restrict__ A, int64_t lda, int d, int kb,
@@ -99,24 +95,29 @@ __device__ __forceinline__ void factor_diag_block(double* __restrict__ A, int64_
     const int i = tid;
     unsigned flags = 0;
     double r[NB];
+    int ir = i;
+    asm volatile("" : "+v"(ir));
 #pragma unroll
-    for (int j = 0; j < NB; ++j) r[j] = Ls[i][j];
-    // a pivot that is not > 0 or not finite is flagged and replaced by 1 (branch-free: it is uniform)
-    auto checked = [&](double p) {
-      const bool ok = (p > 0.0) && (p < INFINITY);
-      flags |= ok ? 0u : ((p <= 0.0) ? DEV_STATUS_NOT_SPD : DEV_STATUS_NONFINITE);
-      return ok ? p : 1.0;
+    for (int j = 0; j < NB; ++j) r[j] = Ls[ir][j];
+    // A pivot that is not finite, or below 2^-1000 (not > 0 in particular), is flagged and its 1/sqrt
+    // replaced by 1, so a matrix that is not positive definite leaves finite values behind; the caller
+    // reports the status. The test runs beside the pivot chain and only the final select joins it.
+    auto inv_sqrt = [&](double p) {
+      const bool ok = (p >= 0x1p-1000) && (p < INFINITY);
+      flags |= ok ? 0u : (isfinite(p) ? DEV_STATUS_NOT_SPD : DEV_STATUS_NONFINITE);
+      const double yr = rsqrt_refined(p);
+      return ok ? yr : 1.0;
     };
-    double piv = checked(readlane_d(r[0], 0));
-    double y = rsqrt_refined(piv);
+    double piv = readlane_d(r[0], 0);
+    double y = inv_sqrt(piv);
     double ydiag = 0.0;
     static_for<0, NB>([&](auto kc) {
       constexpr int k = decltype(kc)::value;
-      r[k] = (i == k) ? piv * y : r[k] * y;
+      r[k] = r[k] * y;  // lane k: piv y = L[k][k]; lanes below: L[i][k]
       ydiag = (i == k) ? y : ydiag;
       if constexpr (k + 1 < NB) {
         // next pivot from lane k+1's own entries: r[k+1] - L[k+1][k]^2 (no LDS on this path)
-        const double pn = checked(readlane_d(fma(-r[k], r[k], r[k + 1]), k + 1));
+        const double pn = readlane_d(fma(-r[k], r[k], r[k + 1]), k + 1);
         col[i] = r[k];
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
@@ -131,7 +132,7 @@ __device__ __forceinline__ void factor_diag_block(double* __restrict__ A, int64_
         static_for<0, (NC < 3 ? NC : 3)>(rd);
         __builtin_amdgcn_sched_barrier(0);
         // the next pivot's 1/sqrt runs while the column reads are in flight
-        const double yn = rsqrt_refined(pn);
+        const double yn = inv_sqrt(pn);
         __builtin_amdgcn_sched_barrier(0);
         static_for<0, NC>([&](auto cc) {
           constexpr int c = decltype(cc)::value;
@@ -150,29 +151,37 @@ __device__ __forceinline__ void factor_diag_block(double* __restrict__ A, int64_
       }
     });
     rdg[i] = ydiag;
+    // a fresh copy of the row index, so the compiler forms these addresses here instead of keeping the
+    // load addresses of the same rows alive through the elimination
+    int iw = i;
+    asm volatile("" : "+v"(iw));
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
-      Ls[i][j] = (j <= i) ? r[j] : 0.0;
-      Lc[j][i & 3][i >> 2] = (j < i) ? r[j] : 0.0;
+      Ls[iw][j] = (j <= iw) ? r[j] : 0.0;
+      Lc[j][iw & 3][iw >> 2] = (j < iw) ? r[j] : 0.0;
     }
     if (flags && i == 0) atomicOr(status, flags);
   }
   __syncthreads();
+  // a fresh copy of the thread index for the later phases (keeps the first phase's addresses from
+  // staying alive, and spilling, across the elimination)
+  int tw = tid;
+  asm volatile("" : "+v"(tw));
   {
     double v[NB * NB / 256];
 #pragma unroll
     for (int t = 0; t < NB * NB / 256; ++t) {
-      const int e = tid + 256 * t;
+      const int e = tw + 256 * t;
       v[t] = Ls[e / NB][e % NB];
     }
 #pragma unroll
     for (int t = 0; t < NB * NB / 256; ++t) {
-      const int e = tid + 256 * t, i = e / NB, j = e % NB;
+      const int e = tw + 256 * t, i = e / NB, j = e % NB;
       if (i < m && j < m) A[(int64_t)(o + i) * lda + o + j] = v[t];
     }
   }
   // inverse: lane 4j + r holds c[q] = (L^-1)[4q + r][j], starting from e_j
-  const int jc = tid >> 2, rr = tid & 3;
+  const int jc = tw >> 2, rr = tw & 3;
   double c[16];
 #pragma unroll
   for (int q = 0; q < 16; ++q) c[q] = (4 * q + rr == jc) ? 1.0 : 0.0;
