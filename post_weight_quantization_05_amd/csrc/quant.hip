@@ -268,6 +268,12 @@ __global__ __launch_bounds__(256) void k_panel(double* __restrict__ Wq, int out,
     err_m[m] = 0.0;
   }
 
+  // row j of the U block and 1/U[j][j] are read from LDS one step ahead, so the LDS latency stays off
+  // the chain of dependent steps
+  double ucur[8], unext[8];
+  double dcur = rdiag[0], dnext = 0.0;
+#pragma unroll
+  for (int m = 0; m < 8; ++m) ucur[m] = Us[0][c + 16 * m];
 #pragma unroll
   for (int jm = 0; jm < 8; ++jm) {
     // steps past the panel edge (j >= pw) need no guard: there w = 0, U = 0 and 1/U = 0, so they
@@ -275,6 +281,12 @@ __global__ __launch_bounds__(256) void k_panel(double* __restrict__ Wq, int out,
     static_for<0, 16>([&](auto jlc) {
       constexpr int jl = decltype(jlc)::value;
       const int j = jm * 16 + jl;
+      if (j + 1 < PW) {
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+          if (m >= (j + 1) / 16) unext[m] = Us[j + 1][c + 16 * m];
+        dnext = rdiag[j + 1];
+      }
       {
         if (INPANEL && (j % group) == 0) {
           double hi = ASYM ? -INFINITY : 0.0, lo = INFINITY;
@@ -299,19 +311,25 @@ __global__ __launch_bounds__(256) void k_panel(double* __restrict__ Wq, int out,
         double cq, qv;
         if (ASYM) {
           cq = fmin(fmax(rint(__dadd_rn(div_rn(wj, s, sy), z)), 0.0), qmax);
-          qv = __dmul_rn(s, __dsub_rn(cq, z));
+          qv = s * (cq - z);
         } else {
           cq = fmin(fmax(rint(div_rn(wj, s, sy)), -qmax), qmax);
-          qv = __dmul_rn(cq, s);
+          qv = cq * s;
         }
-        const double e = __dmul_rn(__dsub_rn(wj, qv), rdiag[j]);
-        if (c == jl) {
-          code_m[jm] = (int)cq;
-          err_m[jm] = e;
-        }
+        asm volatile("" : "+v"(qv));  // q is rounded before the subtraction (no contraction into an FMA)
+        const double e = (wj - qv) * dcur;
+        code_m[jm] = (c == jl) ? (int)cq : code_m[jm];
+        err_m[jm] = (c == jl) ? e : err_m[jm];
+        asm volatile("" : "+v"(code_m[jm]), "+v"(err_m[jm]));
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
-          if (m >= jm) w[m] = fma(-e, Us[j][c + 16 * m], w[m]);
+          if (m >= jm) w[m] = fma(-e, ucur[m], w[m]);
+        }
+        if (j + 1 < PW) {
+#pragma unroll
+          for (int m = 0; m < 8; ++m)
+            if (m >= (j + 1) / 16) ucur[m] = unext[m];
+          dcur = dnext;
         }
       }
     });
