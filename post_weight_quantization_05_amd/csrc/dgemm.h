@@ -25,16 +25,19 @@ struct DgemmArgs {
   int kmode;
   int m_lim, m_step;  // when m_step != 0: rows of batch b = min(M, m_lim - b * m_step)
   int k_by_m;         // K of each batch equals its row count (square triangular A)
-  // When fuse_diag is set (A B^T products only), the workgroup of tile (0, 0) then factors the 64 x 64
-  // diagonal block diag_kb of diag_A (which that tile has just written) and stores its inverse in
-  // diag_Dinv, flagging bad pivots in diag_status, while the other tiles are still being computed.
-  int fuse_diag;
-  double* diag_A;
-  int diag_d, diag_kb;
+  // Block-column step of the factorization (colstep_launch only): the next diagonal block is block
+  // diag_kb; its L goes to diag_Lstage[diag_kb], its L^-1 to diag_Dinv[diag_kb] (64 x 64 each), bad
+  // pivots to diag_status.
+  int diag_kb;
+  double* diag_Lstage;
   double* diag_Dinv;
   unsigned* diag_status;
 };
 
 hipError_t dgemm_launch(const DgemmArgs& a, bool ta, bool tb, int batches, hipStream_t stream);
+// One block-column step of the blocked Cholesky factorization (see k_colstep in dgemm.hip): C -= A B^T
+// on the lower tiles of the M x N region C, the diagonal block at its origin factored and inverted, and
+// the column-0 tiles below it solved against that factor.
+hipError_t colstep_launch(const DgemmArgs& a, hipStream_t stream);
 
 }  // namespace gptq

@@ -46,63 +46,17 @@ struct Lds {
   static constexpr int SZ = (TK * KI > T * IK) ? TK * KI : T * IK;
 };
 
-// T x T tile, 4 waves in 2 x 2, each (T/2) x (T/2). Operand chunks of
-// T x 16 are fetched as 16-byte vectors into registers while the MFMAs of the previous chunk run, then
-// stored to the other LDS buffer.
-template <bool TA, bool TB, int T, bool DIAG>
-__global__ __launch_bounds__(256) void k_dgemm(DgemmArgs a) {
+// acc = sum over k in [klo, khi) of opA(A)[i0 + i][k] opB(B)[k][j0 + j] for the T x T tile at (i0, j0)
+// (zero outside M x N x K). 4 waves in 2 x 2, each (T/2) x (T/2). Operand chunks of T x 16 are fetched
+// as 16-byte vectors into registers while the MFMAs of earlier chunks run, then stored to the other LDS
+// buffer. Ends with a barrier, so the LDS buffers may be reused at once.
+template <bool TA, bool TB, int T>
+__device__ __forceinline__ void tile_product(const DgemmArgs& a, const double* A, const double* B, int M, int N,
+                                             int K, int i0, int j0, int klo, int khi,
+                                             double (*As)[Lds<T>::SZ], double (*Bs)[Lds<T>::SZ],
+                                             f64x4 (&acc)[T / 32][T / 32]) {
   constexpr int NV = T * TK / 2 / 256;   // 16-byte loads per thread per operand and chunk
   using L = Lds<T>;
-  __shared__ __attribute__((aligned(16))) double As[2][L::SZ];
-  __shared__ __attribute__((aligned(16))) double Bs[2][L::SZ];
-
-  const int batch = blockIdx.y;
-  int I, J;
-  if (a.tri_tiles) {
-    const int t = blockIdx.x;
-    int I0 = (int)((sqrt(8.0 * (double)t + 1.0) - 1.0) * 0.5);
-    while ((I0 + 1) * (I0 + 2) / 2 <= t) ++I0;
-    while (I0 * (I0 + 1) / 2 > t) --I0;
-    I = I0;
-    J = t - I0 * (I0 + 1) / 2;
-  } else {
-    const int ntn = (a.N + T - 1) / T;
-    I = blockIdx.x / ntn;
-    J = blockIdx.x - I * ntn;
-    // Triangular K-ranges make a tile's work depend on J (KMODE_GE_J) or on I (the other modes). The
-    // workgroups that share a CU are about 256 apart in dispatch order (8 XCDs x 32 CUs), so in every
-    // other run of 256 workgroups the K-determining coordinate is mirrored: long and short tiles then
-    // share CUs instead of piling up on the same ones. Both maps are permutations of the tile set.
-    if (a.kmode == KMODE_GE_J) {
-      const int64_t first = (int64_t)blockIdx.y * gridDim.x + (int64_t)I * ntn;  // this row's first tile
-      if ((first / 256) & 1) J = ntn - 1 - J;
-    } else if (a.kmode != KMODE_FULL) {
-      const int nti = (int)(gridDim.x / ntn);
-      const int R = max(1, 256 / ntn);  // tile rows per run of 256 workgroups
-      const int G = (nti + R - 1) / R;
-      const int g = I / R;
-      if ((((int)blockIdx.y * G + g) & 1) && (g + 1) * R <= nti) I = g * R + (R - 1 - (I - g * R));
-    }
-  }
-  if (a.lower_only && I < J) return;
-  const int M = (a.m_step != 0) ? min(a.M, a.m_lim - batch * a.m_step) : a.M;
-  const int N = a.N;
-  const int K = a.k_by_m ? M : a.K;
-  const int i0 = I * T, j0 = J * T;
-  if (i0 >= M || j0 >= N) return;
-
-  // no __restrict__: the factorization's panel solve reads and writes the same block (each workgroup
-  // reads all of its rows before it writes them)
-  const double* A = a.A + (int64_t)batch * a.strideA;
-  const double* B = a.B + (int64_t)batch * a.strideB;
-  double* C = a.C + (int64_t)batch * a.strideC;
-
-  int klo = 0, khi = K;
-  if (a.kmode == KMODE_GE_J) klo = j0;                        // B lower triangular: B[k][j] = 0 for k < j
-  else if (a.kmode == KMODE_LT_I_END) khi = min(K, i0 + T);   // A lower triangular: A[i][k] = 0 for k > i
-  else if (a.kmode == KMODE_GE_I) klo = i0;                   // A^T with A lower: A[k][i] = 0 for k < i
-  klo = (klo / TK) * TK;
-
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   // vector loads need 16-byte aligned pairs; otherwise two scalar loads
@@ -166,7 +120,6 @@ __global__ __launch_bounds__(256) void k_dgemm(DgemmArgs a) {
   // FR x FC such 16 x 16 tiles.
   constexpr int FR = T / 32;
   constexpr int FC = T / 32;
-  f64x4 acc[FR][FC];
 #pragma unroll
   for (int p = 0; p < FR; ++p)
 #pragma unroll
@@ -210,6 +163,69 @@ __global__ __launch_bounds__(256) void k_dgemm(DgemmArgs a) {
     __syncthreads();
     });
   }
+}
+
+// T x T tile of C = alpha opA(A) opB(B) + beta C (see the file comment for the options).
+template <bool TA, bool TB, int T>
+__global__ __launch_bounds__(256) void k_dgemm(DgemmArgs a) {
+  using L = Lds<T>;
+  __shared__ __attribute__((aligned(16))) double As[2][L::SZ];
+  __shared__ __attribute__((aligned(16))) double Bs[2][L::SZ];
+
+  const int batch = blockIdx.y;
+  int I, J;
+  if (a.tri_tiles) {
+    const int t = blockIdx.x;
+    int I0 = (int)((sqrt(8.0 * (double)t + 1.0) - 1.0) * 0.5);
+    while ((I0 + 1) * (I0 + 2) / 2 <= t) ++I0;
+    while (I0 * (I0 + 1) / 2 > t) --I0;
+    I = I0;
+    J = t - I0 * (I0 + 1) / 2;
+  } else {
+    const int ntn = (a.N + T - 1) / T;
+    I = blockIdx.x / ntn;
+    J = blockIdx.x - I * ntn;
+    // Triangular K-ranges make a tile's work depend on J (KMODE_GE_J) or on I (the other modes). The
+    // workgroups that share a CU are about 256 apart in dispatch order (8 XCDs x 32 CUs), so in every
+    // other run of 256 workgroups the K-determining coordinate is mirrored: long and short tiles then
+    // share CUs instead of piling up on the same ones. Both maps are permutations of the tile set.
+    if (a.kmode == KMODE_GE_J) {
+      const int64_t first = (int64_t)blockIdx.y * gridDim.x + (int64_t)I * ntn;  // this row's first tile
+      if ((first / 256) & 1) J = ntn - 1 - J;
+    } else if (a.kmode != KMODE_FULL) {
+      const int nti = (int)(gridDim.x / ntn);
+      const int R = max(1, 256 / ntn);  // tile rows per run of 256 workgroups
+      const int G = (nti + R - 1) / R;
+      const int g = I / R;
+      if ((((int)blockIdx.y * G + g) & 1) && (g + 1) * R <= nti) I = g * R + (R - 1 - (I - g * R));
+    }
+  }
+  if (a.lower_only && I < J) return;
+  const int M = (a.m_step != 0) ? min(a.M, a.m_lim - batch * a.m_step) : a.M;
+  const int N = a.N;
+  const int K = a.k_by_m ? M : a.K;
+  const int i0 = I * T, j0 = J * T;
+  if (i0 >= M || j0 >= N) return;
+
+  // no __restrict__: the factorization's panel solve reads and writes the same block (each workgroup
+  // reads all of its rows before it writes them)
+  const double* A = a.A + (int64_t)batch * a.strideA;
+  const double* B = a.B + (int64_t)batch * a.strideB;
+  double* C = a.C + (int64_t)batch * a.strideC;
+
+  int klo = 0, khi = K;
+  if (a.kmode == KMODE_GE_J) klo = j0;                        // B lower triangular: B[k][j] = 0 for k < j
+  else if (a.kmode == KMODE_LT_I_END) khi = min(K, i0 + T);   // A lower triangular: A[i][k] = 0 for k > i
+  else if (a.kmode == KMODE_GE_I) klo = i0;                   // A^T with A lower: A[k][i] = 0 for k < i
+  klo = (klo / TK) * TK;
+
+  constexpr int FR = T / 32;
+  constexpr int FC = T / 32;
+  f64x4 acc[FR][FC];
+  tile_product<TA, TB, T>(a, A, B, M, N, K, i0, j0, klo, khi, As, Bs, acc);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int lk = lane >> 4, lc = lane & 15;
 
   const bool diag_tile = (a.tri_tiles || a.lower_only) && I == J;
 #pragma unroll
@@ -227,12 +243,155 @@ __global__ __launch_bounds__(256) void k_dgemm(DgemmArgs a) {
           if (!diag_tile || gj - j0 <= gi - i0) *ptr = (a.beta == 0.0) ? v : fma(a.beta, *ptr, v);
         }
       }
-  if constexpr (DIAG) {
-    if (blockIdx.x == 0 && blockIdx.y == 0) {
-      __syncthreads();  // the tile's stores are visible to the whole workgroup
-      diagblock::factor_diag_block(a.diag_A, a.diag_d, a.diag_d, a.diag_kb, a.diag_Dinv, a.diag_status);
-    }
+}
+
+// Block-column step of the factorization (T = 64, C = A B^T update with beta = 1, kmode FULL). C is the
+// region A[c1:, c1:c1 + N] of the matrix being factored, M x N with M >= N; its tile (0, 0) is the next
+// 64 x 64 diagonal block and its column-0 tiles below are the next panel. Workgroup roles:
+//  * tiles (I, J >= 1), I >= J: the update C -= A B^T, as k_dgemm with lower_only;
+//  * tile (0, 0): the updated diagonal block D is factored; L goes to diag_Lstage[kb], L^-1 to
+//    diag_Dinv[kb], bad pivots to diag_status. The block in C itself is not written in this launch;
+//  * tiles (I >= 1, 0): the updated tile X and, again, D from the same inputs (so every one of these
+//    workgroups gets the same L^-1 as tile (0, 0) without waiting for it); X is then solved,
+//    X L^-T = X (L^-1)^T, and written in place: the panel of the next step.
+// With K = 0 the update is empty and the launch only factors the block and solves the panel.
+template <int T>
+__global__ __launch_bounds__(256) void k_colstep(DgemmArgs a) {
+  static_assert(T == diagblock::NB, "the diagonal block is one tile");
+  using L = Lds<T>;
+  __shared__ __attribute__((aligned(16))) double ABs[4 * L::SZ];  // operands; later the tile X
+  __shared__ diagblock::DiagSmem dsm;
+  static_assert(4 * L::SZ >= T * (T + 1), "tile buffer");
+  double(*As)[L::SZ] = reinterpret_cast<double(*)[L::SZ]>(ABs);
+  double(*Bs)[L::SZ] = reinterpret_cast<double(*)[L::SZ]>(ABs + 2 * L::SZ);
+
+  const int ntn = (a.N + T - 1) / T;
+  const int I = blockIdx.x / ntn, J = blockIdx.x - I * ntn;
+  if (I < J) return;
+  const int M = a.M, N = a.N, K = a.K;
+  const int i0 = I * T, j0 = J * T;
+  if (i0 >= M || j0 >= N) return;
+  const double* A = a.A;
+  const double* B = a.B;
+  double* C = a.C;
+  constexpr int FR = T / 32;
+  constexpr int FC = T / 32;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int lk = lane >> 4, lc = lane & 15;
+  // element (r, q, e) of a thread's fragments is tile entry (ti(r, e), tj(q))
+  auto ti = [&](int r, int e) { return wm * (T / 2) + r * 16 + 4 * e + lk; };
+  auto tj = [&](int q) { return wn * (T / 2) + q * 16 + lc; };
+  const int m = min(T, N);  // size of the diagonal block
+  // column 0: the old values of this tile and of the diagonal block are loaded before the products,
+  // so their latency overlaps them
+  double cown[FR][FC][4], cdiag[FR][FC][4];
+  if (J == 0) {
+#pragma unroll
+    for (int r = 0; r < FR; ++r)
+#pragma unroll
+      for (int q = 0; q < FC; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = ti(r, e), j = tj(q);
+          const bool din = (i < m && j < m && j <= i);
+          cdiag[r][q][e] = din ? C[(int64_t)i * a.ldc + j] : 0.0;
+          const bool oin = (i0 + i < M && j < m);
+          cown[r][q][e] = (I > 0 && oin) ? C[(int64_t)(i0 + i) * a.ldc + j] : 0.0;
+        }
   }
+  f64x4 acc[FR][FC];
+  tile_product<false, true, T>(a, A, B, M, N, K, i0, j0, 0, K, As, Bs, acc);
+
+  if (J != 0) {
+    const bool diag_tile = (I == J);
+#pragma unroll
+    for (int r = 0; r < FR; ++r)
+#pragma unroll
+      for (int q = 0; q < FC; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int gi = i0 + ti(r, e), gj = j0 + tj(q);
+          if (gi < M && gj < N && (!diag_tile || gj - j0 <= gi - i0)) {
+            double* ptr = C + (int64_t)gi * a.ldc + gj;
+            *ptr = fma(a.beta, *ptr, a.alpha * acc[r][q][e]);
+          }
+        }
+    return;
+  }
+
+  // the updated diagonal block, staged for the factorization (identity past the edge)
+  auto stage_diag = [&](const f64x4 (&d)[FR][FC]) {
+#pragma unroll
+    for (int r = 0; r < FR; ++r)
+#pragma unroll
+      for (int q = 0; q < FC; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = ti(r, e), j = tj(q);
+          double v = (i == j) ? 1.0 : 0.0;
+          if (i < m && j < m && j <= i) v = fma(a.beta, cdiag[r][q][e], a.alpha * d[r][q][e]);
+          dsm.Ls[i][j] = v;
+        }
+  };
+  if (I == 0) {
+    stage_diag(acc);
+    __syncthreads();
+    diagblock::diag_factor(dsm, m, a.diag_Lstage + (int64_t)a.diag_kb * T * T, T,
+                           a.diag_Dinv + (int64_t)a.diag_kb * T * T, a.diag_status, false);
+    return;
+  }
+  // this tile, updated (kept in registers through the factorization)
+  f64x4 x[FR][FC];
+#pragma unroll
+  for (int r = 0; r < FR; ++r)
+#pragma unroll
+    for (int q = 0; q < FC; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int gi = i0 + ti(r, e), gj = tj(q);
+        x[r][q][e] = (gi < M && gj < m) ? fma(a.beta, cown[r][q][e], a.alpha * acc[r][q][e]) : 0.0;
+      }
+  f64x4 dacc[FR][FC];
+  tile_product<false, true, T>(a, A, B, M, N, K, 0, 0, 0, K, As, Bs, dacc);
+  stage_diag(dacc);
+  __syncthreads();
+  diagblock::diag_factor(dsm, m, nullptr, 0, nullptr, nullptr, true);  // L^-1 now in dsm.Ls
+  // X into LDS (row-major, stride T + 1), then X (L^-1)^T on the matrix cores
+  double(*Xs)[T + 1] = reinterpret_cast<double(*)[T + 1]>(ABs);
+#pragma unroll
+  for (int r = 0; r < FR; ++r)
+#pragma unroll
+    for (int q = 0; q < FC; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Xs[ti(r, e)][tj(q)] = x[r][q][e];
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < FR; ++r)
+#pragma unroll
+    for (int q = 0; q < FC; ++q) acc[r][q] = f64x4{0.0, 0.0, 0.0, 0.0};
+#pragma unroll 4
+  for (int k4 = 0; k4 < T; k4 += 4) {
+    const int kr = k4 + lk;
+    double fa[FR], fb[FC];
+#pragma unroll
+    for (int r = 0; r < FR; ++r) fa[r] = Xs[wm * (T / 2) + r * 16 + lc][kr];
+#pragma unroll
+    for (int q = 0; q < FC; ++q) fb[q] = dsm.Ls[wn * (T / 2) + q * 16 + lc][kr];  // (L^-1)^T[k][j]
+#pragma unroll
+    for (int r = 0; r < FR; ++r)
+#pragma unroll
+      for (int q = 0; q < FC; ++q) acc[r][q] = __builtin_amdgcn_mfma_f64_16x16x4f64(fa[r], fb[q], acc[r][q], 0, 0, 0);
+  }
+#pragma unroll
+  for (int r = 0; r < FR; ++r)
+#pragma unroll
+    for (int q = 0; q < FC; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int gi = i0 + ti(r, e), gj = tj(q);
+        if (gi < M && gj < m) C[(int64_t)gi * a.ldc + gj] = acc[r][q][e];
+      }
 }
 
 }  // namespace
@@ -247,14 +406,10 @@ static hipError_t dgemm_launch_t(const DgemmArgs& a, bool ta, bool tb, int batch
     tiles = ((a.M + T - 1) / T) * ((a.N + T - 1) / T);
   }
   dim3 grid(tiles, batches);
-  if (a.fuse_diag) {
-    // the fused diagonal factorization needs tile (0, 0) at the block's origin, unmirrored
-    if (ta || !tb || a.kmode != KMODE_FULL || a.tri_tiles || !a.diag_A) return hipErrorInvalidValue;
-    k_dgemm<false, true, T, true><<<grid, dim3(256), 0, stream>>>(a);
-  } else if (!ta && !tb) k_dgemm<false, false, T, false><<<grid, dim3(256), 0, stream>>>(a);
-  else if (!ta && tb) k_dgemm<false, true, T, false><<<grid, dim3(256), 0, stream>>>(a);
-  else if (ta && !tb) k_dgemm<true, false, T, false><<<grid, dim3(256), 0, stream>>>(a);
-  else k_dgemm<true, true, T, false><<<grid, dim3(256), 0, stream>>>(a);
+  if (!ta && !tb) k_dgemm<false, false, T><<<grid, dim3(256), 0, stream>>>(a);
+  else if (!ta && tb) k_dgemm<false, true, T><<<grid, dim3(256), 0, stream>>>(a);
+  else if (ta && !tb) k_dgemm<true, false, T><<<grid, dim3(256), 0, stream>>>(a);
+  else k_dgemm<true, true, T><<<grid, dim3(256), 0, stream>>>(a);
   return hipGetLastError();
 }
 
@@ -263,6 +418,14 @@ hipError_t dgemm_launch(const DgemmArgs& a, bool ta, bool tb, int batches, hipSt
   // 64 x 64 tiles: the triangular K-ranges rely on zeros above the diagonal inside the factorization's
   // 64 x 64 diagonal blocks, which is exactly one tile (128 x 128 tiles measured no faster here)
   return dgemm_launch_t<64>(a, ta, tb, batches, stream);
+}
+
+hipError_t colstep_launch(const DgemmArgs& a, hipStream_t stream) {
+  if (a.M <= 0 || a.N <= 0 || a.N > a.M || a.K < 0 || !a.diag_Lstage || !a.diag_Dinv || !a.diag_status)
+    return hipErrorInvalidValue;
+  const int tiles = ((a.M + 63) / 64) * ((a.N + 63) / 64);
+  k_colstep<64><<<dim3(tiles), dim3(256), 0, stream>>>(a);
+  return hipGetLastError();
 }
 
 }  // namespace gptq

@@ -1,6 +1,6 @@
-// Factorization of one 64 x 64 diagonal block (fp64, gfx950): Cholesky in place and the inverse of the
-// factor. Used by the stand-alone diagonal-block kernel and, fused, by the block-column update that
-// produces the next diagonal block (only the workgroup that owns that block runs it).
+// Factorization of one 64 x 64 diagonal block (fp64, gfx950): its Cholesky factor and the inverse of
+// the factor. Used by the block-column step of the blocked factorization (k_colstep), where the
+// workgroups of the next panel each factor the block from the same inputs.
 //
 // GPTQ guide ("GPTQ", herodthegreater.github.io/pigeon/guide/gptq/), "GPTQ's two tricks", trick 2: U is
 // a Cholesky factor; these blocks are the diagonal steps of the blocked factorization that yields it.
@@ -50,8 +50,9 @@ __device__ __forceinline__ double quad_bcast(double v) {
   return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
 }
 
-// Factor the diagonal block kb of A in place (lower, zeros above) and write its inverse to Dinv[kb].
-// 256 threads. The block is staged through LDS with coalesced loads and stores.
+// Factorization of one diagonal block staged in LDS (lower part; rows/columns past the matrix edge as
+// the identity): its Cholesky factor L and L^-1. 256 threads. Outputs are optional: L to global memory,
+// L^-1 to global memory, the status bits, and L^-1 left in LDS for a caller that solves with it.
 //  Cholesky (wave 0): lane i holds row i in registers and eliminates right-looking. Pivot k is
 //  r_k[k]; 1/L[k][k] comes from rsqrt_refined, so no square root or division sits on the chain. After
 //  scaling column k, every lane updates its entries j > k with column k, which goes through LDS. The
@@ -65,32 +66,25 @@ __device__ __forceinline__ double quad_bcast(double v) {
 // status bits (and are treated as 1 from there on).
 constexpr int LC_STRIDE = 18;  // doubles per (k, r) row of Lc
 
-__device__ __forceinline__ void factor_diag_block(double* __restrict__ A, int64_t lda, int d, int kb,
-                                                  double* __restrict__ Dinv, unsigned* status) {
-  __shared__ double Ls[NB][NB + 1];
-  __shared__ __attribute__((aligned(16))) double Lc[NB][4][LC_STRIDE];
-  __shared__ double col[NB];
-  __shared__ double rdg[NB];
-  const int o = kb * NB;
-  const int m = min(NB, d - o);
+struct DiagSmem {
+  double Ls[NB][NB + 1];                                // the block, later L (row-major)
+  __attribute__((aligned(16))) double Lc[NB][4][LC_STRIDE];  // Lc[k][r][m] = L[4m + r][k]
+  double col[NB];                                       // column k during the elimination
+  double rdg[NB];                                       // 1 / L[k][k]
+};
+
+// Factor the block in sm.Ls (staged by the caller, followed by a barrier). m is the block's size.
+//   Lout (nullable): L written to Lout[i * ldo + j] for i, j < m, zeros above the diagonal;
+//   Dout (nullable): L^-1 as a row-major 64 x 64 block, the identity past the edge;
+//   status (nullable): flags of bad pivots;
+//   inv_to_ls: on return (after a barrier), sm.Ls[i][j] holds L^-1[i][j] (zeros above the diagonal).
+__device__ __forceinline__ void diag_factor(DiagSmem& sm, int m, double* __restrict__ Lout, int64_t ldo,
+                                            double* __restrict__ Dout, unsigned* status, bool inv_to_ls) {
+  auto& Ls = sm.Ls;
+  auto& Lc = sm.Lc;
+  auto& col = sm.col;
+  auto& rdg = sm.rdg;
   const int tid = threadIdx.x;
-  {
-    // all 16 loads of a thread in flight at once (addresses clamped into the block, values selected)
-    double v[NB * NB / 256];
-#pragma unroll
-    for (int t = 0; t < NB * NB / 256; ++t) {
-      const int e = tid + 256 * t, i = e / NB, j = e % NB;
-      const bool in = (i < m && j < m && j <= i);
-      const double x = A[(int64_t)(o + (in ? i : 0)) * lda + o + (in ? j : 0)];
-      v[t] = in ? x : ((i == j) ? 1.0 : 0.0);
-    }
-#pragma unroll
-    for (int t = 0; t < NB * NB / 256; ++t) {
-      const int e = tid + 256 * t;
-      Ls[e / NB][e % NB] = v[t];
-    }
-  }
-  __syncthreads();
   if (tid < 64) {
     const int i = tid;
     unsigned flags = 0;
@@ -160,14 +154,14 @@ __device__ __forceinline__ void factor_diag_block(double* __restrict__ A, int64_
       Ls[iw][j] = (j <= iw) ? r[j] : 0.0;
       Lc[j][iw & 3][iw >> 2] = (j < iw) ? r[j] : 0.0;
     }
-    if (flags && i == 0) atomicOr(status, flags);
+    if (status && flags && i == 0) atomicOr(status, flags);
   }
   __syncthreads();
   // a fresh copy of the thread index for the later phases (keeps the first phase's addresses from
   // staying alive, and spilling, across the elimination)
   int tw = tid;
   asm volatile("" : "+v"(tw));
-  {
+  if (Lout) {
     double v[NB * NB / 256];
 #pragma unroll
     for (int t = 0; t < NB * NB / 256; ++t) {
@@ -177,7 +171,7 @@ __device__ __forceinline__ void factor_diag_block(double* __restrict__ A, int64_
 #pragma unroll
     for (int t = 0; t < NB * NB / 256; ++t) {
       const int e = tw + 256 * t, i = e / NB, j = e % NB;
-      if (i < m && j < m) A[(int64_t)(o + i) * lda + o + j] = v[t];
+      if (i < m && j < m) Lout[(int64_t)i * ldo + j] = v[t];
     }
   }
   // inverse: lane 4j + r holds c[q] = (L^-1)[4q + r][j], starting from e_j
@@ -212,14 +206,23 @@ __device__ __forceinline__ void factor_diag_block(double* __restrict__ A, int64_
       dcur = dnext;
     }
   });
-  double* D = Dinv + (int64_t)kb * NB * NB;
+  if (Dout) {
 #pragma unroll
-  for (int q = 0; q < 16; ++q) {
-    const int row = 4 * q + rr;
-    D[row * NB + jc] = (row < m && jc < m) ? c[q] : ((row == jc) ? 1.0 : 0.0);
+    for (int q = 0; q < 16; ++q) {
+      const int row = 4 * q + rr;
+      Dout[row * NB + jc] = (row < m && jc < m) ? c[q] : ((row == jc) ? 1.0 : 0.0);
+    }
+  }
+  if (inv_to_ls) {
+    __syncthreads();  // every thread is past its reads of Ls (the L store above)
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int row = 4 * q + rr;
+      Ls[row][jc] = (row < m && jc < m) ? c[q] : ((row == jc) ? 1.0 : 0.0);
+    }
+    __syncthreads();
   }
 }
-
 
 }  // namespace diagblock
 }  // namespace gptq

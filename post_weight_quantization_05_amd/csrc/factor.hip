@@ -12,9 +12,11 @@
 //                 non-finite check on colsq.
 //  k_perm         act_order permutation by ranks (descending key, ties by index): a stable sort.
 //  k_gather       H_p = P^T H P (optionally index-reversed) from S's lower triangle, lower part only.
-//  k_potrf_diag   factors a 64 x 64 diagonal block (one wave, lane = row, rsqrt-refined pivots) and
-//                 inverts it (four waves, a quad of lanes per column); flags pivots that are not > 0
-//                 or not finite.
+//  k_colstep      (dgemm.hip) one 64-column step of the blocked factorization: block-column update,
+//                 the next 64 x 64 diagonal block factored (one wave, lane = row, rsqrt-refined pivots)
+//                 and inverted (four waves, a quad of lanes per column; diagblock.h), the next panel
+//                 solved; flags pivots that are not > 0 or not finite.
+//  k_place_lblocks the staged factors of the diagonal blocks into A.
 //  panel / SYRK / triangular-inverse levels / H^-1 = L^-T L^-1 use the fp64 MFMA GEMM core (dgemm.hip).
 // Routes (flags): INVERSE_RECHOL = potrf, trtri, lauum, potrf, transpose (the guide's order);
 // REVERSED = potrf and trtri of J H J, then U = J L^-1 J (same unique U, half the work).
@@ -121,9 +123,17 @@ __global__ __launch_bounds__(256) void k_gather(const double* __restrict__ S, co
   }
   A[(int64_t)a * d + b] = v;
 }
-__global__ __launch_bounds__(256) void k_potrf_diag(double* __restrict__ A, int64_t lda, int d, int kb,
-                                                    double* __restrict__ Dinv, unsigned* status) {
-  diagblock::factor_diag_block(A, lda, d, kb, Dinv, status);
+// Copy the staged factors of the diagonal blocks into the diagonal of A (lower part, zeros above).
+__global__ __launch_bounds__(256) void k_place_lblocks(const double* __restrict__ Lst, double* __restrict__ A,
+                                                       int64_t lda, int d) {
+  const int kb = blockIdx.x;
+  const int o = kb * NB;
+  const int m = min(NB, d - o);
+  const double* Lb = Lst + (int64_t)kb * NB * NB;
+  for (int e = threadIdx.x; e < NB * NB; e += 256) {
+    const int i = e / NB, j = e % NB;
+    if (i < m && j < m) A[(int64_t)(o + i) * lda + o + j] = Lb[e];
+  }
 }
 
 // Copy the inverted diagonal blocks into the diagonal of A (start of the triangular inverse).
@@ -181,56 +191,42 @@ __global__ __launch_bounds__(256) void k_reverse_to_upper(const double* __restri
 }
 
 // Blocked right-looking Cholesky in two levels. Inside an outer block column of NBO columns, each
-// 64-column step factors its diagonal block, solves its panel for every row below, and updates only the
-// remaining columns of the outer block (K = 64). After the outer block, one product with K = NBO updates
-// the whole trailing matrix. Same operations as the one-level form, in fewer and larger launches.
-constexpr int NBO = 256;
+// 64-column step is one launch (k_colstep): the outer block's remaining columns get the previous
+// panel's update (K = 64), the next diagonal block is factored and inverted, and the next panel is
+// solved against it. After the outer block, one product with K = NBO updates the whole trailing
+// matrix. The factors of the diagonal blocks are staged in Lst and copied into A at the end (A's
+// diagonal block is read by several workgroups of the launch that factors it).
+#ifndef GPTQ_FACTOR_NBO
+#define GPTQ_FACTOR_NBO 256
+#endif
+constexpr int NBO = GPTQ_FACTOR_NBO;  // outer block width (a multiple of 64)
 
-hipError_t potrf_lower(double* A, int d, double* Dinv, unsigned* status, hipStream_t stream) {
-  bool diag_done = false;  // the previous block-column update already factored this diagonal block
+hipError_t potrf_lower(double* A, int d, double* Dinv, double* Lst, unsigned* status, hipStream_t stream) {
+  // one block-column step: update C = A[c1:, c1:c1 + n] with the panel A[c1:, o:o + k] (k = 0: no
+  // update), factor the diagonal block at (c1, c1), solve the panel below it
+  auto colstep = [&](int c1, int n, int o, int k) {
+    DgemmArgs s{};
+    const double* P = A + (int64_t)c1 * d + o;
+    s.A = P; s.lda = d;
+    s.B = P; s.ldb = d;
+    s.C = A + (int64_t)c1 * d + c1; s.ldc = d;
+    s.M = d - c1; s.N = n; s.K = k;
+    s.alpha = -1.0; s.beta = 1.0;
+    s.kmode = KMODE_FULL;
+    s.diag_kb = c1 / NB; s.diag_Lstage = Lst; s.diag_Dinv = Dinv; s.diag_status = status;
+    return colstep_launch(s, stream);
+  };
+  hipError_t e;
   for (int b0 = 0; b0 < d; b0 += NBO) {
     const int b1 = min(d, b0 + NBO);
-    for (int o = b0; o < b1; o += NB) {
-      const int kb = o / NB;
-      hipError_t e;
-      if (!diag_done) {
-        hipLaunchKernelGGL(k_potrf_diag, dim3(1), dim3(256), 0, stream, A, (int64_t)d, d, kb, Dinv, status);
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
-      }
-      diag_done = false;
-      const int m = min(NB, d - o);
-      const int c1 = o + m;
-      const int rest = d - c1;
-      if (rest <= 0) return hipSuccess;
-      double* panel = A + (int64_t)c1 * d + o;
-      // panel <- panel * Dinv^T (solve X L_kk^T = panel)
-      DgemmArgs p{};
-      p.A = panel; p.lda = d;
-      p.B = Dinv + (int64_t)kb * NB * NB; p.ldb = NB;
-      p.C = panel; p.ldc = d;
-      p.M = rest; p.N = m; p.K = m;
-      p.alpha = 1.0; p.beta = 0.0;
-      p.kmode = KMODE_FULL;
-      e = dgemm_launch(p, false, true, 1, stream);
+    // first block of the outer block column: its diagonal block and panel, no update
+    e = colstep(b0, min(NB, d - b0), b0, 0);
+    if (e != hipSuccess) return e;
+    for (int o = b0; o + NB < b1; o += NB) {
+      // the outer block's remaining columns get panel o; the next block is factored and its panel solved
+      const int c1 = o + NB;
+      e = colstep(c1, b1 - c1, o, NB);
       if (e != hipSuccess) return e;
-      if (c1 < b1) {
-        // the outer block's remaining columns: A[c1:, c1:b1] -= panel panel[c1:b1]^T (lower tiles);
-        // tile (0, 0) is the next diagonal block, which its workgroup factors right away
-        DgemmArgs s{};
-        s.A = panel; s.lda = d;
-        s.B = panel; s.ldb = d;
-        s.C = A + (int64_t)c1 * d + c1; s.ldc = d;
-        s.M = rest; s.N = b1 - c1; s.K = m;
-        s.alpha = -1.0; s.beta = 1.0;
-        s.lower_only = 1;
-        s.kmode = KMODE_FULL;
-        s.fuse_diag = 1;
-        s.diag_A = A; s.diag_d = d; s.diag_kb = kb + 1; s.diag_Dinv = Dinv; s.diag_status = status;
-        e = dgemm_launch(s, false, true, 1, stream);
-        if (e != hipSuccess) return e;
-        diag_done = true;
-      }
     }
     if (b1 < d) {
       // trailing update with the whole outer panel: A22 -= Q Q^T, Q = A[b1:, b0:b1] (lower tiles)
@@ -243,11 +239,13 @@ hipError_t potrf_lower(double* A, int d, double* Dinv, unsigned* status, hipStre
       s.alpha = -1.0; s.beta = 1.0;
       s.tri_tiles = 1;
       s.kmode = KMODE_FULL;
-      hipError_t e = dgemm_launch(s, false, true, 1, stream);
+      e = dgemm_launch(s, false, true, 1, stream);
       if (e != hipSuccess) return e;
     }
   }
-  return hipSuccess;
+  const int nblk = (d + NB - 1) / NB;
+  hipLaunchKernelGGL(k_place_lblocks, dim3(nblk), dim3(256), 0, stream, Lst, A, (int64_t)d, d);
+  return hipGetLastError();
 }
 
 // L (lower, in A, diagonal blocks already replaced by their inverses) -> L^-1 in place. T is scratch of
@@ -291,6 +289,7 @@ size_t prepare_ws_bytes(int64_t in) {
   size_t b = 0;
   b += align_up((size_t)d * d * sizeof(double), 256);          // A
   b += align_up((size_t)nblk * NB * NB * sizeof(double), 256);  // Dinv
+  b += align_up((size_t)nblk * NB * NB * sizeof(double), 256);  // staged factors of the diagonal blocks
   b += align_up((size_t)d * sizeof(double), 256);              // diag of H
   b += 256;                                                    // status
   return b;
@@ -305,6 +304,8 @@ hipError_t prepare_launch(const double* S, const double* colsq, int64_t n_total,
   double* A = reinterpret_cast<double*>(w);
   w += align_up((size_t)d * d * sizeof(double), 256);
   double* Dinv = reinterpret_cast<double*>(w);
+  w += align_up((size_t)nblk * NB * NB * sizeof(double), 256);
+  double* Lst = reinterpret_cast<double*>(w);
   w += align_up((size_t)nblk * NB * NB * sizeof(double), 256);
   double* diag_h = reinterpret_cast<double*>(w);
   w += align_up((size_t)d * sizeof(double), 256);
@@ -328,7 +329,7 @@ hipError_t prepare_launch(const double* S, const double* colsq, int64_t n_total,
                      d, reversed ? 1 : 0, A);
   GPTQ_TRY(hipGetLastError());
 
-  GPTQ_TRY(potrf_lower(A, d, Dinv, status, stream));
+  GPTQ_TRY(potrf_lower(A, d, Dinv, Lst, status, stream));
   hipLaunchKernelGGL(k_place_dinv, dim3((unsigned)nblk), dim3(256), 0, stream, Dinv, A, (int64_t)d, d);
   GPTQ_TRY(hipGetLastError());
   GPTQ_TRY(trtri_lower(A, d, U /* scratch */, stream));
@@ -346,7 +347,7 @@ hipError_t prepare_launch(const double* S, const double* colsq, int64_t n_total,
     g.tri_tiles = 1;
     g.kmode = KMODE_GE_I;
     GPTQ_TRY(dgemm_launch(g, true, false, 1, stream));
-    GPTQ_TRY(potrf_lower(U, d, Dinv, status, stream));
+    GPTQ_TRY(potrf_lower(U, d, Dinv, Lst, status, stream));
     const int nt = (d + 31) / 32;
     hipLaunchKernelGGL(k_transpose_lower_to_upper, dim3(nt * (nt + 1) / 2), dim3(256), 0, stream, U, d);
     GPTQ_TRY(hipGetLastError());
