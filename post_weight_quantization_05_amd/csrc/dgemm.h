@@ -21,6 +21,7 @@ struct DgemmArgs {
   int M, N, K;
   double alpha, beta;
   int tri_tiles;  // only tiles with I >= J (square C)
+  int tile_first; // tri_tiles: launch covers lower tiles tile_first, tile_first + 1, ... in tile order
   int lower_only; // rectangular C whose origin lies on a diagonal: tiles with I < J are skipped
   int kmode;
   int m_lim, m_step;  // when m_step != 0: rows of batch b = min(M, m_lim - b * m_step)
@@ -37,7 +38,9 @@ struct DgemmArgs {
 hipError_t dgemm_launch(const DgemmArgs& a, bool ta, bool tb, int batches, hipStream_t stream);
 // One block-column step of the blocked Cholesky factorization (see k_colstep in dgemm.hip): C -= A B^T
 // on the lower tiles of the M x N region C, the diagonal block at its origin factored and inverted, and
-// the column-0 tiles below it solved against that factor.
-hipError_t colstep_launch(const DgemmArgs& a, hipStream_t stream);
+// the column-0 tiles below it solved against that factor. The same launch also computes lower tiles
+// x_first .. x_first + x_count - 1 (in tile order) of x, an independent A B^T update of a square region
+// (x may be null when x_count is 0).
+hipError_t colstep_launch(const DgemmArgs& a, const DgemmArgs* x, int x_first, int x_count, hipStream_t stream);
 
 }  // namespace gptq

@@ -175,7 +175,7 @@ __global__ __launch_bounds__(256) void k_dgemm(DgemmArgs a) {
   const int batch = blockIdx.y;
   int I, J;
   if (a.tri_tiles) {
-    const int t = blockIdx.x;
+    const int t = blockIdx.x + a.tile_first;
     int I0 = (int)((sqrt(8.0 * (double)t + 1.0) - 1.0) * 0.5);
     while ((I0 + 1) * (I0 + 2) / 2 <= t) ++I0;
     while (I0 * (I0 + 1) / 2 > t) --I0;
@@ -256,7 +256,7 @@ __global__ __launch_bounds__(256) void k_dgemm(DgemmArgs a) {
 //    X L^-T = X (L^-1)^T, and written in place: the panel of the next step.
 // With K = 0 the update is empty and the launch only factors the block and solves the panel.
 template <int T>
-__global__ __launch_bounds__(256) void k_colstep(DgemmArgs a) {
+__global__ __launch_bounds__(256) void k_colstep(DgemmArgs a, DgemmArgs xa, int x_first, int n_own) {
   static_assert(T == diagblock::NB, "the diagonal block is one tile");
   using L = Lds<T>;
   __shared__ __attribute__((aligned(16))) double ABs[4 * L::SZ];  // operands; later the tile X
@@ -265,6 +265,35 @@ __global__ __launch_bounds__(256) void k_colstep(DgemmArgs a) {
   double(*As)[L::SZ] = reinterpret_cast<double(*)[L::SZ]>(ABs);
   double(*Bs)[L::SZ] = reinterpret_cast<double(*)[L::SZ]>(ABs + 2 * L::SZ);
 
+  if ((int)blockIdx.x >= n_own) {
+    // a tile of the deferred trailing update xa (lower tiles of a square region, in tile order from
+    // x_first): independent of this step's own work, it fills CUs the step leaves idle
+    const int t = x_first + ((int)blockIdx.x - n_own);
+    int XI = (int)((sqrt(8.0 * (double)t + 1.0) - 1.0) * 0.5);
+    while ((XI + 1) * (XI + 2) / 2 <= t) ++XI;
+    while (XI * (XI + 1) / 2 > t) --XI;
+    const int XJ = t - XI * (XI + 1) / 2;
+    const int xi0 = XI * T, xj0 = XJ * T;
+    if (xi0 >= xa.M || xj0 >= xa.N) return;
+    f64x4 xacc[T / 32][T / 32];
+    tile_product<false, true, T>(xa, xa.A, xa.B, xa.M, xa.N, xa.K, xi0, xj0, 0, xa.K, As, Bs, xacc);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+    for (int r = 0; r < T / 32; ++r)
+#pragma unroll
+      for (int q = 0; q < T / 32; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int gi = xi0 + wm * (T / 2) + r * 16 + 4 * e + (lane >> 4);
+          const int gj = xj0 + wn * (T / 2) + q * 16 + (lane & 15);
+          if (gi < xa.M && gj < xa.N && (XI != XJ || gj - xj0 <= gi - xi0)) {
+            double* ptr = xa.C + (int64_t)gi * xa.ldc + gj;
+            *ptr = fma(xa.beta, *ptr, xa.alpha * xacc[r][q][e]);
+          }
+        }
+    return;
+  }
   const int ntn = (a.N + T - 1) / T;
   const int I = blockIdx.x / ntn, J = blockIdx.x - I * ntn;
   if (I < J) return;
@@ -401,7 +430,8 @@ static hipError_t dgemm_launch_t(const DgemmArgs& a, bool ta, bool tb, int batch
   int tiles;
   if (a.tri_tiles) {
     const int nt = (a.M + T - 1) / T;
-    tiles = nt * (nt + 1) / 2;
+    tiles = nt * (nt + 1) / 2 - a.tile_first;
+    if (tiles <= 0) return hipSuccess;
   } else {
     tiles = ((a.M + T - 1) / T) * ((a.N + T - 1) / T);
   }
@@ -420,11 +450,14 @@ hipError_t dgemm_launch(const DgemmArgs& a, bool ta, bool tb, int batches, hipSt
   return dgemm_launch_t<64>(a, ta, tb, batches, stream);
 }
 
-hipError_t colstep_launch(const DgemmArgs& a, hipStream_t stream) {
+hipError_t colstep_launch(const DgemmArgs& a, const DgemmArgs* x, int x_first, int x_count, hipStream_t stream) {
   if (a.M <= 0 || a.N <= 0 || a.N > a.M || a.K < 0 || !a.diag_Lstage || !a.diag_Dinv || !a.diag_status)
     return hipErrorInvalidValue;
   const int tiles = ((a.M + 63) / 64) * ((a.N + 63) / 64);
-  k_colstep<64><<<dim3(tiles), dim3(256), 0, stream>>>(a);
+  DgemmArgs none{};
+  if (!x || x_count < 0) x_count = 0;
+  if (x_count > 0 && (x->M != x->N || x->kmode != KMODE_FULL)) return hipErrorInvalidValue;
+  k_colstep<64><<<dim3(tiles + x_count), dim3(256), 0, stream>>>(a, x_count > 0 ? *x : none, x_first, tiles);
   return hipGetLastError();
 }
 

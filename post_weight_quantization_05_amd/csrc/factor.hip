@@ -193,18 +193,27 @@ __global__ __launch_bounds__(256) void k_reverse_to_upper(const double* __restri
 // Blocked right-looking Cholesky in two levels. Inside an outer block column of NBO columns, each
 // 64-column step is one launch (k_colstep): the outer block's remaining columns get the previous
 // panel's update (K = 64), the next diagonal block is factored and inverted, and the next panel is
-// solved against it. After the outer block, one product with K = NBO updates the whole trailing
-// matrix. The factors of the diagonal blocks are staged in Lst and copied into A at the end (A's
+// solved against it. After the outer block, products with K = NBO update the trailing matrix: the next
+// outer block's columns at once, the rest inside the next outer block's steps. The factors of the diagonal blocks are staged in Lst and copied into A at the end (A's
 // diagonal block is read by several workgroups of the launch that factors it).
 #ifndef GPTQ_FACTOR_NBO
 #define GPTQ_FACTOR_NBO 256
 #endif
 constexpr int NBO = GPTQ_FACTOR_NBO;  // outer block width (a multiple of 64)
+#ifndef GPTQ_FACTOR_DEFER
+#define GPTQ_FACTOR_DEFER 160
+#endif
+constexpr int DEFER_PER_STEP = GPTQ_FACTOR_DEFER;  // deferred trailing tiles per block-column step
 
 hipError_t potrf_lower(double* A, int d, double* Dinv, double* Lst, unsigned* status, hipStream_t stream) {
+  // The trailing update of an outer block is split in two: the next outer block's columns right away
+  // (its first step needs them), the rest (columns from the block after that on) deferred and spread over
+  // the next outer block's steps as extra workgroups. Per tile the arithmetic is unchanged.
+  DgemmArgs pend{};  // deferred part of the previous outer block's trailing update
+  int pend_tiles = 0, pend_done = 0;
   // one block-column step: update C = A[c1:, c1:c1 + n] with the panel A[c1:, o:o + k] (k = 0: no
-  // update), factor the diagonal block at (c1, c1), solve the panel below it
-  auto colstep = [&](int c1, int n, int o, int k) {
+  // update), factor the diagonal block at (c1, c1), solve the panel below it; plus `share` deferred tiles
+  auto colstep = [&](int c1, int n, int o, int k, int share) {
     DgemmArgs s{};
     const double* P = A + (int64_t)c1 * d + o;
     s.A = P; s.lda = d;
@@ -214,33 +223,68 @@ hipError_t potrf_lower(double* A, int d, double* Dinv, double* Lst, unsigned* st
     s.alpha = -1.0; s.beta = 1.0;
     s.kmode = KMODE_FULL;
     s.diag_kb = c1 / NB; s.diag_Lstage = Lst; s.diag_Dinv = Dinv; s.diag_status = status;
-    return colstep_launch(s, stream);
+    share = min(share, pend_tiles - pend_done);
+    const hipError_t e = colstep_launch(s, &pend, pend_done, share, stream);
+    pend_done += share;
+    return e;
   };
   hipError_t e;
   for (int b0 = 0; b0 < d; b0 += NBO) {
     const int b1 = min(d, b0 + NBO);
+    const int steps = (b1 - b0 + NB - 1) / NB;
+    // the deferred tiles are shared out evenly over this outer block's steps (all of them by its end)
+    int step = 0;
+    auto share = [&]() {
+      const int left = pend_tiles - pend_done, rem = steps - step++;
+      return (left + rem - 1) / rem;
+    };
     // first block of the outer block column: its diagonal block and panel, no update
-    e = colstep(b0, min(NB, d - b0), b0, 0);
+    e = colstep(b0, min(NB, d - b0), b0, 0, share());
     if (e != hipSuccess) return e;
     for (int o = b0; o + NB < b1; o += NB) {
       // the outer block's remaining columns get panel o; the next block is factored and its panel solved
       const int c1 = o + NB;
-      e = colstep(c1, b1 - c1, o, NB);
+      e = colstep(c1, b1 - c1, o, NB, share());
       if (e != hipSuccess) return e;
     }
+    pend_tiles = pend_done = 0;
     if (b1 < d) {
-      // trailing update with the whole outer panel: A22 -= Q Q^T, Q = A[b1:, b0:b1] (lower tiles)
+      // trailing update with the whole outer panel Q = A[b1:, b0:b1]: A22 -= Q Q^T (lower part)
+      const int b2 = min(d, b1 + NBO);
       const double* Q = A + (int64_t)b1 * d + b0;
-      DgemmArgs s{};
+      DgemmArgs s{};  // the next outer block's columns, now
       s.A = Q; s.lda = d;
       s.B = Q; s.ldb = d;
       s.C = A + (int64_t)b1 * d + b1; s.ldc = d;
-      s.M = d - b1; s.N = d - b1; s.K = b1 - b0;
+      s.M = d - b1; s.N = b2 - b1; s.K = b1 - b0;
       s.alpha = -1.0; s.beta = 1.0;
-      s.tri_tiles = 1;
+      s.lower_only = 1;
       s.kmode = KMODE_FULL;
       e = dgemm_launch(s, false, true, 1, stream);
       if (e != hipSuccess) return e;
+      if (b2 < d) {  // the rest, deferred
+        pend = DgemmArgs{};
+        const double* Q2 = A + (int64_t)b2 * d + b0;
+        pend.A = Q2; pend.lda = d;
+        pend.B = Q2; pend.ldb = d;
+        pend.C = A + (int64_t)b2 * d + b2; pend.ldc = d;
+        pend.M = d - b2; pend.N = d - b2; pend.K = b1 - b0;
+        pend.alpha = -1.0; pend.beta = 1.0;
+        pend.kmode = KMODE_FULL;
+        const int nt = (pend.M + NB - 1) / NB;
+        const int all = nt * (nt + 1) / 2;
+        // the next outer block's steps take as many as they can hide (about one tile per CU that a
+        // step leaves idle); the remaining tiles are launched now as a product of their own
+        const int next_steps = (b2 - b1 + NB - 1) / NB;
+        pend_tiles = min(all, next_steps * DEFER_PER_STEP);
+        if (pend_tiles < all) {
+          DgemmArgs r = pend;
+          r.tri_tiles = 1;
+          r.tile_first = pend_tiles;
+          e = dgemm_launch(r, false, true, 1, stream);
+          if (e != hipSuccess) return e;
+        }
+      }
     }
   }
   const int nblk = (d + NB - 1) / NB;
