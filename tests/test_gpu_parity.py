@@ -117,7 +117,9 @@ def test_prepare_matches_oracle(cfg, act, flags):
     assert np.linalg.norm(U.T @ U - Hinv) / np.linalg.norm(Hinv) <= 1e-10
 
 
-@pytest.mark.parametrize("d", [1, 2, 63, 64, 65, 129])
+# sizes around the 64-column steps, the 256-column outer blocks, and the first size whose trailing
+# updates are partly deferred into later steps (more than two outer blocks)
+@pytest.mark.parametrize("d", [1, 2, 63, 64, 65, 129, 255, 257, 320, 513, 577, 1000])
 def test_prepare_small_and_edge_sizes(d):
     rng = np.random.default_rng(d)
     X = rng.standard_normal((3 * d + 2, d)) @ (np.eye(d) + 0.2 * rng.standard_normal((d, d)))
