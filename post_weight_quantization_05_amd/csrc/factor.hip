@@ -100,29 +100,52 @@ __global__ __launch_bounds__(256) void k_perm(const double* __restrict__ colsq, 
 
 // A[a][b] (a >= b) = H[perm[x]][perm[y]] with (x, y) = (a, b), or (d-1-a, d-1-b) when reversed; the
 // strictly upper part of A is set to 0. H off-diagonal = (2/n) S[max][min]; diagonal = diag_h (dead
-// fixed, damped).
+// fixed, damped). One 64 x 64 tile of A per workgroup, staged through LDS: without act_order the source
+// of a tile is one 64 x 64 block of S, and threads walk along S's rows (along A's columns when A is in
+// S's order, along A's rows when reversed), so reads and writes are both coalesced.
 __global__ __launch_bounds__(256) void k_gather(const double* __restrict__ S, const double* __restrict__ diag_h,
                                                 const int32_t* __restrict__ perm, int64_t n_total, int d,
                                                 int reversed, double* __restrict__ A) {
-  const int nbx = (d + 255) / 256;
-  const int a = blockIdx.x / nbx;
-  const int b = (blockIdx.x - a * nbx) * 256 + threadIdx.x;
-  if (b >= d) return;
-  double v = 0.0;
-  if (b <= a) {
-    const int x = reversed ? d - 1 - a : a;
-    const int y = reversed ? d - 1 - b : b;
-    const int pi = min(max(perm[x], 0), d - 1);
-    const int pj = min(max(perm[y], 0), d - 1);
-    if (pi == pj) {
-      v = diag_h[pi];
-    } else {
-      const int hi = max(pi, pj), lo = min(pi, pj);
-      v = (2.0 / (double)n_total) * S[(int64_t)hi * d + lo];
+  __shared__ double t[64][65];
+  const int a0 = blockIdx.y * 64, b0 = blockIdx.x * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  const double s2n = 2.0 / (double)n_total;
+  auto value = [&](int a, int b) {
+    double v = 0.0;
+    if (a < d && b < d && b <= a) {
+      const int x = reversed ? d - 1 - a : a;
+      const int y = reversed ? d - 1 - b : b;
+      const int pi = min(max(perm[x], 0), d - 1);
+      const int pj = min(max(perm[y], 0), d - 1);
+      if (pi == pj) {
+        v = diag_h[pi];
+      } else {
+        const int hi = max(pi, pj), lo = min(pi, pj);
+        v = s2n * S[(int64_t)hi * d + lo];
+      }
     }
+    return v;
+  };
+  if (b0 > a0) {  // strictly upper tile
+    for (int aa = ty; aa < 64; aa += 4) {
+      const int a = a0 + aa, b = b0 + tx;
+      if (a < d && b < d) A[(int64_t)a * d + b] = 0.0;
+    }
+    return;
   }
-  A[(int64_t)a * d + b] = v;
+  if (reversed) {
+    // (a, b) reads S[d-1-b][d-1-a]: consecutive a are consecutive addresses
+    for (int bb = ty; bb < 64; bb += 4) t[bb][tx] = value(a0 + tx, b0 + bb);
+  } else {
+    for (int aa = ty; aa < 64; aa += 4) t[tx][aa] = value(a0 + aa, b0 + tx);
+  }
+  __syncthreads();
+  for (int aa = ty; aa < 64; aa += 4) {
+    const int a = a0 + aa, b = b0 + tx;
+    if (a < d && b < d) A[(int64_t)a * d + b] = t[tx][aa];
+  }
 }
+
 // Copy the staged factors of the diagonal blocks into the diagonal of A (lower part, zeros above).
 __global__ __launch_bounds__(256) void k_place_lblocks(const double* __restrict__ Lst, double* __restrict__ A,
                                                        int64_t lda, int d) {
@@ -369,7 +392,7 @@ hipError_t prepare_launch(const double* S, const double* colsq, int64_t n_total,
   GPTQ_TRY(hipGetLastError());
   hipLaunchKernelGGL(k_perm, dim3((unsigned)ceil_div(d, 256)), dim3(256), 0, stream, colsq, d, act_order, perm);
   GPTQ_TRY(hipGetLastError());
-  hipLaunchKernelGGL(k_gather, dim3((unsigned)(ceil_div(d, 256) * d)), dim3(256), 0, stream, S, diag_h, perm, n_total,
+  hipLaunchKernelGGL(k_gather, dim3((unsigned)ceil_div(d, 64), (unsigned)ceil_div(d, 64)), dim3(256), 0, stream, S, diag_h, perm, n_total,
                      d, reversed ? 1 : 0, A);
   GPTQ_TRY(hipGetLastError());
 

@@ -129,15 +129,34 @@ __global__ __launch_bounds__(256) void k_rowprep(const T* __restrict__ W, int64_
   const T* wr = W + (int64_t)r * ld_w;
   double* q = Wq + (int64_t)r * in;
   double mx = ASYM ? -INFINITY : 0.0, mn = INFINITY;
-  for (int j = threadIdx.x; j < in; j += 256) {
-    const int p = min(max(perm[j], 0), in - 1);
-    const double v = dead[p] ? 0.0 : to_f64<T>(wr[p]);
-    q[j] = v;
-    if (ASYM) {
-      mx = fmax(mx, v);
-      mn = fmin(mn, v);
-    } else {
-      mx = fmax(mx, fabs(v));
+  // eight columns per thread per pass: the index loads, then the gathered loads, all in flight together
+  constexpr int U8 = 8;
+  for (int j0 = threadIdx.x; j0 < in; j0 += 256 * U8) {
+    int p[U8];
+#pragma unroll
+    for (int u = 0; u < U8; ++u) {
+      const int j = j0 + 256 * u;
+      p[u] = (j < in) ? min(max(perm[j], 0), in - 1) : 0;
+    }
+    double v[U8];
+#pragma unroll
+    for (int u = 0; u < U8; ++u) {
+      const bool dd = dead[p[u]] != 0;
+      const double x = to_f64<T>(wr[p[u]]);
+      v[u] = dd ? 0.0 : x;
+    }
+#pragma unroll
+    for (int u = 0; u < U8; ++u) {
+      const int j = j0 + 256 * u;
+      if (j < in) {
+        q[j] = v[u];
+        if (ASYM) {
+          mx = fmax(mx, v[u]);
+          mn = fmin(mn, v[u]);
+        } else {
+          mx = fmax(mx, fabs(v[u]));
+        }
+      }
     }
   }
   red[threadIdx.x] = mx;
