@@ -50,11 +50,11 @@ struct Lds {
 // (zero outside M x N x K). 4 waves in 2 x 2, each (T/2) x (T/2). Operand chunks of T x 16 are fetched
 // as 16-byte vectors into registers while the MFMAs of earlier chunks run, then stored to the other LDS
 // buffer. Ends with a barrier, so the LDS buffers may be reused at once.
-template <bool TA, bool TB, int T>
+template <bool TA, bool TB, int T, bool BB = false>
 __device__ __forceinline__ void tile_product(const DgemmArgs& a, const double* A, const double* B, int M, int N,
                                              int K, int i0, int j0, int klo, int khi,
                                              double (*As)[Lds<T>::SZ], double (*Bs)[Lds<T>::SZ],
-                                             f64x4 (&acc)[T / 32][T / 32]) {
+                                             f64x4 (&acc)[T / 32][T / 32], f64x4 (*acc_bb)[T / 32] = nullptr) {
   constexpr int NV = T * TK / 2 / 256;   // 16-byte loads per thread per operand and chunk
   using L = Lds<T>;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -123,7 +123,10 @@ __device__ __forceinline__ void tile_product(const DgemmArgs& a, const double* A
 #pragma unroll
   for (int p = 0; p < FR; ++p)
 #pragma unroll
-    for (int q = 0; q < FC; ++q) acc[p][q] = f64x4{0.0, 0.0, 0.0, 0.0};
+    for (int q = 0; q < FC; ++q) {
+      acc[p][q] = f64x4{0.0, 0.0, 0.0, 0.0};
+      if constexpr (BB) acc_bb[p][q] = f64x4{0.0, 0.0, 0.0, 0.0};
+    }
 
   const int nk = (khi > klo) ? (khi - klo + TK - 1) / TK : 0;
   static_for_d<0, PD>([&](auto pc) {
@@ -158,6 +161,19 @@ __device__ __forceinline__ void tile_product(const DgemmArgs& a, const double* A
       for (int r = 0; r < FR; ++r)
 #pragma unroll
         for (int q = 0; q < FC; ++q) acc[r][q] = __builtin_amdgcn_mfma_f64_16x16x4f64(fa[r], fb[q], acc[r][q], 0, 0, 0);
+      if constexpr (BB) {
+        // acc_bb += B's tile rows times themselves transposed (B^T stored as [j][k]): the product of the
+        // tile at (j0, j0), from the operand already in LDS
+        static_assert(TB, "B^T operand");
+        double fbb[FR];
+#pragma unroll
+        for (int r = 0; r < FR; ++r) fbb[r] = Bs[st][(wm * (T / 2) + r * 16 + lc) * L::IK + kr];
+#pragma unroll
+        for (int r = 0; r < FR; ++r)
+#pragma unroll
+          for (int q = 0; q < FC; ++q)
+            acc_bb[r][q] = __builtin_amdgcn_mfma_f64_16x16x4f64(fbb[r], fb[q], acc_bb[r][q], 0, 0, 0);
+      }
     }
     if (kt + 1 < nk) lstore(std::integral_constant<int, (p + 1) % PD>{}, st ^ 1);
     __syncthreads();
@@ -330,7 +346,9 @@ __global__ __launch_bounds__(256) void k_colstep(DgemmArgs a, DgemmArgs xa, int 
         }
   }
   f64x4 acc[FR][FC];
-  tile_product<false, true, T>(a, A, B, M, N, K, i0, j0, 0, K, As, Bs, acc);
+  f64x4 dacc[FR][FC];  // column 0 below the diagonal: the diagonal block's product, from the same B
+  if (J == 0 && I > 0) tile_product<false, true, T, true>(a, A, B, M, N, K, i0, j0, 0, K, As, Bs, acc, dacc);
+  else tile_product<false, true, T>(a, A, B, M, N, K, i0, j0, 0, K, As, Bs, acc);
 
   if (J != 0) {
     const bool diag_tile = (I == J);
@@ -381,8 +399,6 @@ __global__ __launch_bounds__(256) void k_colstep(DgemmArgs a, DgemmArgs xa, int 
         const int gi = i0 + ti(r, e), gj = tj(q);
         x[r][q][e] = (gi < M && gj < m) ? fma(a.beta, cown[r][q][e], a.alpha * acc[r][q][e]) : 0.0;
       }
-  f64x4 dacc[FR][FC];
-  tile_product<false, true, T>(a, A, B, M, N, K, 0, 0, 0, K, As, Bs, dacc);
   stage_diag(dacc);
   __syncthreads();
   diagblock::diag_factor(dsm, m, nullptr, 0, nullptr, nullptr, true);  // L^-1 now in dsm.Ls
