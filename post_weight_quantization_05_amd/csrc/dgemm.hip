@@ -268,8 +268,8 @@ __global__ __launch_bounds__(256) void k_dgemm(DgemmArgs a) {
 //  * tile (0, 0): the updated diagonal block D is factored; L goes to diag_Lstage[kb], L^-1 to
 //    diag_Dinv[kb], bad pivots to diag_status. The block in C itself is not written in this launch;
 //  * tiles (I >= 1, 0): the updated tile X and, again, D from the same inputs (so every one of these
-//    workgroups gets the same L^-1 as tile (0, 0) without waiting for it); X is then solved,
-//    X L^-T = X (L^-1)^T, and written in place: the panel of the next step.
+//    workgroups gets the same factor as tile (0, 0) without waiting for it); X is then solved,
+//    X L^T = X by forward substitution, and written in place: the panel of the next step.
 // With K = 0 the update is empty and the launch only factors the block and solves the panel.
 template <int T>
 __global__ __launch_bounds__(256) void k_colstep(DgemmArgs a, DgemmArgs xa, int x_first, int n_own) {
@@ -385,7 +385,7 @@ __global__ __launch_bounds__(256) void k_colstep(DgemmArgs a, DgemmArgs xa, int 
     stage_diag(acc);
     __syncthreads();
     diagblock::diag_factor(dsm, m, a.diag_Lstage + (int64_t)a.diag_kb * T * T, T,
-                           a.diag_Dinv + (int64_t)a.diag_kb * T * T, a.diag_status, false);
+                           a.diag_Dinv + (int64_t)a.diag_kb * T * T, a.diag_status);
     return;
   }
   // this tile, updated (kept in registers through the factorization)
@@ -399,10 +399,8 @@ __global__ __launch_bounds__(256) void k_colstep(DgemmArgs a, DgemmArgs xa, int 
         const int gi = i0 + ti(r, e), gj = tj(q);
         x[r][q][e] = (gi < M && gj < m) ? fma(a.beta, cown[r][q][e], a.alpha * acc[r][q][e]) : 0.0;
       }
-  stage_diag(dacc);
-  __syncthreads();
-  diagblock::diag_factor(dsm, m, nullptr, 0, nullptr, nullptr, true);  // L^-1 now in dsm.Ls
-  // X into LDS (row-major, stride T + 1), then X (L^-1)^T on the matrix cores
+  // X into LDS (row-major, stride T + 1) and the diagonal block staged; the factorization then solves
+  // X L^T = X in place of forming L^-1 (a forward substitution per row of X) and writes the panel tile
   double(*Xs)[T + 1] = reinterpret_cast<double(*)[T + 1]>(ABs);
 #pragma unroll
   for (int r = 0; r < FR; ++r)
@@ -410,33 +408,10 @@ __global__ __launch_bounds__(256) void k_colstep(DgemmArgs a, DgemmArgs xa, int 
     for (int q = 0; q < FC; ++q)
 #pragma unroll
       for (int e = 0; e < 4; ++e) Xs[ti(r, e)][tj(q)] = x[r][q][e];
+  stage_diag(dacc);
   __syncthreads();
-#pragma unroll
-  for (int r = 0; r < FR; ++r)
-#pragma unroll
-    for (int q = 0; q < FC; ++q) acc[r][q] = f64x4{0.0, 0.0, 0.0, 0.0};
-#pragma unroll 4
-  for (int k4 = 0; k4 < T; k4 += 4) {
-    const int kr = k4 + lk;
-    double fa[FR], fb[FC];
-#pragma unroll
-    for (int r = 0; r < FR; ++r) fa[r] = Xs[wm * (T / 2) + r * 16 + lc][kr];
-#pragma unroll
-    for (int q = 0; q < FC; ++q) fb[q] = dsm.Ls[wn * (T / 2) + q * 16 + lc][kr];  // (L^-1)^T[k][j]
-#pragma unroll
-    for (int r = 0; r < FR; ++r)
-#pragma unroll
-      for (int q = 0; q < FC; ++q) acc[r][q] = __builtin_amdgcn_mfma_f64_16x16x4f64(fa[r], fb[q], acc[r][q], 0, 0, 0);
-  }
-#pragma unroll
-  for (int r = 0; r < FR; ++r)
-#pragma unroll
-    for (int q = 0; q < FC; ++q)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int gi = i0 + ti(r, e), gj = tj(q);
-        if (gi < M && gj < m) C[(int64_t)gi * a.ldc + gj] = acc[r][q][e];
-      }
+  diagblock::diag_factor(dsm, m, nullptr, 0, nullptr, nullptr, &Xs[0][0], C + (int64_t)i0 * a.ldc, a.ldc,
+                         min(T, M - i0));
 }
 
 }  // namespace

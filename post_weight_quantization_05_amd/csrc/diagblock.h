@@ -52,7 +52,8 @@ __device__ __forceinline__ double quad_bcast(double v) {
 
 // Factorization of one diagonal block staged in LDS (lower part; rows/columns past the matrix edge as
 // the identity): its Cholesky factor L and L^-1. 256 threads. Outputs are optional: L to global memory,
-// L^-1 to global memory, the status bits, and L^-1 left in LDS for a caller that solves with it.
+// L^-1 to global memory, the status bits; or, instead of L^-1, the solution X of X L^T = T for a 64-row
+// tile T staged in LDS.
 //  Cholesky (wave 0): lane i holds row i in registers and eliminates right-looking. Pivot k is
 //  r_k[k]; 1/L[k][k] comes from rsqrt_refined, so no square root or division sits on the chain. After
 //  scaling column k, every lane updates its entries j > k with column k, which goes through LDS. The
@@ -77,9 +78,13 @@ struct DiagSmem {
 //   Lout (nullable): L written to Lout[i * ldo + j] for i, j < m, zeros above the diagonal;
 //   Dout (nullable): L^-1 as a row-major 64 x 64 block, the identity past the edge;
 //   status (nullable): flags of bad pivots;
-//   inv_to_ls: on return (after a barrier), sm.Ls[i][j] holds L^-1[i][j] (zeros above the diagonal).
+//   rhs (nullable, LDS, 64 rows of stride NB + 1): instead of L^-1, the substitution solves
+//   X L^T = rhs (each row x of X from L x^T = row^T), and row i < xrows, column j < m of X goes to
+//   Xout[i * ldx + j]. Dout must then be null.
 __device__ __forceinline__ void diag_factor(DiagSmem& sm, int m, double* __restrict__ Lout, int64_t ldo,
-                                            double* __restrict__ Dout, unsigned* status, bool inv_to_ls) {
+                                            double* __restrict__ Dout, unsigned* status,
+                                            const double* rhs = nullptr, double* Xout = nullptr, int64_t ldx = 0,
+                                            int xrows = 0) {
   auto& Ls = sm.Ls;
   auto& Lc = sm.Lc;
   auto& col = sm.col;
@@ -174,11 +179,17 @@ __device__ __forceinline__ void diag_factor(DiagSmem& sm, int m, double* __restr
       if (i < m && j < m) Lout[(int64_t)i * ldo + j] = v[t];
     }
   }
-  // inverse: lane 4j + r holds c[q] = (L^-1)[4q + r][j], starting from e_j
+  // inverse: lane 4j + r holds c[q] = (L^-1)[4q + r][j], starting from e_j (or, with rhs, the solution
+  // of L x = (row j of rhs)^T, starting from that row)
   const int jc = tw >> 2, rr = tw & 3;
   double c[16];
+  if (rhs) {
 #pragma unroll
-  for (int q = 0; q < 16; ++q) c[q] = (4 * q + rr == jc) ? 1.0 : 0.0;
+    for (int q = 0; q < 16; ++q) c[q] = rhs[jc * (NB + 1) + 4 * q + rr];
+  } else {
+#pragma unroll
+    for (int q = 0; q < 16; ++q) c[q] = (4 * q + rr == jc) ? 1.0 : 0.0;
+  }
   // column k of L and 1/L[k][k] are read one step ahead, so their LDS latency is off the chain
   double lcur[16], lnext[16];
   double dcur = rdg[0], dnext = 0.0;
@@ -213,14 +224,12 @@ __device__ __forceinline__ void diag_factor(DiagSmem& sm, int m, double* __restr
       Dout[row * NB + jc] = (row < m && jc < m) ? c[q] : ((row == jc) ? 1.0 : 0.0);
     }
   }
-  if (inv_to_ls) {
-    __syncthreads();  // every thread is past its reads of Ls (the L store above)
+  if (rhs && jc < xrows) {
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
-      const int row = 4 * q + rr;
-      Ls[row][jc] = (row < m && jc < m) ? c[q] : ((row == jc) ? 1.0 : 0.0);
+      const int col = 4 * q + rr;
+      if (col < m) Xout[(int64_t)jc * ldx + col] = c[q];
     }
-    __syncthreads();
   }
 }
 
