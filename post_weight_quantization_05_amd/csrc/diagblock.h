@@ -190,17 +190,19 @@ __device__ __forceinline__ void diag_factor(DiagSmem& sm, int m, double* __restr
 #pragma unroll
     for (int q = 0; q < 16; ++q) c[q] = (4 * q + rr == jc) ? 1.0 : 0.0;
   }
-  // column k of L and 1/L[k][k] are read one step ahead, so their LDS latency is off the chain
+  // column k of L and 1/L[k][k] are read one step ahead, so their LDS latency is off the chain. Every
+  // read goes through one per-lane base (Lc[0][rr]) with a constant offset.
+  const double* lb = &Lc[0][rr][0];
   double lcur[16], lnext[16];
   double dcur = rdg[0], dnext = 0.0;
 #pragma unroll
-  for (int q = 0; q < 16; ++q) lcur[q] = Lc[0][rr][q];
+  for (int q = 0; q < 16; ++q) lcur[q] = lb[q];
   static_for<0, NB>([&](auto kc) {
     constexpr int k = decltype(kc)::value;
     constexpr int mk = k >> 2, rk = k & 3;
     if constexpr (k + 1 < NB) {
 #pragma unroll
-      for (int q = (k + 1) >> 2; q < 16; ++q) lnext[q] = Lc[k + 1][rr][q];
+      for (int q = (k + 1) >> 2; q < 16; ++q) lnext[q] = lb[(k + 1) * 4 * LC_STRIDE + q];
       dnext = rdg[k + 1];
     }
     const double own = c[mk] * dcur;
