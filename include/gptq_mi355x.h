@@ -40,7 +40,7 @@ typedef enum {
   GPTQ_OK = 0,
   GPTQ_ERR_INVALID_ARG = -1, /* bad size, pointer, dtype, bits, damp or leading dimension */
   GPTQ_ERR_UNSUPPORTED = -2, /* valid request this library does not implement (group size, see below) */
-  GPTQ_ERR_NOT_SPD = -3,     /* the damped Hessian has no Cholesky factor (a pivot <= 0) */
+  GPTQ_ERR_NOT_SPD = -3,     /* the damped Hessian has no Cholesky factor (a pivot below 2^-1000) */
   GPTQ_ERR_NONFINITE = -4,   /* NaN or Inf met in S, colsq or during the factorization */
   GPTQ_ERR_WORKSPACE = -5,   /* ws is NULL or ws_bytes is below the size query's value */
   GPTQ_ERR_HIP = -6          /* a HIP runtime call or kernel launch failed */
@@ -98,7 +98,8 @@ int gptq_hessian_accumulate(const void* X, int x_dtype, int64_t n_rows, int64_t 
  *  flags      GPTQ_FACTOR_INVERSE_RECHOL or GPTQ_FACTOR_REVERSED.
  *  ws         at least gptq_prepare_workspace_bytes(in) bytes.
  *  Synchronises `stream` once. Errors: INVALID_ARG (in < 1, n_total < 1, damp < 0 or not finite, NULL
- *  pointer, unknown flags), WORKSPACE, NOT_SPD (a pivot <= 0, e.g. damp = 0 with a rank-deficient X),
+ *  pointer, unknown flags), WORKSPACE, NOT_SPD (a Cholesky pivot below 2^-1000, in particular <= 0, e.g.
+ *  damp = 0 with a rank-deficient X),
  *  NONFINITE (NaN/Inf in S or colsq, or met in a pivot), HIP. On NOT_SPD/NONFINITE, U is unspecified.
  * ------------------------------------------------------------------------------------------------- */
 size_t gptq_prepare_workspace_bytes(int64_t in);
