@@ -261,6 +261,79 @@ __global__ __launch_bounds__(256) void k_dgemm(DgemmArgs a) {
       }
 }
 
+// Single-shot form of tile_product for the block-column step (A B^T, T = 64, K = 64): all operand loads
+// in flight at once, one LDS store, one barrier, then the whole K, unrolled, on the matrix cores. The
+// operands sit in LDS as [row][k] with rows of 68 doubles (a 16 x 4 fragment read touches each bank pair
+// twice). With BB, acc_bb also receives the (j0, j0) tile from B alone, as in tile_product. Ends with a
+// barrier.
+constexpr int K64S = 68;
+template <bool BB>
+__device__ __forceinline__ void tile_product_k64(const double* A, const double* B, int64_t lda, int64_t ldb, int M,
+                                                 int N, int i0, int j0, double* As, double* Bs,
+                                                 f64x4 (&acc)[2][2], f64x4 (*acc_bb)[2] = nullptr) {
+  constexpr int T = 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int lk = lane >> 4, lc = lane & 15;
+  const bool a_vec = ((lda & 1) == 0) && ((reinterpret_cast<uintptr_t>(A) & 15) == 0);
+  const bool b_vec = ((ldb & 1) == 0) && ((reinterpret_cast<uintptr_t>(B) & 15) == 0);
+  auto ld2 = [&](const double* P, int64_t ld, int r, int rlim, int c2, bool vec) {
+    double2 v = make_double2(0.0, 0.0);
+    if (r < rlim) {
+      const double* q = P + (int64_t)r * ld + c2;
+      if (vec) {
+        v = *reinterpret_cast<const double2*>(q);
+      } else {
+        v.x = q[0];
+        v.y = q[1];
+      }
+    }
+    return v;
+  };
+  double2 ra[8], rb[8];
+#pragma unroll
+  for (int v = 0; v < 8; ++v) {
+    const int e = tid + 256 * v, r = e >> 5, c2 = (e & 31) * 2;
+    ra[v] = ld2(A, lda, i0 + r, M, c2, a_vec);
+    rb[v] = ld2(B, ldb, j0 + r, N, c2, b_vec);
+  }
+#pragma unroll
+  for (int p = 0; p < 2; ++p)
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      acc[p][q] = f64x4{0.0, 0.0, 0.0, 0.0};
+      if constexpr (BB) acc_bb[p][q] = f64x4{0.0, 0.0, 0.0, 0.0};
+    }
+#pragma unroll
+  for (int v = 0; v < 8; ++v) {
+    const int e = tid + 256 * v, r = e >> 5, c2 = (e & 31) * 2;
+    *reinterpret_cast<double2*>(&As[r * K64S + c2]) = ra[v];
+    *reinterpret_cast<double2*>(&Bs[r * K64S + c2]) = rb[v];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k4 = 0; k4 < T; k4 += 4) {
+    const int kr = k4 + lk;
+    double fa[2], fb[2], fbb[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) fa[r] = As[(wm * (T / 2) + r * 16 + lc) * K64S + kr];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) fb[q] = Bs[(wn * (T / 2) + q * 16 + lc) * K64S + kr];
+    if constexpr (BB) {
+#pragma unroll
+      for (int r = 0; r < 2; ++r) fbb[r] = Bs[(wm * (T / 2) + r * 16 + lc) * K64S + kr];
+    }
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        acc[r][q] = __builtin_amdgcn_mfma_f64_16x16x4f64(fa[r], fb[q], acc[r][q], 0, 0, 0);
+        if constexpr (BB) acc_bb[r][q] = __builtin_amdgcn_mfma_f64_16x16x4f64(fbb[r], fb[q], acc_bb[r][q], 0, 0, 0);
+      }
+  }
+  __syncthreads();
+}
+
 // Block-column step of the factorization (T = 64, C = A B^T update with beta = 1, kmode FULL). C is the
 // region A[c1:, c1:c1 + N] of the matrix being factored, M x N with M >= N; its tile (0, 0) is the next
 // 64 x 64 diagonal block and its column-0 tiles below are the next panel. Workgroup roles:
@@ -275,9 +348,12 @@ template <int T>
 __global__ __launch_bounds__(256) void k_colstep(DgemmArgs a, DgemmArgs xa, int x_first, int n_own) {
   static_assert(T == diagblock::NB, "the diagonal block is one tile");
   using L = Lds<T>;
-  __shared__ __attribute__((aligned(16))) double ABs[4 * L::SZ];  // operands; later the tile X
+  // operands (2 x 64 rows of K64S for the step's own K = 64 product, or the ring of tile_product for
+  // other K and for deferred tiles); later the tile X
+  constexpr int AB_SZ = (2 * T * K64S > 4 * L::SZ) ? 2 * T * K64S : 4 * L::SZ;
+  __shared__ __attribute__((aligned(16))) double ABs[AB_SZ];
   __shared__ diagblock::DiagSmem dsm;
-  static_assert(4 * L::SZ >= T * (T + 1), "tile buffer");
+  static_assert(AB_SZ >= T * (T + 1), "tile buffer");
   double(*As)[L::SZ] = reinterpret_cast<double(*)[L::SZ]>(ABs);
   double(*Bs)[L::SZ] = reinterpret_cast<double(*)[L::SZ]>(ABs + 2 * L::SZ);
 
@@ -347,8 +423,14 @@ __global__ __launch_bounds__(256) void k_colstep(DgemmArgs a, DgemmArgs xa, int 
   }
   f64x4 acc[FR][FC];
   f64x4 dacc[FR][FC];  // column 0 below the diagonal: the diagonal block's product, from the same B
-  if (J == 0 && I > 0) tile_product<false, true, T, true>(a, A, B, M, N, K, i0, j0, 0, K, As, Bs, acc, dacc);
-  else tile_product<false, true, T>(a, A, B, M, N, K, i0, j0, 0, K, As, Bs, acc);
+  if (K == T) {
+    if (J == 0 && I > 0) tile_product_k64<true>(A, B, a.lda, a.ldb, M, N, i0, j0, ABs, ABs + T * K64S, acc, dacc);
+    else tile_product_k64<false>(A, B, a.lda, a.ldb, M, N, i0, j0, ABs, ABs + T * K64S, acc);
+  } else if (J == 0 && I > 0) {
+    tile_product<false, true, T, true>(a, A, B, M, N, K, i0, j0, 0, K, As, Bs, acc, dacc);
+  } else {
+    tile_product<false, true, T>(a, A, B, M, N, K, i0, j0, 0, K, As, Bs, acc);
+  }
 
   if (J != 0) {
     const bool diag_tile = (I == J);
