@@ -66,12 +66,14 @@ typedef enum { GPTQ_F32 = 0, GPTQ_BF16 = 1 } gptq_dtype;
  *           Rows may start at any element offset; 16-byte aligned rows (ld_x*elem % 16 == 0 and X 16-byte
  *           aligned) take the fast load path.
  *  S        in x in fp64. Only the lower triangle (i >= j) is read and written: S[i][j] += sum_k
- *           X[k][i] X[k][j]. The caller zero-initialises S before the first chunk. The products of bf16
+ *           X[k][i] X[k][j]. The first chunk (*n_total == 0 on entry) writes S[i][j] = sum_k X[k][i]
+ *           X[k][j] instead, so S needs no zeroing; later chunks add to it. The products of bf16
  *           or fp32 inputs are formed on the matrix cores and summed in fp32 within a slice of rows;
  *           slices are summed in fp64 in a fixed order, so results are bitwise reproducible.
  *  colsq    fp64[in]: colsq[i] += sum_k X[k][i]^2, summed in fp64 (the act_order key and the exact
- *           dead-input test need it exact up to fp64 rounding). Caller zero-initialises.
- *  n_total  HOST pointer; incremented by n_rows when the call is accepted.
+ *           dead-input test need it exact up to fp64 rounding); written, not added, on the first chunk.
+ *  n_total  HOST pointer; rows accumulated so far (0 before the first chunk); incremented by n_rows
+ *           when the call is accepted.
  *  ws       workspace of at least gptq_hessian_workspace_bytes(n_rows, in, x_dtype) bytes.
  *  Errors   INVALID_ARG (n_rows < 1, in < 1, ld_x < in, unknown dtype, NULL pointer), WORKSPACE, HIP.
  * ------------------------------------------------------------------------------------------------- */

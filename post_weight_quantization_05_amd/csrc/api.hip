@@ -49,7 +49,8 @@ int gptq_hessian_accumulate(const void* X, int x_dtype, int64_t n_rows, int64_t 
   HessianPlan p = hessian_plan(n_rows, in, x_dtype);
   p.ld = ld_x;
   if (!ws || ws_bytes < p.total_bytes) return GPTQ_ERR_WORKSPACE;
-  const int st = hip_status(hessian_launch(p, X, S, colsq, ws, reinterpret_cast<hipStream_t>(stream)));
+  const int st =
+      hip_status(hessian_launch(p, X, S, colsq, ws, reinterpret_cast<hipStream_t>(stream), *n_total == 0));
   if (st == GPTQ_OK) *n_total += n_rows;
   return st;
 }

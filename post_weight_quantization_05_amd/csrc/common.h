@@ -39,8 +39,9 @@ struct HessianPlan {
   size_t part_bytes, colsq_part_bytes, total_bytes;
 };
 HessianPlan hessian_plan(int64_t n_rows, int64_t in, int dtype);
+// first: S's lower triangle and colsq are written (not added to): the first chunk of a stream
 hipError_t hessian_launch(const HessianPlan& p, const void* X, double* S, double* colsq, void* ws,
-                          hipStream_t stream);
+                          hipStream_t stream, bool first);
 
 // Prepare + factorization (factor.hip)
 size_t prepare_ws_bytes(int64_t in);

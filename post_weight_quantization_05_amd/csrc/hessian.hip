@@ -124,7 +124,7 @@ template <int TILE>
 __global__ __launch_bounds__(256) void k_xtx_reduce(const float* __restrict__ part,
                                                     const double* __restrict__ colsq_part, int colsq_stride,
                                                     int n_tiles, int splits, int d, double* __restrict__ S,
-                                                    double* __restrict__ colsq) {
+                                                    double* __restrict__ colsq, int first) {
   constexpr int Q = TILE / 4;                 // 4-column groups per tile row
   constexpr int NCH = TILE / FIN_RC;          // row chunks per tile
   constexpr int FIN_G = FIN_RC * Q / 256;     // groups per thread
@@ -178,7 +178,7 @@ __global__ __launch_bounds__(256) void k_xtx_reduce(const float* __restrict__ pa
 #pragma unroll
   for (int k = 0; k < FIN_G; ++k)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) old[k][c] = S[(int64_t)min(gi[k], d - 1) * d + min(gj[k] + c, d - 1)];
+    for (int c = 0; c < 4; ++c) old[k][c] = first ? 0.0 : S[(int64_t)min(gi[k], d - 1) * d + min(gj[k] + c, d - 1)];
 #pragma unroll
   for (int k = 0; k < FIN_G; ++k)
 #pragma unroll
@@ -199,7 +199,7 @@ __global__ __launch_bounds__(256) void k_xtx_reduce(const float* __restrict__ pa
 #pragma unroll
         for (int u = 0; u < FIN_SB; ++u) sum += w[u];
       }
-      colsq[gc] += sum;
+      colsq[gc] = first ? sum : colsq[gc] + sum;
     }
   }
 }
@@ -808,7 +808,7 @@ HessianPlan hessian_plan(int64_t n_rows, int64_t in, int dtype) {
 }
 
 hipError_t hessian_launch(const HessianPlan& p, const void* X, double* S, double* colsq, void* ws,
-                          hipStream_t stream) {
+                          hipStream_t stream, bool first) {
   float* part = reinterpret_cast<float*>(ws);
   double* cpart = reinterpret_cast<double*>(reinterpret_cast<char*>(ws) + p.part_bytes);
   const int grid = p.splits * p.n_tiles;
@@ -831,14 +831,14 @@ hipError_t hessian_launch(const HessianPlan& p, const void* X, double* S, double
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_xtx_reduce<BT>, dim3((unsigned)(p.n_tiles * (BT / FIN_RC))), dim3(256), 0, stream, part,
-                       cpart, cstride, p.n_tiles, p.splits, (int)p.in, S, colsq);
+                       cpart, cstride, p.n_tiles, p.splits, (int)p.in, S, colsq, first ? 1 : 0);
   } else {
     hipLaunchKernelGGL(k_xtx_f32, dim3(grid), dim3(256), 0, stream, (const float*)X, p.ld, p.n_rows, (int)p.in,
                        p.n_tiles, p.rows_per_split, remap, p.splits, part, cpart, cstride);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_xtx_reduce<FT>, dim3((unsigned)(p.n_tiles * (FT / FIN_RC))), dim3(256), 0, stream, part,
-                       cpart, cstride, p.n_tiles, p.splits, (int)p.in, S, colsq);
+                       cpart, cstride, p.n_tiles, p.splits, (int)p.in, S, colsq, first ? 1 : 0);
   }
   return hipGetLastError();
 }

@@ -85,6 +85,26 @@ def test_hessian_streaming_determinism_and_strided_rows():
     assert np.linalg.norm((S2 - S_ref)[low]) / np.linalg.norm(S_ref[low]) <= 1e-6
 
 
+def test_hessian_first_chunk_overwrites():
+    """With n_total == 0 the call writes S's lower triangle and colsq (no zeroing needed); later chunks add."""
+    cfg = HESS_CASES[2]
+    W, X, W64, X64 = layer_inputs(cfg)
+    Xd = to_device(X, cfg.dtype)
+    ref = G.HessianState(cfg.d_in)
+    G.hessian_accumulate(Xd[:700], ref)
+    G.hessian_accumulate(Xd[700:], ref)
+    st = G.HessianState(cfg.d_in)
+    st.S.fill_(float("nan"))  # stale contents, upper triangle included
+    st.colsq.fill_(-1.0)
+    G.hessian_accumulate(Xd[:700], st)
+    G.hessian_accumulate(Xd[700:], st)
+    torch.cuda.synchronize()
+    low = torch.tril(torch.ones_like(ref.S, dtype=torch.bool))
+    assert torch.equal(st.S[low], ref.S[low])  # bitwise: same sums in the same order
+    assert torch.equal(st.colsq, ref.colsq)
+    assert st.n_total == ref.n_total == cfg.n
+
+
 def _oracle_prep(cfg, act_order, damp=0.01):
     W, X, W64, X64 = layer_inputs(cfg)
     S, colsq, n = O.hessian_from_x(X64)
