@@ -228,7 +228,10 @@ constexpr int NBO = GPTQ_FACTOR_NBO;  // outer block width (a multiple of 64)
 #endif
 constexpr int DEFER_PER_STEP = GPTQ_FACTOR_DEFER;  // deferred trailing tiles per block-column step
 
-hipError_t potrf_lower(double* A, int d, double* Dinv, double* Lst, unsigned* status, hipStream_t stream) {
+// place_l: copy the diagonal blocks' factors into A at the end (not needed when the caller next replaces
+// those blocks with their inverses, as the triangular inverse does)
+hipError_t potrf_lower(double* A, int d, double* Dinv, double* Lst, unsigned* status, bool place_l,
+                       hipStream_t stream) {
   // The trailing update of an outer block is split in two: the next outer block's columns right away
   // (its first step needs them), the rest (columns from the block after that on) deferred and spread over
   // the next outer block's steps as extra workgroups. Per tile the arithmetic is unchanged.
@@ -310,6 +313,7 @@ hipError_t potrf_lower(double* A, int d, double* Dinv, double* Lst, unsigned* st
       }
     }
   }
+  if (!place_l) return hipSuccess;
   const int nblk = (d + NB - 1) / NB;
   hipLaunchKernelGGL(k_place_lblocks, dim3(nblk), dim3(256), 0, stream, Lst, A, (int64_t)d, d);
   return hipGetLastError();
@@ -396,7 +400,7 @@ hipError_t prepare_launch(const double* S, const double* colsq, int64_t n_total,
                      d, reversed ? 1 : 0, A);
   GPTQ_TRY(hipGetLastError());
 
-  GPTQ_TRY(potrf_lower(A, d, Dinv, Lst, status, stream));
+  GPTQ_TRY(potrf_lower(A, d, Dinv, Lst, status, false, stream));  // k_place_dinv follows
   hipLaunchKernelGGL(k_place_dinv, dim3((unsigned)nblk), dim3(256), 0, stream, Dinv, A, (int64_t)d, d);
   GPTQ_TRY(hipGetLastError());
   GPTQ_TRY(trtri_lower(A, d, U /* scratch */, stream));
@@ -414,7 +418,7 @@ hipError_t prepare_launch(const double* S, const double* colsq, int64_t n_total,
     g.tri_tiles = 1;
     g.kmode = KMODE_GE_I;
     GPTQ_TRY(dgemm_launch(g, true, false, 1, stream));
-    GPTQ_TRY(potrf_lower(U, d, Dinv, Lst, status, stream));
+    GPTQ_TRY(potrf_lower(U, d, Dinv, Lst, status, true, stream));
     const int nt = (d + 31) / 32;
     hipLaunchKernelGGL(k_transpose_lower_to_upper, dim3(nt * (nt + 1) / 2), dim3(256), 0, stream, U, d);
     GPTQ_TRY(hipGetLastError());
