@@ -4,6 +4,7 @@ python -m post_weight_quantization_05_amd.profsum stats <dir>          per-kerne
 python -m post_weight_quantization_05_amd.profsum counters <dir> [substr]  per-dispatch counter sums
 python -m post_weight_quantization_05_amd.profsum bykernel <dir> [from]   per-kernel counter means
 python -m post_weight_quantization_05_amd.profsum durations <dir> [from]  per-kernel mean durations (trace)
+python -m post_weight_quantization_05_amd.profsum clock <dir>             per-kernel clock and MFMA busy share
   [from]: only the dispatches from the first one whose kernel name contains this text (a stage's kernels)
 """
 from __future__ import annotations
@@ -92,11 +93,46 @@ def durations(d: str, start: str = "") -> str:
     return "\n".join(out)
 
 
+def clock(d: str, xcds: int = 8, simds: int = 1024) -> str:
+    """Mean clock and MFMA-busy share per kernel, from a run with GRBM_GUI_ACTIVE and SQ_VALU_MFMA_BUSY_CYCLES.
+
+    The collection CSV holds GRBM_GUI_ACTIVE summed over the XCDs, so one XCD's active cycles are the value
+    over xcds; over the dispatch's duration that is the mean clock. The busy share is the MFMA-busy cycles
+    summed over SIMDs over (active cycles x SIMDs). Short dispatches read high: the counters also see a few
+    microseconds around the dispatch.
+    """
+    f = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)[0]
+    gui, busy, dur, kern = {}, {}, {}, {}
+    for r in csv.DictReader(open(f)):
+        disp = int(r["Dispatch_Id"])
+        if r["Counter_Name"] == "GRBM_GUI_ACTIVE":
+            gui[disp] = gui.get(disp, 0.0) + float(r["Counter_Value"])
+        elif r["Counter_Name"] == "SQ_VALU_MFMA_BUSY_CYCLES":
+            busy[disp] = busy.get(disp, 0.0) + float(r["Counter_Value"])
+        dur[disp] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e9
+        kern[disp] = _short(r["Kernel_Name"])
+    agg = collections.defaultdict(lambda: [0, 0.0, 0.0, 0.0])
+    for disp, g in gui.items():
+        a = agg[kern[disp]]
+        a[0] += 1
+        a[1] += g / xcds
+        a[2] += dur[disp]
+        a[3] += busy.get(disp, 0.0)
+    out = ["| kernel | dispatches | total ms | mean clock GHz | MFMA busy % |", "|---|---|---|---|---|"]
+    for k, (n, cyc, t, b) in sorted(agg.items(), key=lambda kv: -kv[1][2]):
+        if t <= 0 or cyc <= 0:
+            continue
+        out.append(f"| `{k}` | {n} | {t * 1e3:.3f} | {cyc / t / 1e9:.3f} | {100 * b / (cyc * simds):.1f} |")
+    return "\n".join(out)
+
+
 if __name__ == "__main__":
     if sys.argv[1] == "stats":
         print(stats(sys.argv[2]))
     elif sys.argv[1] == "bykernel":
         print(bykernel(sys.argv[2], sys.argv[3] if len(sys.argv) > 3 else ""))
+    elif sys.argv[1] == "clock":
+        print(clock(sys.argv[2]))
     elif sys.argv[1] == "durations":
         print(durations(sys.argv[2], sys.argv[3] if len(sys.argv) > 3 else ""))
     else:
