@@ -207,6 +207,13 @@ def main():
     achieved = hess_flops / (hess_ms * 1e-3) / 1e12
     bound_ms = (hess_flops / (PEAK_BF16_TFLOPS * 1e12) + factor_flops / (PEAK_FP64_TFLOPS * 1e12)
                 + loop_flops / (PEAK_FP64_TFLOPS * 1e12)) * 1e3
+
+    def stage_roof(flops, ms, peak):
+        # one stage against the peak of the arithmetic it is bound by (all three are compute-bound: their
+        # algorithmic bytes take far less time at 8 TB/s than their flops at the peak)
+        ach = flops / (ms * 1e-3) / 1e12
+        return {"algorithmic_flop": float(f"{flops:.4e}"), "bound_ms": round(flops / (peak * 1e12) * 1e3, 4),
+                "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s", "frac": round(ach / peak, 4)}
     line = {
         "metric": METRIC,
         "value": round(ms_per_step, 4),
@@ -236,6 +243,11 @@ def main():
             "launch_ms": round(hess_ms, 4),
         },
         "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+        "stages_roofline": {
+            "hessian": stage_roof(hess_flops, stage_ms["hessian"], PEAK_BF16_TFLOPS),
+            "prepare": stage_roof(factor_flops, stage_ms["prepare"], PEAK_FP64_TFLOPS),
+            "quantize": stage_roof(loop_flops, stage_ms["quantize"], PEAK_FP64_TFLOPS),
+        },
         "weights_per_s": round(out * d / (ms_per_step * 1e-3), 1),
         "combined_bound_ms": round(bound_ms, 4),
         "frac_of_combined_bound": round(bound_ms / ms_per_step, 4),
