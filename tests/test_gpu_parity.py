@@ -34,6 +34,9 @@ HESS_CASES = [
 # wider than two 1024-column outer blocks of the quantize loop, with a ragged last panel: covers the
 # outer-block updates and their side-stream look-ahead
 WIDE = _cfg("bf16_wide", 40, 2600, 4096, dtype="bf16", w_std=0.02, outlier_channels=8, w_seed=17, x_seed=18)
+# an odd input width: U's rows (the update products' B operand) and W's rows are not 16-byte aligned, and
+# every update in the quantize loop has a ragged N
+ODD = _cfg("bf16_odd", 33, 389, 1111, dtype="bf16", w_std=0.02, outlier_channels=3, w_seed=19, x_seed=20)
 
 
 @pytest.mark.parametrize("cfg", HESS_CASES, ids=lambda c: c.name)
@@ -186,6 +189,8 @@ QUANT_CASES = [
     (WIDE, 4, 128, True),
     (WIDE, 3, 0, False),
     (WIDE, 4, 384, False),
+    (ODD, 4, 0, False),
+    (ODD, 3, 64, True),
 ]
 
 
@@ -221,6 +226,7 @@ E2E_CASES = [
     (HESS_CASES[2], 4, 128, False),
     (HESS_CASES[3], 3, 128, True),
     (WIDE, 4, 0, True),
+    (ODD, 4, 0, False),
 ]
 
 
