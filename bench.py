@@ -238,7 +238,7 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": hessian_traffic(),
+            "traffic": hessian_traffic() if cfg.name == "q_proj" else None,  # counters taken on q_proj only
             "algorithmic_per_launch": f"{hess_flops:.4e} flop (n*in*(in+1)), {x_bytes:.4e} B of X",
             "launch_ms": round(hess_ms, 4),
         },
