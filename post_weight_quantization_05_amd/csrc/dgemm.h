@@ -35,9 +35,9 @@ struct DgemmArgs {
   unsigned* diag_status;
 };
 
-// C = alpha op(A) op(B) + beta C on 64 x 64 tiles. Single plain products with small K take kernels that
-// keep a whole tile's operands in flight: op(B) = B with K <= 128 (no lower_only), and op(B) = B^T with
-// K <= 256 and no tile list. Everything else (batches, triangular K ranges, tile lists, op(A) = A^T, larger
+// C = alpha op(A) op(B) + beta C on 64 x 64 tiles. Single plain products with small K and at most 1024
+// tiles take kernels that keep a whole tile's operands in flight: op(B) = B with K <= 128 (no lower_only),
+// and op(B) = B^T with K <= 256 and no tile list. Everything else (batches, triangular K ranges, tile lists, op(A) = A^T, larger
 // K) takes the chunked-ring GEMM.
 hipError_t dgemm_launch(const DgemmArgs& a, bool ta, bool tb, int batches, hipStream_t stream);
 // One block-column step of the blocked Cholesky factorization (see k_colstep in dgemm.hip): C -= A B^T
