@@ -11,55 +11,71 @@ from oracle import gptq_oracle as O
 import tests.test_oracle_pins as P
 
 
-def _loop_factory(kind):
-    def loop(W0, U, bits, group=0):
-        qmax = O.qmax_for(bits)
-        W = np.array(W0, dtype=np.float64, copy=True)
-        out, d = W.shape
-        n_groups = -(-d // group) if group else 1
-        codes = np.zeros((out, d), dtype=np.int64)
-        scales = np.zeros((out, n_groups))
-        errs = np.zeros((out, d))
-        scale = O.row_scales(W, qmax)
-        orig = W.copy()
-        if not group:
-            scales[:, 0] = scale
-        for j in range(d):
-            if group and j % group == 0:
-                src = orig if kind == "group_from_original" else W
-                scale = O.row_scales(src[:, j:j + group], qmax)
-                scales[:, j // group] = scale
-            w = W[:, j]
-            c = np.clip(np.round(w / scale), -qmax, qmax)
-            if kind == "floor_not_round":
-                c = np.clip(np.floor(w / scale), -qmax, qmax)
-            q = c * scale
-            e = (w - q) / U[j, j]
-            if kind == "no_divide":
-                e = w - q
-            if kind == "unclipped_error":
-                e = (w - np.round(w / scale) * scale) / U[j, j]
-            codes[:, j] = c.astype(np.int64)
-            errs[:, j] = e
-            if j + 1 < d:
-                if kind == "sign":
-                    W[:, j + 1:] += np.outer(e, U[j, j + 1:])
-                elif kind == "transposed_u":
-                    W[:, j + 1:] -= np.outer(e, U[j + 1:, j])
-                elif kind == "off_by_one":
-                    W[:, j + 1:] -= np.outer(e, U[j, j:-1])
-                else:
-                    W[:, j + 1:] -= np.outer(e, U[j, j + 1:])
-        loss = np.einsum("rj,rj->r", errs, errs)
-        return codes, scales, errs, loss
-    return loop
+# Mistakes in the steps of the sweep: each replaces one of the oracle's step functions.
+def _propagate_sign(w, j, eps, U):
+    w[j + 1:] += eps * U[j, j + 1:]
+
+
+def _propagate_transposed(w, j, eps, U):
+    w[j + 1:] -= eps * U[j + 1:, j]
+
+
+def _propagate_off_by_one(w, j, eps, U):
+    w[j + 1:] -= eps * U[j, j:-1]
+
+
+def _step_error_undivided(residual, pivot):
+    return residual
+
+
+def _sym_code_unclipped(w, scale, qmax):
+    return np.rint(w / scale)
+
+
+def _sym_code_floor(w, scale, qmax):
+    return np.minimum(np.maximum(np.floor(w / scale), -qmax), qmax)
+
+
+def _grid_from_start(w_now, w_start, j, group):
+    if group:
+        return w_start[j:j + group] if j % group == 0 else None
+    return w_start if j == 0 else None
+
+
+def _grid_never_refit(w_now, w_start, j, group):
+    return w_start if j == 0 else None
+
+
+def _grid_refit_every_step(w_now, w_start, j, group):
+    return w_now[j:j + group] if group else (w_start if j == 0 else None)
+
+
+def _asym_code_unclipped(w, scale, zero, bits):
+    return np.rint(w / scale + zero)
+
+
+SWEEP_MUTATIONS = {
+    "sign": ("_propagate", _propagate_sign),
+    "transposed_u": ("_propagate", _propagate_transposed),
+    "off_by_one": ("_propagate", _propagate_off_by_one),
+    "no_divide": ("_step_error", _step_error_undivided),
+    "unclipped": ("sym_code", _sym_code_unclipped),
+    "floor_not_round": ("sym_code", _sym_code_floor),
+    "group_from_original": ("_grid_source", _grid_from_start),
+    "groups_ignored": ("_grid_source", _grid_never_refit),
+    "refit_every_step": ("_grid_source", _grid_refit_every_step),
+}
+
+
+def _sweep_factory(kind):
+    return SWEEP_MUTATIONS[kind][1]
 
 
 def _prepare_factory(kind):
     def prepare(S, colsq, n, damp, act_order):
         d = S.shape[0]
-        H = (2.0 / n) * S if kind != "no_two" else (1.0 / n) * S
-        H = 0.5 * (H + H.T)
+        Sym = np.tril(S) + np.tril(S, -1).T
+        H = (2.0 / n) * Sym if kind != "no_two" else (1.0 / n) * Sym
         dead = colsq == 0.0
         idx = np.flatnonzero(dead)
         if kind == "damp_before_dead":
@@ -114,9 +130,7 @@ PINS = [
 ]
 
 MUTATIONS = [
-    ("compensation_loop", _loop_factory, k) for k in
-    ["sign", "transposed_u", "off_by_one", "no_divide", "unclipped_error", "floor_not_round",
-     "group_from_original"]
+    (SWEEP_MUTATIONS[k][0], _sweep_factory, k) for k in SWEEP_MUTATIONS
 ] + [
     ("prepare", _prepare_factory, k) for k in ["no_two", "damp_before_dead", "absolute_damp", "ascending"]
 ] + [
@@ -147,8 +161,8 @@ def _asym_params_factory(kind):
         levels = 2 ** bits - 1
         if kind == "symmetric_levels":
             levels = 2 ** (bits - 1) - 1
-        wmin = Wblock.min(axis=1)
-        wmax = Wblock.max(axis=1)
+        wmin = Wblock.min(axis=-1)
+        wmax = Wblock.max(axis=-1)
         if kind == "levels_off_by_one":
             scale = np.where(wmax > wmin, (wmax - wmin) / (levels + 1), 1.0)
         else:
@@ -171,37 +185,15 @@ def _asym_value_factory(kind):
     return value
 
 
-def _asym_loop_factory(kind):
-    def loop(W0, U, bits, group=0):
-        W = np.array(W0, dtype=np.float64, copy=True)
-        orig = W.copy()
-        out, d = W.shape
-        n_groups = -(-d // group) if group else 1
-        codes = np.zeros((out, d), dtype=np.int64)
-        scales = np.zeros((out, n_groups))
-        zeros = np.zeros((out, n_groups))
-        errs = np.zeros((out, d))
-        scale, zero = O.asym_params(W, bits)
-        if not group:
-            scales[:, 0], zeros[:, 0] = scale, zero
-        for j in range(d):
-            if group and j % group == 0:
-                src = orig if kind == "group_from_original" else W
-                scale, zero = O.asym_params(src[:, j:j + group], bits)
-                scales[:, j // group], zeros[:, j // group] = scale, zero
-            w = W[:, j]
-            c = O.asym_code(w, scale, zero, bits)
-            q = O.asym_value(c, scale, zero)
-            e = (w - q) / U[j, j]
-            if kind == "error_before_clip":
-                e = (w - scale * (np.round(w / scale + zero) - zero)) / U[j, j]
-            codes[:, j] = c.astype(np.int64)
-            errs[:, j] = e
-            if j + 1 < d:
-                W[:, j + 1:] -= np.outer(e, U[j, j + 1:])
-        loss = np.einsum("rj,rj->r", errs, errs)
-        return codes, scales, zeros, errs, loss
-    return loop
+ASYM_SWEEP_MUTATIONS = {
+    "group_from_original": ("_grid_source", _grid_from_start),
+    "error_before_clip": ("asym_code", _asym_code_unclipped),
+    "no_divide": ("_step_error", _step_error_undivided),
+}
+
+
+def _asym_sweep_factory(kind):
+    return ASYM_SWEEP_MUTATIONS[kind][1]
 
 
 PINS_ASYM = [
@@ -210,6 +202,8 @@ PINS_ASYM = [
     (PA.test_loop_matches_exact_rational_obs_asym, (0,)),
     (PA.test_loop_matches_exact_rational_obs_asym, (2,)),
     (PA.test_loop_matches_exact_rational_obs_asym, (5,)),
+    (PA.test_group_params_from_updated_weights_exact_asym, (0,)),
+    (PA.test_group_params_from_updated_weights_exact_asym, (1,)),
     (PA.test_heavy_damping_is_rtn_asym, (3, 32)),
     (PA.test_loss_identity_asym, (4, True)),
     (PA.test_outputs_consistent_asym, ()),
@@ -222,7 +216,7 @@ MUTATIONS_ASYM = [
 ] + [
     ("asym_value", _asym_value_factory, "no_zero_shift"),
 ] + [
-    ("compensation_loop_asym", _asym_loop_factory, k) for k in ["group_from_original", "error_before_clip"]
+    (ASYM_SWEEP_MUTATIONS[k][0], _asym_sweep_factory, k) for k in ASYM_SWEEP_MUTATIONS
 ]
 
 
@@ -339,6 +333,62 @@ def test_storage_pins_catch_planted_mistake(monkeypatch, name, factory, kind):
     for fn, args in PINS_STORAGE:
         try:
             fn(*args)
+        except (AssertionError, ValueError, IndexError):
+            caught.append(fn.__name__)
+    assert caught, f"no pin caught mutation {name}:{kind}"
+
+
+# ------------------------------------------------------------------------------------------------
+# Input decoding and the noise-floor modes
+# ------------------------------------------------------------------------------------------------
+def _decode_factory(kind):
+    def to_f64(a, dtype):
+        if dtype == "bf16":
+            u = np.asarray(a, dtype=np.uint16).astype(np.uint32)
+            if kind == "low_half":
+                return u.view(np.float32).astype(np.float64)
+            if kind == "truncated_sign":
+                return (u << np.uint32(17) >> np.uint32(1)).view(np.float32).astype(np.float64)
+        return np.asarray(a, dtype=np.float32 if dtype == "f32" else np.float64).astype(np.float64)
+    return to_f64
+
+
+def _segments_factory(kind):
+    def acc(S, colsq, X64, seg_rows=2048):
+        n = X64.shape[0]
+        for r0 in range(0, n, seg_rows):
+            blk = X64[r0:r0 + seg_rows]
+            if kind == "fp64_sums":
+                S += blk.T @ blk
+            elif kind == "fp32_total":
+                S[:] = (S.astype(np.float32) + (blk.astype(np.float32).T @ blk.astype(np.float32))).astype(np.float64)
+            colsq += np.einsum("ki,ki->i", blk, blk)
+        return n
+    return acc
+
+
+PINS_INPUTS = [
+    (P.test_bf16_decoding_matches_torch_for_every_pattern, ()),
+    (P.test_fp32_segment_hessian_is_exact_on_integer_data, ()),
+    (P.test_fp32_segment_hessian_error_is_fp32_sized, ()),
+    (P.test_noise_floor_is_zero_when_the_fp32_sums_are_exact, ()),
+]
+
+MUTATIONS_INPUTS = [
+    ("to_f64", _decode_factory, k) for k in ["low_half", "truncated_sign"]
+] + [
+    ("accumulate_fp32_segments", _segments_factory, k) for k in ["fp64_sums", "fp32_total"]
+]
+
+
+@pytest.mark.parametrize("name,factory,kind", MUTATIONS_INPUTS, ids=[f"{m[0]}-{m[2]}" for m in MUTATIONS_INPUTS])
+def test_input_pins_catch_planted_mistake(monkeypatch, name, factory, kind):
+    monkeypatch.setattr(O, name, factory(kind))
+    caught = []
+    for fn, args in PINS_INPUTS:
+        try:
+            with np.errstate(invalid="ignore"):
+                fn(*args)
         except (AssertionError, ValueError, IndexError):
             caught.append(fn.__name__)
     assert caught, f"no pin caught mutation {name}:{kind}"

@@ -416,8 +416,8 @@ def test_output_error_gram_form_equals_direct():
 @pytest.mark.parametrize("name,bits,act", [("tiny", 4, False), ("tiny", 3, False), ("teacher", 3, False),
                                            ("teacher", 2, False), ("teacher", 3, True), ("teacher", 2, True)])
 def test_output_error_well_below_rtn(name, bits, act):
-    """P-12: [lesson] acceptance test: the output error on X is well below plain rounding's. The ratio
-    should be near mean(1/U_jj^2) / mean(H_jj) (the variance of x_j left after regressing on the
+    """P-12: [lesson] acceptance check: on X, GPTQ's output error must be clearly lower than that of
+    round-to-nearest. The ratio should be near mean(1/U_jj^2) / mean(H_jj) (the variance of x_j left after regressing on the
     inputs not yet quantized, relative to its total variance)."""
     c = syn.config_by_name(name)
     W = O.to_f64(syn.gen_w(c), c.dtype)
@@ -473,3 +473,97 @@ def test_bf16_encoding_matches_torch_and_is_deterministic():
     x2 = syn.gen_x(c, 4000, 4100, threads=1)
     np.testing.assert_array_equal(x1, x2)
     assert (syn.gen_x(c, 0, 64)[:, syn.workloads.dead_channels(c)] == 0).all()
+
+
+def test_bf16_decoding_matches_torch_for_every_pattern():
+    """to_f64's bf16 branch against torch's own bf16 -> fp32 widening, for all 65536 bit patterns
+    (zeros, subnormals, normals, infinities; NaN patterns must decode to NaN)."""
+    torch = pytest.importorskip("torch")
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    with np.errstate(invalid="ignore"):  # NaN patterns widen with a warning
+        ours = O.to_f64(bits, "bf16")
+        ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float32).numpy().astype(np.float64)
+    nan = np.isnan(ref)
+    assert nan.sum() == 2 * 127  # exponent all ones, mantissa != 0, either sign
+    np.testing.assert_array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan].view(np.uint64), ref[~nan].view(np.uint64))  # bitwise, -0.0 included
+
+
+def test_prepare_reads_the_lower_triangle_of_s():
+    """S's lower triangle is authoritative (the library writes only that half): whatever the strictly
+    upper half holds, H is built from the lower half mirrored."""
+    W, X = rand_problem(81, 3, 9, 40)
+    S, colsq, n = O.hessian_from_x(X)
+    junk = S.copy()
+    junk[np.triu_indices(9, 1)] = np.random.default_rng(2).standard_normal(36) * 1e3
+    a = O.prepare(S, colsq, n, 0.01, False)[0]
+    b = O.prepare(junk, colsq, n, 0.01, False)[0]
+    assert np.array_equal(a, b) and np.array_equal(b, b.T)
+
+
+# ------------------------------------------------------------------------------------------------
+# Noise floor (the oracle against itself with an fp32-accumulated Hessian, or with U in fp32)
+# ------------------------------------------------------------------------------------------------
+def test_fp32_segment_hessian_is_exact_on_integer_data():
+    """Integer-valued X whose segment sums stay below 2^24: every fp32 product and partial sum inside a
+    segment is exact, so the fp32-segment S must equal the fp64 S bit for bit (and colsq is the same
+    fp64 sum). The totals over all 64 segments pass 2^24, so summing the segments in fp32 would not be
+    exact: the segments must be combined in fp64."""
+    rng = np.random.default_rng(23)
+    X = rng.integers(-31, 32, size=(64 * 2048 + 5, 12)).astype(np.float64)  # |segment sum| <= 2048*961 < 2^24
+    S64, c64, n64 = O.hessian_from_x(X)
+    S32, c32, n32 = O.hessian_from_x(X, fp32_segments=True)
+    assert n64 == n32 == X.shape[0]
+    assert np.diag(S64).min() > 2.0 ** 24
+    assert np.array_equal(S64, S32) and np.array_equal(c64, c32)
+
+
+def test_fp32_segment_hessian_error_is_fp32_sized():
+    """On N(0,1) data the fp32-segment S differs from the fp64 S, and every entry stays inside the
+    floating-point dot-product bound for m = 2048 fp32 terms per segment,
+    |dS_ij| <= gamma_m sum_k |x_ki x_kj|, gamma_m = m u / (1 - m u), u = 2^-24 (plus fp64 rounding).
+    Its typical relative size is near 1e-7 (a few fp32 ulps)."""
+    rng = np.random.default_rng(29)
+    X = rng.standard_normal((3 * 2048 + 111, 16)).astype(np.float32).astype(np.float64)
+    S64, _, _ = O.hessian_from_x(X)
+    S32, _, _ = O.hessian_from_x(X, fp32_segments=True)
+    A = np.abs(X).T @ np.abs(X)
+    u, m = 2.0 ** -24, 2048
+    gamma = m * u / (1 - m * u)
+    dS = np.abs(S32 - S64)
+    assert (dS <= gamma * A + 1e-12 * A).all()
+    rel = dS / np.sqrt(np.outer(np.diag(S64), np.diag(S64)))
+    assert 1e-9 < np.median(rel[np.tril_indices(16)]) < 1e-5
+    assert rel.max() > 0.0
+
+
+def test_fp32_segment_hessian_rejects_wider_inputs():
+    with pytest.raises(ValueError):
+        O.hessian_from_x(np.full((4, 2), 0.1), fp32_segments=True)
+
+
+def test_u_rounded_to_fp32_is_within_half_an_fp32_ulp():
+    W, X = rand_problem(83, 4, 20, 60)
+    S, colsq, n = O.hessian_from_x(X)
+    r64 = O.gptq_oracle(W, hessian=(S, colsq, n))
+    r32 = O.gptq_oracle(W, hessian=(S, colsq, n), u_round=np.float32)
+    nz = r64["U"] != 0
+    assert np.all(np.abs(r32["U"][nz] - r64["U"][nz]) <= 2.0 ** -24 * np.abs(r64["U"][nz]))
+    assert np.array_equal(r32["U"][~nz], r64["U"][~nz])
+    assert np.array_equal(r32["U"].astype(np.float32).astype(np.float64), r32["U"])
+
+
+def test_noise_floor_is_zero_when_the_fp32_sums_are_exact():
+    """The floor measures the oracle against itself: with integer data the fp32-segment mode reproduces
+    the fp64 run exactly (no drift), while the fp32-U mode still perturbs U."""
+    rng = np.random.default_rng(31)
+    X = rng.integers(-3, 4, size=(3000, 32)).astype(np.float64)
+    X = X @ (np.eye(32, dtype=np.int64) + np.eye(32, k=1, dtype=np.int64))  # correlated, still integral
+    W = 0.05 * rng.standard_normal((40, 32))
+    S64, colsq, n = O.hessian_from_x(X)
+    S32, _, _ = O.hessian_from_x(X, fp32_segments=True)
+    fl = O.noise_floor(W, S64, S32, colsq, n, 3, 8, 0.01, True)
+    assert fl["fp32_segment_S"] == dict(f=0.0, mismatches=0, q_rel=0.0, out_rel=0.0)
+    ref = O.gptq_oracle(W, X, bits=3, group=8, act_order=True)
+    assert np.array_equal(fl["ref"]["codes"], ref["codes"])
+    assert fl["fp32_U"]["f"] <= 0.01

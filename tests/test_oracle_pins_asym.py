@@ -126,6 +126,20 @@ def test_loop_matches_exact_rational_obs_asym(seed):
     np.testing.assert_array_equal(r["codes_q"], ex_codes)
 
 
+@pytest.mark.parametrize("seed", range(4))
+def test_group_params_from_updated_weights_exact_asym(seed):
+    """With groups, each group's (scale, zero) comes from its weights as the earlier steps have updated
+    them (the handbook's per-column loop; the guide's "The code, line by line" for the scale). Exact
+    rational run with three groups per row and strongly coupled inputs, so that the updates move each
+    later group's min and max."""
+    W, X = rand_problem(940 + seed, 3, 6, 9)
+    X[:, 1] += 2.0 * X[:, 0]
+    X[:, 3] -= 1.5 * X[:, 2]
+    r = O.gptq_oracle_asym(W, X, bits=2, group=2, damp=0.01)
+    ex_codes, _ = _exact_asym(W, X, 2, 2, 0.01)
+    np.testing.assert_array_equal(r["codes_q"], ex_codes)
+
+
 @pytest.mark.parametrize("bits,group", [(3, 0), (4, 0), (3, 32)])
 def test_heavy_damping_is_rtn_asym(bits, group):
     """Heavy damping makes H a multiple of I: nothing is pushed and the asymmetric GPTQ codes are the
