@@ -200,7 +200,7 @@ def main():
     # algorithmic work (lower triangle of X^T X, the two-step factor, the loop's multiply-adds)
     n = cfg.n
     hess_flops = n * d * (d + 1)
-    factor_flops = (2.0 / 3.0 if flags else 4.0 / 3.0) * d ** 3
+    factor_flops = (2.0 / 3.0 if flags == G.GPTQ_FACTOR_REVERSED else 4.0 / 3.0) * d ** 3
     loop_flops = out * d * (d - 1)
     x_bytes = n * d * (2 if cfg.dtype == "bf16" else 4)
     hess_ms = stage_ms["hessian"]

@@ -19,8 +19,8 @@
  *  - The caller owns every buffer, workspace included. The library allocates no device memory, frees
  *    nothing and keeps no pointer after a call returns. Workspaces are sized by the *_workspace_bytes
  *    queries and need no initialisation. Their contents after a call are unspecified.
- *  - `stream` is a hipStream_t (NULL = the null stream). Calls 1 and 3 are fully asynchronous; call 2
- *    synchronises `stream` once to read a 4-byte status word written by its kernels.
+ *  - `stream` is a hipStream_t (NULL = the null stream). Call 1 is fully asynchronous; calls 2 and 3
+ *    synchronise `stream` once, at their end, to read a 4-byte status word written by their kernels.
  *  - Every call returns a gptq_status. On an argument error nothing is launched and no output is
  *    written. Calls on different streams with disjoint buffers are independent; the library has no
  *    global mutable state.
@@ -49,12 +49,13 @@ typedef enum {
 typedef enum { GPTQ_F32 = 0, GPTQ_BF16 = 1 } gptq_dtype;
 
 /* Factorization route for gptq_prepare_chol (`flags`).
- *  GPTQ_FACTOR_INVERSE_RECHOL (0): L = chol(H); L^-1; H^-1 = L^-T L^-1; U = (chol(H^-1))^T, the order the
- *    guide's _hessian_inverse_chol takes ("The code, line by line").
- *  GPTQ_FACTOR_REVERSED (1): U = J chol(J H J)^-1 J with J the index reversal; the same unique U (upper,
- *    positive diagonal, U^T U = H^-1) with half the flops, because H = V V^T with V = U^-1 upper. */
-#define GPTQ_FACTOR_INVERSE_RECHOL 0u
-#define GPTQ_FACTOR_REVERSED 1u
+ *  GPTQ_FACTOR_REVERSED (0, the default): U = J chol(J H J)^-1 J with J the index reversal: one Cholesky
+ *    factorization and one triangular inverse. It is the unique U (upper, positive diagonal,
+ *    U^T U = H^-1) because H = V V^T with V = U^-1 upper, and J V J is lower.
+ *  GPTQ_FACTOR_INVERSE_RECHOL (1): L = chol(H); L^-1; H^-1 = L^-T L^-1; U = (chol(H^-1))^T, the order the
+ *    guide's _hessian_inverse_chol takes ("The code, line by line"), at twice the flops. */
+#define GPTQ_FACTOR_REVERSED 0u
+#define GPTQ_FACTOR_INVERSE_RECHOL 1u
 
 /* ---------------------------------------------------------------------------------------------------
  * 1. Hessian accumulation. GPTQ guide, "The idea": H = 2 X^T X / n is the curvature of the layer's
@@ -97,7 +98,7 @@ int gptq_hessian_accumulate(const void* X, int x_dtype, int64_t n_rows, int64_t 
  *             quantization order; the strictly lower triangle is set to 0.
  *  perm       out: int32[in], perm[j] = original input index quantized at position j.
  *  dead       out: uint8[in], 1 for dead inputs (original order).
- *  flags      GPTQ_FACTOR_INVERSE_RECHOL or GPTQ_FACTOR_REVERSED.
+ *  flags      GPTQ_FACTOR_REVERSED (0) or GPTQ_FACTOR_INVERSE_RECHOL; other bits -> INVALID_ARG.
  *  ws         at least gptq_prepare_workspace_bytes(in) bytes.
  *  Synchronises `stream` once. Errors: INVALID_ARG (in < 1, n_total < 1, damp < 0 or not finite, NULL
  *  pointer, unknown flags), WORKSPACE, NOT_SPD (a Cholesky pivot below 2^-1000, in particular <= 0, e.g.
@@ -111,8 +112,9 @@ int gptq_prepare_chol(const double* S, const double* colsq, int64_t n_total, int
                       void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------------------------
- * 3. The error-compensation loop. Lesson "GPTQ's error-compensation loop" (the four steps: round column
- *    j of every row, err = (w - q) / U[j][j], W[:, j+1:] -= outer(err, U[j, j+1:])) and GPTQ guide,
+ * 3. The error-compensation loop. Lesson "GPTQ's error-compensation loop" (its four steps: each column in
+ *    turn is snapped to the grid in every row, the residual over the pivot U[j][j] is the row's error, and
+ *    the later columns k of the row take off error * U[j][k]) and GPTQ guide,
  *    "The code, line by line" (per-row scales from the starting weights; with groups, scales from the
  *    already-updated weights at each group boundary; clip to +-qmax) and "When it breaks" (g_idx).
  *    The guide's "Simplifications" mentions lazy updates in 128-column blocks; this library quantizes
@@ -133,9 +135,10 @@ int gptq_prepare_chol(const double* S, const double* colsq, int64_t n_total, int
  *             for the row's dead-zeroed, permuted start w0 and result q.
  *  Dequantized weights: Q[r][c] = codes[r][c] * scales[r][g_idx[c]] (with fp64 scales: see row_loss).
  *  ws         at least gptq_quantize_workspace_bytes(out, in) bytes.
- *  Non-finite weights are not detected; their codes are unspecified.
+ *  Synchronises `stream` once at its end (the status word of the weight check).
  *  Errors: INVALID_ARG (out/in < 1, ld_w < in, bits outside 2..8, group < 0, unknown dtype, NULL required
- *  pointer), UNSUPPORTED (group), WORKSPACE, HIP.
+ *  pointer), UNSUPPORTED (group), WORKSPACE, NONFINITE (a NaN or Inf weight in a live input column; the
+ *  outputs are then unspecified; weights of dead columns are zeroed first and never read), HIP.
  * ------------------------------------------------------------------------------------------------- */
 size_t gptq_quantize_workspace_bytes(int64_t out, int64_t in);
 int gptq_quantize_layer(const void* W, int w_dtype, int64_t out, int64_t in, int64_t ld_w,

@@ -18,8 +18,8 @@ GPTQ_ERR_HIP = -6
 GPTQ_F32 = 0
 GPTQ_BF16 = 1
 
-GPTQ_FACTOR_INVERSE_RECHOL = 0
-GPTQ_FACTOR_REVERSED = 1
+GPTQ_FACTOR_REVERSED = 0  # the default route
+GPTQ_FACTOR_INVERSE_RECHOL = 1
 
 GPTQ_GRID_SYMMETRIC = 0
 GPTQ_GRID_ASYMMETRIC = 1

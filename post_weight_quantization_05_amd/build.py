@@ -37,9 +37,17 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+# A test build of the same library in which every fp64 product takes the chunked-ring GEMM (the small-K
+# kernels' tile cutoff set to 0), so that parity tests cover those routes at small sizes too. Only the
+# GEMM source differs; the tests load it beside the main library.
+VARIANT_LIB = os.path.join(PKG, "libgptq_mi355x_ringonly.so")
+VARIANT_DEFS = ["-DGPTQ_DGEMM_SMALLK_TILES=0"]
+VARIANT_SRC = "dgemm.hip"
+
+
+def _compile(src: str, defs=(), tag: str = "") -> str:
+    obj = os.path.join(BUILD, os.path.basename(src) + tag + ".o")
+    cmd = [HIPCC, *CFLAGS, *defs, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
@@ -56,18 +64,29 @@ def build(verbose: bool = True) -> str:
         raise RuntimeError("hipcc not found; set HIPCC")
     os.makedirs(BUILD, exist_ok=True)
     srcs = sources()
-    with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    var_src = os.path.join(CSRC, VARIANT_SRC)
+    with ThreadPoolExecutor(max_workers=min(8, len(srcs) + 1)) as ex:
+        objs_f = ex.map(_compile, srcs)
+        var_f = ex.submit(_compile, var_src, VARIANT_DEFS, ".ringonly")
+        objs = list(objs_f)
+        var_obj = var_f.result()
+    _link(objs, LIB)
+    _link([var_obj if o.endswith(os.sep + VARIANT_SRC + ".o") else o for o in objs], VARIANT_LIB)
+    if verbose:
+        print(f"built {LIB} (and the test build {os.path.basename(VARIANT_LIB)})")
+    return LIB
+
+
+def _link(objs, out: str) -> None:
+    tmp = out + ".tmp"
+    # -Bsymbolic: calls between the library's own functions bind inside it, so the test build can be loaded
+    # beside the main library in one process
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,-Bsymbolic", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
         raise RuntimeError("link failed")
-    os.replace(tmp, LIB)
-    if verbose:
-        print(f"built {LIB}")
-    return LIB
+    os.replace(tmp, out)
 
 
 if __name__ == "__main__":

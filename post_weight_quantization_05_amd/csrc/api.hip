@@ -66,7 +66,7 @@ int gptq_prepare_chol(const double* S, const double* colsq, int64_t n_total, int
   if (!S || !colsq || !U || !perm || !dead) return GPTQ_ERR_INVALID_ARG;
   if (in < 1 || in > MAX_IN || n_total < 1) return GPTQ_ERR_INVALID_ARG;
   if (!(damp >= 0.0) || !std::isfinite(damp)) return GPTQ_ERR_INVALID_ARG;
-  if ((flags & ~GPTQ_FACTOR_REVERSED) != 0u) return GPTQ_ERR_INVALID_ARG;
+  if ((flags & ~GPTQ_FACTOR_INVERSE_RECHOL) != 0u) return GPTQ_ERR_INVALID_ARG;
   if (!ws || ws_bytes < prepare_ws_bytes(in)) return GPTQ_ERR_WORKSPACE;
   unsigned dev_status = 0;
   hipError_t e = prepare_launch(S, colsq, n_total, in, damp, act_order ? 1 : 0, flags, U, perm, dead, ws,
@@ -94,8 +94,11 @@ int gptq_quantize_layer_ex(const void* W, int w_dtype, int64_t out, int64_t in, 
   if (bits < 2 || bits > 8 || group < 0) return GPTQ_ERR_INVALID_ARG;
   if (group != 0 && !(128 % group == 0 || group % 128 == 0)) return GPTQ_ERR_UNSUPPORTED;
   if (!ws || ws_bytes < quantize_ws_bytes(out, in)) return GPTQ_ERR_WORKSPACE;
-  return hip_status(quantize_launch(W, w_dtype, out, in, ld_w, U, perm, dead, bits, group, grid, codes, scales,
-                                    zeros, g_idx, row_loss, ws, reinterpret_cast<hipStream_t>(stream)));
+  unsigned dev_status = 0;
+  const hipError_t e = quantize_launch(W, w_dtype, out, in, ld_w, U, perm, dead, bits, group, grid, codes, scales,
+                                       zeros, g_idx, row_loss, ws, reinterpret_cast<hipStream_t>(stream), &dev_status);
+  if (e != hipSuccess) return GPTQ_ERR_HIP;
+  return (dev_status & DEV_STATUS_NONFINITE) ? GPTQ_ERR_NONFINITE : GPTQ_OK;
 }
 
 int gptq_quantize_layer(const void* W, int w_dtype, int64_t out, int64_t in, int64_t ld_w, const double* U,
@@ -128,7 +131,8 @@ int gptq_dequant_matmul(const void* X, int x_dtype, int64_t n, int64_t in, int64
     return GPTQ_ERR_INVALID_ARG;
   if (ld_x < in || ld_y < out || !valid_dtype(x_dtype) || bits < 2 || bits > 8 || group < 0 || (relu != 0 && relu != 1))
     return GPTQ_ERR_INVALID_ARG;
-  if (((n + 63) / 64) * ((out + 63) / 64) > (int64_t)INT32_MAX) return GPTQ_ERR_INVALID_ARG;  // one workgroup per 64 x 64 tile
+  // one workgroup of 256 work-items per 64 x 64 tile of Y, in a 1-D grid of at most 2^32 - 1 work-items
+  if (((n + 63) / 64) * ((out + 63) / 64) > (int64_t)(UINT32_MAX / 256)) return GPTQ_ERR_INVALID_ARG;
   const int n_groups = group ? (int)((in + group - 1) / group) : 1;
   return hip_status(dequant_matmul_launch(X, x_dtype, n, in, ld_x, packed, scales, zeros, g_idx, out, bits, grid,
                                           n_groups, bias, relu, Y, ld_y, reinterpret_cast<hipStream_t>(stream)));

@@ -16,7 +16,7 @@ typedef __attribute__((ext_vector_type(4))) double f64x4;
 
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-// Device status word bits (written with atomicOr, read once by the host at the end of prepare).
+// Device status word bits (written with atomicOr, read once by the host at the end of prepare and of quantize).
 enum : unsigned {
   DEV_STATUS_NOT_SPD = 1u,
   DEV_STATUS_NONFINITE = 2u,
@@ -54,7 +54,7 @@ size_t quantize_ws_bytes(int64_t out, int64_t in);
 hipError_t quantize_launch(const void* W, int w_dtype, int64_t out, int64_t in, int64_t ld_w, const double* U,
                            const int32_t* perm, const uint8_t* dead, int bits, int group, int grid, int8_t* codes,
                            float* scales, int32_t* zeros, int32_t* g_idx, double* row_loss, void* ws,
-                           hipStream_t stream);
+                           hipStream_t stream, unsigned* host_status);
 
 // Packed codes and the dequantizing matmul (pack.hip)
 int64_t packed_words_per_row(int64_t in, int bits);

@@ -507,7 +507,10 @@ __global__ __launch_bounds__(256) void k_colstep(DgemmArgs a, DgemmArgs xa, int 
 #define GPTQ_DGEMM_SMALLK 1
 #endif
 constexpr int SK_MAX = 128;
-constexpr int SK_TILES = 1024;  // at most this many 64 x 64 tiles per launch
+#ifndef GPTQ_DGEMM_SMALLK_TILES
+#define GPTQ_DGEMM_SMALLK_TILES 1024
+#endif
+constexpr int SK_TILES = GPTQ_DGEMM_SMALLK_TILES;  // at most this many 64 x 64 tiles per launch (0: never)
 constexpr int SK_AS = 68, SK_BS = 80;
 __global__ __launch_bounds__(256) void k_dgemm_nn_smallk(DgemmArgs a) {
   constexpr int T = 64, NH = SK_MAX / T;

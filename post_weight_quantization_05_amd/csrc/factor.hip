@@ -20,6 +20,7 @@
 //  panel / SYRK / triangular-inverse levels / H^-1 = L^-T L^-1 use the fp64 MFMA GEMM core (dgemm.hip).
 // Routes (flags): INVERSE_RECHOL = potrf, trtri, lauum, potrf, transpose (the guide's order);
 // REVERSED = potrf and trtri of J H J, then U = J L^-1 J (same unique U, half the work).
+#include <algorithm>
 #include <type_traits>
 
 #include "common.h"
@@ -203,14 +204,14 @@ __global__ __launch_bounds__(256) void k_transpose_lower_to_upper(double* __rest
   }
 }
 
-// U[a][b] = Li[d-1-a][d-1-b] for a <= b, 0 below the diagonal.
+// U[a][b] = Li[d-1-a][d-1-b] for a <= b, 0 below the diagonal. Grid: x = 256-column blocks of a row,
+// y = rows in a grid-stride loop (the grid stays small at any d).
 __global__ __launch_bounds__(256) void k_reverse_to_upper(const double* __restrict__ Li, int d,
                                                           double* __restrict__ U) {
-  const int nbx = (d + 255) / 256;
-  const int a = blockIdx.x / nbx;
-  const int b = (blockIdx.x - a * nbx) * 256 + threadIdx.x;
+  const int b = blockIdx.x * 256 + threadIdx.x;
   if (b >= d) return;
-  U[(int64_t)a * d + b] = (b >= a) ? Li[(int64_t)(d - 1 - a) * d + (d - 1 - b)] : 0.0;
+  for (int a = blockIdx.y; a < d; a += gridDim.y)
+    U[(int64_t)a * d + b] = (b >= a) ? Li[(int64_t)(d - 1 - a) * d + (d - 1 - b)] : 0.0;
 }
 
 // Blocked right-looking Cholesky in two levels. Inside an outer block column of NBO columns, each
@@ -381,7 +382,7 @@ hipError_t prepare_launch(const double* S, const double* colsq, int64_t n_total,
   double* diag_h = reinterpret_cast<double*>(w);
   w += align_up((size_t)d * sizeof(double), 256);
   unsigned* status = reinterpret_cast<unsigned*>(w);
-  const bool reversed = (flags & GPTQ_FACTOR_REVERSED) != 0;
+  const bool reversed = (flags & GPTQ_FACTOR_INVERSE_RECHOL) == 0;
 
   hipError_t e;
 #define GPTQ_TRY(x)          \
@@ -405,7 +406,8 @@ hipError_t prepare_launch(const double* S, const double* colsq, int64_t n_total,
   GPTQ_TRY(hipGetLastError());
   GPTQ_TRY(trtri_lower(A, d, U /* scratch */, stream));
   if (reversed) {
-    hipLaunchKernelGGL(k_reverse_to_upper, dim3((unsigned)(ceil_div(d, 256) * d)), dim3(256), 0, stream, A, d, U);
+    hipLaunchKernelGGL(k_reverse_to_upper, dim3((unsigned)ceil_div(d, 256), (unsigned)std::min(d, 4096)), dim3(256),
+                       0, stream, A, d, U);
     GPTQ_TRY(hipGetLastError());
   } else {
     // H^-1 = Li^T Li (lower tiles) into U, then its Cholesky factor, then U = Lu^T

@@ -14,22 +14,24 @@
 //                    driver feeds to the next layer ("How it works", apply_layerwise). 64 x 64 tiles of
 //                    Y, 4 waves of 32 x 32 on v_mfma_f32_16x16x4f32; X (bf16 widened exactly, or fp32)
 //                    and the dequantized weights go through LDS as [k][i] in chunks of 16 inputs.
+#include <algorithm>
+
 #include "common.h"
 
 namespace gptq {
 
 namespace {
 
-__global__ __launch_bounds__(256) void k_pack(const int8_t* __restrict__ codes, int out, int in, int bits,
-                                              int offset, int wpr, uint32_t* __restrict__ packed) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (int64_t)out * wpr) return;
-  const int r = (int)(idx / wpr), w = (int)(idx - (int64_t)r * wpr);
+// word idx = r * wpr + w of the packed output: the (at most 32 / bits + 1) codes that touch it
+__device__ __forceinline__ void pack_word(const int8_t* __restrict__ codes, int in, int bits, int offset, int wpr,
+                                          int64_t idx, uint32_t* __restrict__ packed) {
+  const int64_t r = idx / wpr;
+  const int w = (int)(idx - r * wpr);
   const uint32_t mask = (1u << bits) - 1u;
   const int64_t bit0 = (int64_t)w * 32;
   const int j0 = (int)(bit0 / bits);
   const int j1 = (int)min<int64_t>(in - 1, (bit0 + 31) / bits);
-  const int8_t* crow = codes + (int64_t)r * in;
+  const int8_t* crow = codes + r * in;
   uint32_t word = 0u;
   for (int j = j0; j <= j1; ++j) {
     const uint32_t v = ((uint32_t)(uint8_t)crow[j] + (uint32_t)offset) & mask;
@@ -37,6 +39,14 @@ __global__ __launch_bounds__(256) void k_pack(const int8_t* __restrict__ codes, 
     word |= (pos >= 0) ? (v << pos) : (v >> (-pos));
   }
   packed[idx] = word;
+}
+
+// one thread per output word, in a grid-stride loop over the out * wpr words (up to 2^34 of them)
+__global__ __launch_bounds__(256) void k_pack(const int8_t* __restrict__ codes, int out, int in, int bits,
+                                              int offset, int wpr, uint32_t* __restrict__ packed) {
+  const int64_t total = (int64_t)out * wpr;
+  for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (int64_t)gridDim.x * 256)
+    pack_word(codes, in, bits, offset, wpr, idx, packed);
 }
 
 // code (r, c) from the packed stream: the word holding its first bit and, when it straddles, the next one
@@ -147,8 +157,9 @@ hipError_t pack_launch(const int8_t* codes, int64_t out, int64_t in, int bits, i
   const int wpr = (int)packed_words_per_row(in, bits);
   const int offset = (grid == GPTQ_GRID_ASYMMETRIC) ? 0 : (1 << (bits - 1));
   const int64_t total = out * (int64_t)wpr;
-  hipLaunchKernelGGL(k_pack, dim3((unsigned)ceil_div(total, 256)), dim3(256), 0, stream, codes, (int)out, (int)in,
-                     bits, offset, wpr, packed);
+  const unsigned blocks = (unsigned)std::min<int64_t>(ceil_div(total, 256), 1 << 20);
+  hipLaunchKernelGGL(k_pack, dim3(blocks), dim3(256), 0, stream, codes, (int)out, (int)in, bits, offset, wpr,
+                     packed);
   return hipGetLastError();
 }
 

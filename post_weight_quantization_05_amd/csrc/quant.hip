@@ -1,8 +1,8 @@
 // The error-compensation loop on gfx950 (fp64 working copy).
 //
-// Lesson "GPTQ's error-compensation loop" (herodthegreater.github.io/pigeon/school/gptq_loop/): for
-// columns j = 0, 1, ...: q = round_to_grid(W[:, j]); err = (W[:, j] - q) / U[j][j];
-// W[:, j+1:] -= outer(err, U[j, j+1:]). GPTQ guide ("GPTQ", herodthegreater.github.io/pigeon/guide/gptq/),
+// Lesson "GPTQ's error-compensation loop" (herodthegreater.github.io/pigeon/school/gptq_loop/): the columns
+// are taken in order; each weight of column j is snapped to the grid, its residual divided by the pivot
+// U[j][j] is that row's error, and the row's later columns k take off error * U[j][k]. GPTQ guide ("GPTQ", herodthegreater.github.io/pigeon/guide/gptq/),
 // "The code, line by line": one scale per row from the starting weights, or, with groups, a scale from
 // the already-updated weights of columns [j, j + group) at each group boundary; codes are
 // clip(round(w / scale), -qmax, qmax). "Simplifications" mentions lazy 128-column batch updates.
@@ -33,6 +33,7 @@
 
 #include "common.h"
 #include "dgemm.h"
+#include "divide.h"
 
 namespace gptq {
 
@@ -95,15 +96,6 @@ __device__ __forceinline__ double sum16(double v) {
   return v;
 }
 
-// a / b correctly rounded from y = RN(1 / b): q = RN(a y), r = a - b q (exact with an FMA),
-// RN(q + r y) = RN(a / b) (Markstein's theorem; finite normal operands, no overflow or underflow).
-// The same quotient as an IEEE division, in three dependent operations.
-__device__ __forceinline__ double div_rn(double a, double b, double y) {
-  const double q = a * y;
-  const double r = fma(-b, q, a);
-  return fma(r, y, q);
-}
-
 template <typename T>
 __device__ __forceinline__ double to_f64(T v);
 template <>
@@ -122,13 +114,14 @@ __global__ __launch_bounds__(256) void k_rowprep(const T* __restrict__ W, int64_
                                                  double qmax, int group, double* __restrict__ Wq,
                                                  double* __restrict__ scale_row, double* __restrict__ zero_row,
                                                  float* __restrict__ scales, int32_t* __restrict__ zeros,
-                                                 double* __restrict__ row_loss) {
+                                                 double* __restrict__ row_loss, unsigned* __restrict__ status) {
   __shared__ double red[256];
   __shared__ double red2[256];
   const int r = blockIdx.x;
   const T* wr = W + (int64_t)r * ld_w;
   double* q = Wq + (int64_t)r * in;
   double mx = ASYM ? -INFINITY : 0.0, mn = INFINITY;
+  bool bad = false;  // a NaN or Inf among the row's live weights
   // eight columns per thread per pass: the index loads, then the gathered loads, all in flight together
   constexpr int U8 = 8;
   for (int j0 = threadIdx.x; j0 < in; j0 += 256 * U8) {
@@ -150,6 +143,7 @@ __global__ __launch_bounds__(256) void k_rowprep(const T* __restrict__ W, int64_
       const int j = j0 + 256 * u;
       if (j < in) {
         q[j] = v[u];
+        bad = bad || !isfinite(v[u]);
         if (ASYM) {
           mx = fmax(mx, v[u]);
           mn = fmin(mn, v[u]);
@@ -159,6 +153,7 @@ __global__ __launch_bounds__(256) void k_rowprep(const T* __restrict__ W, int64_
       }
     }
   }
+  if (bad) atomicOr(status, DEV_STATUS_NONFINITE);
   red[threadIdx.x] = mx;
   red2[threadIdx.x] = mn;
   __syncthreads();
@@ -374,6 +369,8 @@ __global__ __launch_bounds__(256) void k_panel(double* __restrict__ Wq, int out,
   }
 }
 
+__global__ void k_clear_status(unsigned* p) { *p = 0u; }
+
 __global__ void k_gidx(const int32_t* __restrict__ perm, int in, int group, int32_t* __restrict__ g_idx) {
   const int j = blockIdx.x * blockDim.x + threadIdx.x;
   if (j >= in) return;
@@ -389,6 +386,7 @@ size_t quantize_ws_bytes(int64_t out, int64_t in) {
   b += align_up((size_t)out * OB * sizeof(double), 256);  // errors of one outer block
   b += align_up((size_t)out * sizeof(double), 256);       // current fp64 scale per row
   b += align_up((size_t)out * sizeof(double), 256);       // current zero point per row (asymmetric grid)
+  b += 256;                                                // status word
   return b;
 }
 
@@ -396,13 +394,13 @@ template <bool ASYM>
 static hipError_t launch_rowprep(const void* W, int w_dtype, int out, int in, int64_t ld_w, const int32_t* perm,
                                  const uint8_t* dead, double qmax, int group, double* Wq, double* scale_row,
                                  double* zero_row, float* scales, int32_t* zeros, double* row_loss,
-                                 hipStream_t stream) {
+                                 unsigned* status, hipStream_t stream) {
   if (w_dtype == GPTQ_BF16)
     hipLaunchKernelGGL((k_rowprep<uint16_t, ASYM>), dim3(out), dim3(256), 0, stream, (const uint16_t*)W, ld_w, in,
-                       perm, dead, qmax, group, Wq, scale_row, zero_row, scales, zeros, row_loss);
+                       perm, dead, qmax, group, Wq, scale_row, zero_row, scales, zeros, row_loss, status);
   else
     hipLaunchKernelGGL((k_rowprep<float, ASYM>), dim3(out), dim3(256), 0, stream, (const float*)W, ld_w, in, perm,
-                       dead, qmax, group, Wq, scale_row, zero_row, scales, zeros, row_loss);
+                       dead, qmax, group, Wq, scale_row, zero_row, scales, zeros, row_loss, status);
   return hipGetLastError();
 }
 
@@ -423,7 +421,7 @@ static hipError_t launch_panel(bool inpanel, dim3 grid, double* Wq, int out, int
 hipError_t quantize_launch(const void* W, int w_dtype, int64_t out64, int64_t in64, int64_t ld_w, const double* U,
                            const int32_t* perm, const uint8_t* dead, int bits, int group, int grid, int8_t* codes,
                            float* scales, int32_t* zeros, int32_t* g_idx, double* row_loss, void* ws,
-                           hipStream_t stream) {
+                           hipStream_t stream, unsigned* host_status) {
   const int out = (int)out64, in = (int)in64;
   const bool asym = (grid == GPTQ_GRID_ASYMMETRIC);
   char* w = reinterpret_cast<char*>(ws);
@@ -434,6 +432,8 @@ hipError_t quantize_launch(const void* W, int w_dtype, int64_t out64, int64_t in
   double* scale_row = reinterpret_cast<double*>(w);
   w += align_up((size_t)out * sizeof(double), 256);
   double* zero_row = reinterpret_cast<double*>(w);
+  w += align_up((size_t)out * sizeof(double), 256);
+  unsigned* status = reinterpret_cast<unsigned*>(w);
   // largest code: qmax of the symmetric grid, or the top level 2^b - 1 of the asymmetric one
   const double qmax = asym ? (double)((1 << bits) - 1) : (double)((1 << (bits - 1)) - 1);
   const int n_groups = group ? (int)ceil_div(in, group) : 1;
@@ -442,10 +442,13 @@ hipError_t quantize_launch(const void* W, int w_dtype, int64_t out64, int64_t in
   // to one panel per outer block (every later column updated after every panel)
   const int ob = (group > PW && OB % group != 0 && group % OB != 0) ? PW : OB;
 
-  hipError_t e = asym ? launch_rowprep<true>(W, w_dtype, out, in, ld_w, perm, dead, qmax, group, Wq, scale_row,
-                                             zero_row, scales, zeros, row_loss, stream)
-                      : launch_rowprep<false>(W, w_dtype, out, in, ld_w, perm, dead, qmax, group, Wq, scale_row,
-                                              zero_row, scales, zeros, row_loss, stream);
+  hipLaunchKernelGGL(k_clear_status, dim3(1), dim3(1), 0, stream, status);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = asym ? launch_rowprep<true>(W, w_dtype, out, in, ld_w, perm, dead, qmax, group, Wq, scale_row, zero_row,
+                                  scales, zeros, row_loss, status, stream)
+           : launch_rowprep<false>(W, w_dtype, out, in, ld_w, perm, dead, qmax, group, Wq, scale_row, zero_row,
+                                   scales, zeros, row_loss, status, stream);
   if (e != hipSuccess) return e;
 
   const dim3 pgrid((unsigned)ceil_div(out, 16));
@@ -487,8 +490,12 @@ hipError_t quantize_launch(const void* W, int w_dtype, int64_t out64, int64_t in
   if (g_idx) {
     hipLaunchKernelGGL(k_gidx, dim3((unsigned)ceil_div(in, 256)), dim3(256), 0, stream, perm, in, group, g_idx);
     e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-  return e;
+  // the row-prep pass flagged non-finite live weights: one read of the status word at the end
+  e = hipMemcpyAsync(host_status, status, sizeof(unsigned), hipMemcpyDeviceToHost, stream);
+  if (e != hipSuccess) return e;
+  return hipStreamSynchronize(stream);
 }
 
 }  // namespace gptq

@@ -6,6 +6,7 @@ Defaults follow the GPTQ guide's gptq() signature (herodthegreater.github.io/pig
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 from dataclasses import dataclass
 
@@ -35,6 +36,17 @@ def _stream(stream) -> int:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def _on(stream):
+    """Context in which torch allocates for `stream`: the caching allocator then hands a freed block
+    (a workspace dropped at return while the library's kernels may still run) only to later work on
+    that same stream, which the stream orders after those kernels. None = the current stream."""
+    if stream is None:
+        return contextlib.nullcontext()
+    if not isinstance(stream, torch.cuda.Stream):
+        stream = torch.cuda.ExternalStream(int(stream))
+    return torch.cuda.stream(stream)
+
+
 def _req_cuda(t: torch.Tensor, name: str) -> None:
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
@@ -54,12 +66,16 @@ def _ld(t: torch.Tensor, name: str) -> int:
 
 
 class HessianState:
-    """Caller-owned running sums for streaming accumulation: S (lower triangle), colsq and n_total."""
+    """Caller-owned running sums for streaming accumulation: S (lower triangle), colsq and n_total.
 
-    def __init__(self, d_in: int, device="cuda"):
+    S and colsq start uninitialised: the first accumulate call (n_total == 0) writes them. Create the
+    state on (or under torch.cuda.stream of) the stream that will accumulate into it."""
+
+    def __init__(self, d_in: int, device="cuda", stream=None):
         self.d_in = d_in
-        self.S = torch.zeros((d_in, d_in), dtype=torch.float64, device=device)
-        self.colsq = torch.zeros(d_in, dtype=torch.float64, device=device)
+        with _on(stream):
+            self.S = torch.empty((d_in, d_in), dtype=torch.float64, device=device)
+            self.colsq = torch.empty(d_in, dtype=torch.float64, device=device)
         self.n_total = 0
         self._ws = None
 
@@ -81,7 +97,8 @@ def hessian_accumulate(X: torch.Tensor, state: HessianState, stream=None) -> Hes
     n_rows, d_in = X.shape
     if d_in != state.d_in:
         raise ValueError("X width does not match the state")
-    ws = state.workspace(n_rows, code)
+    with _on(stream):
+        ws = state.workspace(n_rows, code)
     n_total = ctypes.c_int64(state.n_total)
     st = _lib.load().gptq_hessian_accumulate(
         X.data_ptr(), code, n_rows, d_in, ld, state.S.data_ptr(), state.colsq.data_ptr(), ctypes.byref(n_total),
@@ -92,21 +109,22 @@ def hessian_accumulate(X: torch.Tensor, state: HessianState, stream=None) -> Hes
 
 
 def prepare_chol(S: torch.Tensor, colsq: torch.Tensor, n_total: int, damp: float = 0.01, act_order: bool = False,
-                 flags: int = GPTQ_FACTOR_INVERSE_RECHOL, stream=None, out=None):
+                 flags: int = GPTQ_FACTOR_REVERSED, stream=None, out=None):
     """Returns (U, perm, dead): U upper with U^T U = (P^T H P)^-1, perm int32, dead uint8."""
     _req_cuda(S, "S")
     d = S.shape[0]
     if S.shape != (d, d) or S.dtype != torch.float64 or not S.is_contiguous():
         raise ValueError("S must be a contiguous in x in float64 tensor")
     _contig(colsq, "colsq", torch.float64, (d,))
-    if out is None:
-        U = torch.empty((d, d), dtype=torch.float64, device=S.device)
-        perm = torch.empty(d, dtype=torch.int32, device=S.device)
-        dead = torch.empty(d, dtype=torch.uint8, device=S.device)
-    else:
-        U, perm, dead = out
     lib = _lib.load()
-    ws = torch.empty(max(lib.gptq_prepare_workspace_bytes(d), 1), dtype=torch.uint8, device=S.device)
+    with _on(stream):
+        if out is None:
+            U = torch.empty((d, d), dtype=torch.float64, device=S.device)
+            perm = torch.empty(d, dtype=torch.int32, device=S.device)
+            dead = torch.empty(d, dtype=torch.uint8, device=S.device)
+        else:
+            U, perm, dead = out
+        ws = torch.empty(max(lib.gptq_prepare_workspace_bytes(d), 1), dtype=torch.uint8, device=S.device)
     st = lib.gptq_prepare_chol(S.data_ptr(), colsq.data_ptr(), int(n_total), d, float(damp), int(bool(act_order)),
                                int(flags), U.data_ptr(), perm.data_ptr(), dead.data_ptr(), ws.data_ptr(), ws.numel(),
                                _stream(stream))
@@ -125,13 +143,6 @@ class QuantResult:
     U: torch.Tensor | None = None
     zeros: torch.Tensor | None = None  # int32, out x G (asymmetric grid only)
 
-    def dequantize(self) -> torch.Tensor:
-        g = self.g_idx.long()
-        c = self.codes.to(torch.float64)
-        if self.zeros is not None:
-            c = c - self.zeros.to(torch.float64)[:, g]
-        return c * self.scales.to(torch.float64)[:, g]
-
 
 def quantize_layer(W: torch.Tensor, U: torch.Tensor, perm: torch.Tensor, dead: torch.Tensor, bits: int = 4,
                    group: int | None = None, stream=None, ws: torch.Tensor | None = None,
@@ -147,15 +158,16 @@ def quantize_layer(W: torch.Tensor, U: torch.Tensor, perm: torch.Tensor, dead: t
     group = int(group or 0)
     n_groups = -(-d // group) if group else 1
     dev = W.device
-    codes = torch.empty((out, d), dtype=torch.int8, device=dev)
-    scales = torch.empty((out, n_groups), dtype=torch.float32, device=dev)
-    g_idx = torch.empty(d, dtype=torch.int32, device=dev)
-    row_loss = torch.empty(out, dtype=torch.float64, device=dev)
     lib = _lib.load()
     need = lib.gptq_quantize_workspace_bytes(out, d)
-    if ws is None or ws.numel() < need:
-        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    zeros = torch.empty((out, n_groups), dtype=torch.int32, device=dev) if asymmetric else None
+    with _on(stream):
+        codes = torch.empty((out, d), dtype=torch.int8, device=dev)
+        scales = torch.empty((out, n_groups), dtype=torch.float32, device=dev)
+        g_idx = torch.empty(d, dtype=torch.int32, device=dev)
+        row_loss = torch.empty(out, dtype=torch.float64, device=dev)
+        if ws is None or ws.numel() < need:
+            ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        zeros = torch.empty((out, n_groups), dtype=torch.int32, device=dev) if asymmetric else None
     grid = _lib.GPTQ_GRID_ASYMMETRIC if asymmetric else _lib.GPTQ_GRID_SYMMETRIC
     st = lib.gptq_quantize_layer_ex(W.data_ptr(), _dtype_code(W), out, d, ld, U.data_ptr(), perm.data_ptr(),
                                     dead.data_ptr(), int(bits), group, grid, codes.data_ptr(), scales.data_ptr(),
@@ -177,7 +189,8 @@ def pack_codes(codes: torch.Tensor, bits: int, asymmetric: bool = False, stream=
     wpr = lib.gptq_packed_words_per_row(d, int(bits))
     if wpr <= 0:
         raise ValueError("bad in/bits")
-    packed = torch.empty((out, wpr), dtype=torch.int32, device=codes.device)
+    with _on(stream):
+        packed = torch.empty((out, wpr), dtype=torch.int32, device=codes.device)
     grid = _lib.GPTQ_GRID_ASYMMETRIC if asymmetric else _lib.GPTQ_GRID_SYMMETRIC
     check(lib.gptq_pack_codes(codes.data_ptr(), out, d, int(bits), grid, packed.data_ptr(), _stream(stream)),
           "gptq_pack_codes")
@@ -205,7 +218,8 @@ def dequant_matmul(X: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, 
     wpr = lib.gptq_packed_words_per_row(d, int(bits))
     _contig(packed, "packed", torch.int32, (n_out, wpr))
     if out is None:
-        out = torch.empty((n, n_out), dtype=torch.float32, device=X.device)
+        with _on(stream):
+            out = torch.empty((n, n_out), dtype=torch.float32, device=X.device)
     else:
         _contig(out, "out", torch.float32, (n, n_out))
     grid = _lib.GPTQ_GRID_ASYMMETRIC if zeros is not None else _lib.GPTQ_GRID_SYMMETRIC
@@ -218,10 +232,11 @@ def dequant_matmul(X: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, 
 
 
 def gptq_quantize(W: torch.Tensor, X: torch.Tensor, bits: int = 4, group: int | None = None, damp: float = 0.01,
-                  act_order: bool = False, flags: int = GPTQ_FACTOR_INVERSE_RECHOL, stream=None,
+                  act_order: bool = False, flags: int = GPTQ_FACTOR_REVERSED, stream=None,
                   asymmetric: bool = False) -> QuantResult:
-    """The whole per-layer path: accumulate the Hessian over X, prepare U, quantize W."""
-    state = HessianState(W.shape[1], device=W.device)
+    """The whole per-layer path: accumulate the Hessian over X, prepare U, quantize W. Every kernel and
+    every allocation is on `stream` (None = the current stream)."""
+    state = HessianState(W.shape[1], device=W.device, stream=stream)
     hessian_accumulate(X, state, stream)
     U, perm, dead = prepare_chol(state.S, state.colsq, state.n_total, damp, act_order, flags, stream)
     return quantize_layer(W, U, perm, dead, bits, group, stream, asymmetric=asymmetric)

@@ -31,6 +31,14 @@ def dev64(a: np.ndarray, device="cuda") -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(a)).to(device)
 
 
+def dequantized(res_gpu) -> np.ndarray:
+    """Q of a GPU result (QuantResult), formed on the host in fp64 from its codes, scales (zeros) and
+    g_idx with the oracle's dequantize."""
+    codes = res_gpu.codes.cpu().numpy().astype(np.int64)
+    zeros = None if res_gpu.zeros is None else res_gpu.zeros.cpu().numpy()
+    return O.dequantize(codes, res_gpu.scales.cpu().numpy(), res_gpu.g_idx.cpu().numpy(), zeros)
+
+
 def codes_in_quant_order(codes: np.ndarray, perm: np.ndarray) -> np.ndarray:
     return codes[:, perm]
 

@@ -84,14 +84,14 @@ def test_fullsize_hessian_sampled(name):
 def _oracle_u_from_rows(cfg, rows, act_order):
     X = _x(cfg.name)
     S, colsq, n = O.hessian_from_x(O.to_f64(X[:rows], cfg.dtype))
-    S = 0.5 * (S + S.T)
-    colsq = np.diag(S).copy()
     H_p, perm, dead, lam = O.prepare(S, colsq, n, cfg.damp, act_order)
     U = O.upper_factor_of_inverse(H_p)
     return S, colsq, n, H_p, perm, dead, U
 
 
-@pytest.mark.parametrize("name,rows,flags", [("q_proj", 8192, 0), ("q_proj", 8192, 1), ("down", 16384, 1)])
+@pytest.mark.parametrize("name,rows,flags", [("q_proj", 8192, G.GPTQ_FACTOR_INVERSE_RECHOL),
+                                             ("q_proj", 8192, G.GPTQ_FACTOR_REVERSED),
+                                             ("down", 16384, G.GPTQ_FACTOR_REVERSED)])
 def test_fullsize_prepare_and_quantize_given_oracle_s(name, rows, flags):
     cfg = syn.config_by_name(name)
     print(f"[fullsize] prepare+quantize {name} rows={rows} flags={flags}", flush=True)
