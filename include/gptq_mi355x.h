@@ -206,6 +206,24 @@ int gptq_dequant_matmul(const void* X, int x_dtype, int64_t n, int64_t in, int64
                         const int32_t* g_idx, int64_t out, int bits, int grid, int group,
                         const float* bias, int relu, float* Y, int64_t ld_y, void* stream);
 
+/* ---------------------------------------------------------------------------------------------------
+ * 1'. gptq_hessian_accumulate without a workspace argument, for callers that cannot allocate device
+ *    memory: code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ *  Arguments, layouts, results and errors are those of gptq_hessian_accumulate, without ws / ws_bytes.
+ *  Its scratch (the per-slice partial sums) is a static 80 MiB device array inside the library, one copy
+ *  per GPU, held from the first call on that GPU until the process ends; the call allocates nothing
+ *  (no hipMalloc, no allocating library routine). To fit it the rows may be cut into fewer slices than
+ *  gptq_hessian_accumulate uses, so S can differ from that call's in fp32 rounding (bf16: in <= 4096 runs
+ *  with two slices at most). A size whose single slice does not fit (bf16 in > 6144, fp32 in > 6400)
+ *  returns GPTQ_ERR_UNSUPPORTED without launching anything.
+ *  Every call on one GPU shares that GPU's array: calls that overlap in time on one GPU (different
+ *  streams or host threads of one process) race and give wrong results. Calls ordered on
+ *  one stream are safe; nothing in the array needs clearing between calls.
+ * ------------------------------------------------------------------------------------------------- */
+int gptq_hessian_accumulate_noalloc(const void* X, int x_dtype, int64_t n_rows, int64_t in, int64_t ld_x,
+                                    double* S, double* colsq, int64_t* n_total, void* stream);
+
 /* Human-readable name of a gptq_status value (static storage). */
 const char* gptq_status_string(int status);
 

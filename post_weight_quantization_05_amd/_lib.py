@@ -43,6 +43,8 @@ SIGNATURES = {
     "gptq_quantize_layer_ex": (ctypes.c_int, [_vp, ctypes.c_int, _c_int64, _c_int64, _c_int64, _vp, _vp, _vp,
                                               ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _vp, _vp,
                                               _vp, ctypes.c_size_t, _vp]),
+    "gptq_hessian_accumulate_noalloc": (ctypes.c_int, [_vp, ctypes.c_int, _c_int64, _c_int64, _c_int64, _vp, _vp,
+                                                       ctypes.POINTER(_c_int64), _vp]),
     "gptq_packed_words_per_row": (_c_int64, [_c_int64, ctypes.c_int]),
     "gptq_pack_codes": (ctypes.c_int, [_vp, _c_int64, _c_int64, ctypes.c_int, ctypes.c_int, _vp, _vp]),
     "gptq_dequant_matmul": (ctypes.c_int, [_vp, ctypes.c_int, _c_int64, _c_int64, _c_int64, _vp, _vp, _vp, _vp,

@@ -38,7 +38,9 @@ struct HessianPlan {
   int64_t rows_per_split;
   size_t part_bytes, colsq_part_bytes, total_bytes;
 };
-HessianPlan hessian_plan(int64_t n_rows, int64_t in, int dtype);
+// max_bytes != 0: use no more row slices than keep total_bytes within max_bytes (one slice at least;
+// the caller checks total_bytes)
+HessianPlan hessian_plan(int64_t n_rows, int64_t in, int dtype, size_t max_bytes = 0);
 // first: S's lower triangle and colsq are written (not added to): the first chunk of a stream
 hipError_t hessian_launch(const HessianPlan& p, const void* X, double* S, double* colsq, void* ws,
                           hipStream_t stream, bool first);

@@ -771,7 +771,7 @@ __global__ __launch_bounds__(256, 1) void k_xtx_f32(const float* __restrict__ X,
 
 }  // namespace
 
-HessianPlan hessian_plan(int64_t n_rows, int64_t in, int dtype) {
+HessianPlan hessian_plan(int64_t n_rows, int64_t in, int dtype, size_t max_bytes) {
   HessianPlan p{};
   p.n_rows = n_rows;
   p.in = in;
@@ -783,7 +783,11 @@ HessianPlan hessian_plan(int64_t n_rows, int64_t in, int dtype) {
   // Row slices: balance tiles x slices over the CUs (one resident workgroup per CU), keep each slice at
   // least 1024 rows, and charge a little for every extra slice (its fp32 partial is re-read once).
   const int cus = 256;  // planning constant (MI355X); the launch itself works for any CU count
-  const int64_t max_splits = std::max<int64_t>(1, std::min<int64_t>(64, n_rows / 1024));
+  int64_t max_splits = std::max<int64_t>(1, std::min<int64_t>(64, n_rows / 1024));
+  if (max_bytes) {  // fewer slices when the partials must fit a fixed buffer (at least one slice)
+    const size_t per_split = (size_t)p.n_tiles * p.tile * p.tile * sizeof(float) + (size_t)p.n_tb * p.tile * sizeof(double);
+    max_splits = std::max<int64_t>(1, std::min<int64_t>(max_splits, (int64_t)(max_bytes / (per_split + 512))));
+  }
   double best = 1e30;
   int best_s = 1;
   for (int s = 1; s <= max_splits; ++s) {
