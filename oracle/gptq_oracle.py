@@ -31,9 +31,10 @@ definition directly.
      ([guide] "Simplifications"; [handbook] quantize_weight, dequantize_weight, gptq_quantize_row)
   9. storage and use: packed codes, Q from codes and grid parameters, the layer-wise driver
      ([guide] "When it breaks", "How it works" apply_layerwise; [handbook] int4 storage)
- 10. the noise floor: the oracle re-run with its Hessian summed in fp32 within each 2048-row segment,
-     and with U rounded to fp32, measured against itself (how far an fp32-accumulated Hessian alone
-     moves the result; the calibration set is 128 segments of 2048 tokens, [guide] "How it works").
+ 10. the noise floor: the oracle re-run with its Hessian summed in fp32 (per 2048-row segment by a BLAS
+     product, or as plain sequential fp32 chains), and with U rounded to fp32, measured against itself
+     (how far an fp32-accumulated Hessian alone moves the result; the calibration set is 128 segments of
+     2048 tokens, [guide] "How it works").
 
 Readings where the pages leave a detail open (each is also listed with the build's design notes):
   * qmax for b bits is 2^(b-1) - 1 (the lesson's starter code; "2-bit" = ternary {-s, 0, s} in the guide).
@@ -52,8 +53,10 @@ Readings where the pages leave a detail open (each is also listed with the build
   * Packed layout (the pages fix none): per row a little-endian bit stream of b-bit codes in 32-bit
     words, symmetric codes offset by 2^(b-1). The driver's F is float32; an MLP layer is affine + ReLU
     (no ReLU on the output layer); layer outputs are the exact values rounded once to fp32.
-  * Noise floor: "fp32 accumulation" is read as one single-precision BLAS product per 2048-row segment
-    (the order of its sums is the library's), the segments then summed in fp64; colsq stays fp64.
+  * Noise floor: "fp32 accumulation" is modelled two ways. (a) One single-precision BLAS product per
+    2048-row segment (the order of its sums is the library's), segments summed in fp64. (b) The plainest
+    form: a sequential fp32 running sum over a chain of rows, taking 16 rows at a time with one rounding
+    per step, chains summed in fp64. colsq stays fp64 in both.
 """
 from __future__ import annotations
 
@@ -111,6 +114,46 @@ def accumulate_fp32_segments(S: np.ndarray, colsq: np.ndarray, X64: np.ndarray,
             raise ValueError("inputs are not fp32-representable")
         S += (b32.T @ b32).astype(np.float64)
         colsq += np.einsum("ki,ki->i", blk, blk)
+    return n
+
+
+def fp32_chain_block(XI: np.ndarray, XJ: np.ndarray, chain_rows: int = 4096, group_rows: int = 16) -> np.ndarray:
+    """One block XI^T XJ under the plainest fp32 accumulation (the second noise-floor model): within each
+    chain of `chain_rows` rows, an fp32 running sum takes one group of `group_rows` rows at a time, each
+    step rounded to fp32 (the running value plus the group's sum of products, formed in fp64, where the
+    products of fp32-representable inputs and their short sums are exact); the chains' sums are added in
+    fp64. XI, XJ: the same rows, fp32-representable values widened to fp64."""
+    out = np.zeros((XI.shape[1], XJ.shape[1]))
+    step = np.empty_like(out)
+    run = np.empty(out.shape, dtype=np.float32)
+    for c0 in range(0, XI.shape[0], chain_rows):
+        run.fill(0.0)
+        for g0 in range(c0, min(XI.shape[0], c0 + chain_rows), group_rows):
+            np.matmul(XI[g0:g0 + group_rows].T, XJ[g0:g0 + group_rows], out=step)
+            np.add(step, run, out=step)
+            np.copyto(run, step, casting="same_kind")
+        out += run
+    return out
+
+
+def accumulate_fp32_chains(S: np.ndarray, colsq: np.ndarray, X64: np.ndarray, chain_rows: int = 4096,
+                           group_rows: int = 16, tile: int = 256) -> int:
+    """S (lower triangle) += X^T X under fp32_chain_block, tile by tile (the tiling only keeps a tile of
+    the running sum in cache; every entry sees the same operations). colsq += column sums of squares in
+    fp64. The inputs must be fp32-representable. The strictly upper triangle of S is left as it was."""
+    n, d = X64.shape
+    if not np.array_equal(X64.astype(np.float32).astype(np.float64), X64):
+        raise ValueError("inputs are not fp32-representable")
+    for i0 in range(0, d, tile):
+        for j0 in range(0, i0 + 1, tile):
+            blk = fp32_chain_block(X64[:, i0:i0 + tile], X64[:, j0:j0 + tile], chain_rows, group_rows)
+            dst = S[i0:i0 + tile, j0:j0 + tile]
+            if i0 == j0:
+                low = np.tril(np.ones(blk.shape, dtype=bool))
+                dst[low] += blk[low]
+            else:
+                dst += blk
+    colsq += np.einsum("ki,ki->i", X64, X64)
     return n
 
 
@@ -633,12 +676,12 @@ def apply_layerwise(weights, biases, X64: np.ndarray, quantize, skip_last: bool 
 def output_error(W64: np.ndarray, Q: np.ndarray, S: np.ndarray) -> float:
     """||X (W - Q)^T||_F^2 through the Gram matrix S = X^T X (no n x out product needed)."""
     D = np.asarray(W64, dtype=np.float64) - Q
-    return float(np.einsum("ri,ij,rj->", D, S, D))
+    return float(np.sum((D @ S) * D))
 
 
 def relative_output_error(W64: np.ndarray, Q: np.ndarray, S: np.ndarray) -> float:
     W64 = np.asarray(W64, dtype=np.float64)
-    return output_error(W64, Q, S) / float(np.einsum("ri,ij,rj->", W64, S, W64))
+    return output_error(W64, Q, S) / float(np.sum((W64 @ S) * W64))
 
 
 # ---------------------------------------------------------------------------------------------

@@ -34,8 +34,9 @@ struct HessianPlan {
   int tile;        // square output tile (256)
   int n_tb;        // tile blocks per side = ceil(in / tile)
   int n_tiles;     // lower-triangle tiles = n_tb (n_tb + 1) / 2
-  int splits;      // row slices (split-K)
+  int splits;      // row slices (split-K) of one launch
   int64_t rows_per_split;
+  int64_t chunk_rows;  // rows per launch (splits * rows_per_split at most); longer inputs take several
   size_t part_bytes, colsq_part_bytes, total_bytes;
 };
 // max_bytes != 0: use no more row slices than keep total_bytes within max_bytes (one slice at least;

@@ -771,6 +771,16 @@ __global__ __launch_bounds__(256, 1) void k_xtx_f32(const float* __restrict__ X,
 
 }  // namespace
 
+// Rows of X that one fp32 partial sum may cover: every (slice, tile) item sums at most this many rows on
+// the matrix cores before its partial goes to the fp64 combine. Longer fp32 sums move S by enough to flip
+// near-tie codes of sensitive layers (3-bit, groups, act_order at in = 11008).
+#ifndef GPTQ_XTX_SLICE_ROWS
+#define GPTQ_XTX_SLICE_ROWS 4096
+#endif
+constexpr int64_t SLICE_ROWS = GPTQ_XTX_SLICE_ROWS;
+static_assert(SLICE_ROWS % BK == 0 && SLICE_ROWS % FK == 0 && SLICE_ROWS >= 1024, "slice length");
+constexpr int MAX_SPLITS = 64;  // slices per launch; longer inputs are processed in chunks
+
 HessianPlan hessian_plan(int64_t n_rows, int64_t in, int dtype, size_t max_bytes) {
   HessianPlan p{};
   p.n_rows = n_rows;
@@ -780,30 +790,30 @@ HessianPlan hessian_plan(int64_t n_rows, int64_t in, int dtype, size_t max_bytes
   const int kstep = (dtype == GPTQ_BF16) ? BK : FK;
   p.n_tb = (int)ceil_div(in, p.tile);
   p.n_tiles = p.n_tb * (p.n_tb + 1) / 2;
-  // Row slices: balance tiles x slices over the CUs (one resident workgroup per CU), keep each slice at
-  // least 1024 rows, and charge a little for every extra slice (its fp32 partial is re-read once).
+  const size_t per_split = (size_t)p.n_tiles * p.tile * p.tile * sizeof(float) + (size_t)p.n_tb * p.tile * sizeof(double);
+  // Rows per launch: at most MAX_SPLITS slices of SLICE_ROWS (fewer when the partials must fit max_bytes)
+  int64_t cap = MAX_SPLITS;
+  if (max_bytes) cap = std::max<int64_t>(1, std::min<int64_t>(cap, (int64_t)(max_bytes / (per_split + 512))));
+  p.chunk_rows = std::min<int64_t>(n_rows, cap * SLICE_ROWS);
+  // Slices of one chunk: enough that none covers more than SLICE_ROWS rows; beyond that, balance
+  // tiles x slices over the CUs (one resident workgroup per CU), keep slices at least 1024 rows long,
+  // and charge a little for every extra slice (its fp32 partial is written and read once).
   const int cus = 256;  // planning constant (MI355X); the launch itself works for any CU count
-  int64_t max_splits = std::max<int64_t>(1, std::min<int64_t>(64, n_rows / 1024));
-  if (max_bytes) {  // fewer slices when the partials must fit a fixed buffer (at least one slice)
-    const size_t per_split = (size_t)p.n_tiles * p.tile * p.tile * sizeof(float) + (size_t)p.n_tb * p.tile * sizeof(double);
-    max_splits = std::max<int64_t>(1, std::min<int64_t>(max_splits, (int64_t)(max_bytes / (per_split + 512))));
-  }
+  const int64_t s_min = ceil_div(p.chunk_rows, SLICE_ROWS);
+  const int64_t s_max = std::max<int64_t>(s_min, std::min<int64_t>(cap, p.chunk_rows / 1024));
   double best = 1e30;
-  int best_s = 1;
-  for (int s = 1; s <= max_splits; ++s) {
+  int best_s = (int)s_min;
+  for (int64_t s = s_min; s <= s_max; ++s) {
     const double rounds = (double)ceil_div((int64_t)p.n_tiles * s, cus);
     const double cost = rounds / s + 0.004 * s;
     if (cost < best - 1e-12) {
       best = cost;
-      best_s = s;
+      best_s = (int)s;
     }
   }
-#ifdef GPTQ_XTX_SPLITS
-  best_s = (int)std::min<int64_t>(GPTQ_XTX_SPLITS, max_splits);
-#endif
   p.splits = best_s;
-  p.rows_per_split = ceil_div(ceil_div(n_rows, p.splits), kstep) * kstep;
-  p.splits = (int)ceil_div(n_rows, p.rows_per_split);
+  p.rows_per_split = ceil_div(ceil_div(p.chunk_rows, p.splits), kstep) * kstep;
+  p.splits = (int)ceil_div(p.chunk_rows, p.rows_per_split);
   p.part_bytes = align_up((size_t)p.splits * p.n_tiles * p.tile * p.tile * sizeof(float), 256);
   p.colsq_part_bytes = align_up((size_t)p.splits * p.n_tb * p.tile * sizeof(double), 256);
   p.total_bytes = p.part_bytes + p.colsq_part_bytes;
@@ -811,40 +821,55 @@ HessianPlan hessian_plan(int64_t n_rows, int64_t in, int dtype, size_t max_bytes
   return p;
 }
 
-hipError_t hessian_launch(const HessianPlan& p, const void* X, double* S, double* colsq, void* ws,
-                          hipStream_t stream, bool first) {
+// One chunk of at most p.chunk_rows rows: the accumulation kernel (p.splits slices or fewer) and the
+// fp64 combine into S / colsq.
+static hipError_t hessian_chunk(const HessianPlan& p, const void* X, int64_t n_rows, double* S, double* colsq,
+                                void* ws, hipStream_t stream, bool first) {
   float* part = reinterpret_cast<float*>(ws);
   double* cpart = reinterpret_cast<double*>(reinterpret_cast<char*>(ws) + p.part_bytes);
-  const int grid = p.splits * p.n_tiles;
+  const int splits = (int)ceil_div(n_rows, p.rows_per_split);
+  const int grid = splits * p.n_tiles;
   const int remap = (grid % 8 == 0) ? 1 : 0;
   const int cs = (p.n_tiles + 7) / 8;         // tiles per XCD for the direct-to-LDS kernel
-  const int grid_dma = 8 * cs * p.splits;
+  const int grid_dma = 8 * cs * splits;
   const int cstride = p.n_tb * p.tile;
   if (p.dtype == GPTQ_BF16) {
     const bool vec = (p.ld % 8 == 0) && (p.in % 8 == 0) && ((reinterpret_cast<uintptr_t>(X) & 15) == 0);
     const bool dma = vec && (p.rows_per_split * p.ld * 2 < ((int64_t)1 << 31));
     if (dma)
       hipLaunchKernelGGL(k_xtx_bf16_dma, dim3(grid_dma), dim3(XWAVES * 64), 0, stream, (const uint16_t*)X, p.ld,
-                         p.n_rows, (int)p.in, p.n_tiles, p.rows_per_split, cs, p.splits, part, cpart, cstride);
+                         n_rows, (int)p.in, p.n_tiles, p.rows_per_split, cs, splits, part, cpart, cstride);
     else if (vec)
-      hipLaunchKernelGGL(k_xtx_bf16<true>, dim3(grid), dim3(256), 0, stream, (const uint16_t*)X, p.ld, p.n_rows,
-                         (int)p.in, p.n_tiles, p.rows_per_split, remap, p.splits, part, cpart, cstride);
+      hipLaunchKernelGGL(k_xtx_bf16<true>, dim3(grid), dim3(256), 0, stream, (const uint16_t*)X, p.ld, n_rows,
+                         (int)p.in, p.n_tiles, p.rows_per_split, remap, splits, part, cpart, cstride);
     else
-      hipLaunchKernelGGL(k_xtx_bf16<false>, dim3(grid), dim3(256), 0, stream, (const uint16_t*)X, p.ld, p.n_rows,
-                         (int)p.in, p.n_tiles, p.rows_per_split, remap, p.splits, part, cpart, cstride);
+      hipLaunchKernelGGL(k_xtx_bf16<false>, dim3(grid), dim3(256), 0, stream, (const uint16_t*)X, p.ld, n_rows,
+                         (int)p.in, p.n_tiles, p.rows_per_split, remap, splits, part, cpart, cstride);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_xtx_reduce<BT>, dim3((unsigned)(p.n_tiles * (BT / FIN_RC))), dim3(256), 0, stream, part,
-                       cpart, cstride, p.n_tiles, p.splits, (int)p.in, S, colsq, first ? 1 : 0);
+                       cpart, cstride, p.n_tiles, splits, (int)p.in, S, colsq, first ? 1 : 0);
   } else {
-    hipLaunchKernelGGL(k_xtx_f32, dim3(grid), dim3(256), 0, stream, (const float*)X, p.ld, p.n_rows, (int)p.in,
-                       p.n_tiles, p.rows_per_split, remap, p.splits, part, cpart, cstride);
+    hipLaunchKernelGGL(k_xtx_f32, dim3(grid), dim3(256), 0, stream, (const float*)X, p.ld, n_rows, (int)p.in,
+                       p.n_tiles, p.rows_per_split, remap, splits, part, cpart, cstride);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_xtx_reduce<FT>, dim3((unsigned)(p.n_tiles * (FT / FIN_RC))), dim3(256), 0, stream, part,
-                       cpart, cstride, p.n_tiles, p.splits, (int)p.in, S, colsq, first ? 1 : 0);
+                       cpart, cstride, p.n_tiles, splits, (int)p.in, S, colsq, first ? 1 : 0);
   }
   return hipGetLastError();
+}
+
+hipError_t hessian_launch(const HessianPlan& p, const void* X, double* S, double* colsq, void* ws,
+                          hipStream_t stream, bool first) {
+  const size_t esz = (p.dtype == GPTQ_BF16) ? 2 : 4;
+  for (int64_t r0 = 0; r0 < p.n_rows; r0 += p.chunk_rows) {
+    const void* Xc = reinterpret_cast<const char*>(X) + (size_t)r0 * (size_t)p.ld * esz;
+    const hipError_t e =
+        hessian_chunk(p, Xc, std::min(p.chunk_rows, p.n_rows - r0), S, colsq, ws, stream, first && r0 == 0);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace gptq

@@ -59,6 +59,51 @@ def test_hessian_matches_oracle(cfg):
     assert st.n_total == n_ref
 
 
+def _plan_rows_per_slice(n, d):
+    """Rows per fp32 slice the library plans for a bf16 accumulation of n rows, from its workspace size
+    (fp32 256 x 256 partials of every lower tile plus fp64 column sums, per slice)."""
+    tb = -(-d // 256)
+    per_slice = tb * (tb + 1) // 2 * 256 * 256 * 4 + tb * 256 * 8
+    slices = round(G.load().gptq_hessian_workspace_bytes(n, d, G.GPTQ_BF16) / per_slice)
+    return -(-(-(-n // slices)) // 32) * 32
+
+
+@pytest.mark.parametrize("kind,n,d", [("normal", 4096, 256), ("relu", 9000, 512), ("outliers", 20000, 768)])
+def test_hessian_arithmetic_is_the_fp32_chain_model(kind, n, d):
+    """The Hessian kernel's S against the oracle's model of fp32 matrix-core accumulation with the same
+    slices: per slice a sequential fp32 running sum, 8 rows (products) per rounding step, slices added in
+    fp64. Most entries must be bit-equal, the model must account for most of the kernel's deviation from
+    the exact S, and every entry must lie within the sequential rounding bound of both."""
+    cfg = syn.custom_config(f"chain_{kind}", 4, d, n, dtype="bf16", w_std=0.02,
+                            x_kind="relu" if kind == "relu" else "normal", outlier_channels=5 if kind != "normal" else 0,
+                            lognormal_magnitudes=kind == "relu", w_seed=61, x_seed=62)
+    X = syn.gen_x(cfg)
+    st = G.HessianState(d)
+    G.hessian_accumulate(to_device(X, "bf16"), st)
+    torch.cuda.synchronize()
+    S = st.S.cpu().numpy()
+    X64 = O.to_f64(X, "bf16")
+    rps = _plan_rows_per_slice(n, d)
+    Sm, c = np.zeros((d, d)), np.zeros(d)
+    O.accumulate_fp32_chains(Sm, c, X64, chain_rows=rps, group_rows=8)
+    low = np.tril_indices(d)
+    A = (np.abs(X64).T @ np.abs(X64))[low]  # sum |x_i x_j|: the running sums' magnitude bound
+    S64 = (X64.T @ X64)[low]
+    equal = float(np.mean(S[low] == Sm[low]))
+    dev = float(np.max(np.abs(S[low] - Sm[low]) / A))
+    explained = float(np.sum(np.abs(S[low] - Sm[low])) / np.sum(np.abs(S[low] - S64)))
+    print(f"[hessian-model] {kind}: {equal * 100:.2f}% of entries bit-equal, max |dS| / sum|x x| {dev:.2e}, "
+          f"sum |GPU - model| / sum |GPU - exact| {explained:.3f}", flush=True)
+    # wide exponent ranges inside an 8-product group (outlier channels) make the hardware's inner sum
+    # inexact now and then, so fewer entries match bit for bit there
+    assert equal >= 0.5
+    assert explained <= 0.5  # the model accounts for most of the kernel's deviation from the exact S
+    # both lie within u * (steps per slice) * sum|x x| of the exact S (one rounding of at most u times the
+    # running sum per step), so they are within twice that of each other
+    assert dev <= 2 * (rps // 8) * 2.0 ** -24
+    assert np.array_equal(st.colsq.cpu().numpy() == 0, c == 0)
+
+
 def test_hessian_streaming_determinism_and_strided_rows():
     cfg = HESS_CASES[2]
     W, X, W64, X64 = layer_inputs(cfg)

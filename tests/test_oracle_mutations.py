@@ -367,7 +367,24 @@ def _segments_factory(kind):
     return acc
 
 
+def _chain_factory(kind):
+    def block(XI, XJ, chain_rows=4096, group_rows=16):
+        out = np.zeros((XI.shape[1], XJ.shape[1]))
+        run = np.zeros(out.shape, dtype=np.float32)
+        for c0 in range(0, XI.shape[0], chain_rows):
+            if kind != "no_chain_reset":
+                run = np.zeros(out.shape, dtype=np.float32)
+            for g0 in range(c0, min(XI.shape[0], c0 + chain_rows), group_rows):
+                step = run.astype(np.float64) + XI[g0:g0 + group_rows].T @ XJ[g0:g0 + group_rows]
+                run = step if kind == "fp64_running_sum" else step.astype(np.float32)
+            out = run.astype(np.float64) if kind == "no_chain_reset" else out + run
+        return out
+    return block
+
+
 PINS_INPUTS = [
+    (P.test_fp32_chain_model_equals_scalar_loop_and_is_exact_on_integers, ()),
+    (P.test_fp32_chain_model_error_is_within_the_sequential_bound, ()),
     (P.test_bf16_decoding_matches_torch_for_every_pattern, ()),
     (P.test_fp32_segment_hessian_is_exact_on_integer_data, ()),
     (P.test_fp32_segment_hessian_error_is_fp32_sized, ()),
@@ -378,6 +395,8 @@ MUTATIONS_INPUTS = [
     ("to_f64", _decode_factory, k) for k in ["low_half", "truncated_sign"]
 ] + [
     ("accumulate_fp32_segments", _segments_factory, k) for k in ["fp64_sums", "fp32_total"]
+] + [
+    ("fp32_chain_block", _chain_factory, k) for k in ["no_chain_reset", "fp64_running_sum"]
 ]
 
 

@@ -567,3 +567,51 @@ def test_noise_floor_is_zero_when_the_fp32_sums_are_exact():
     ref = O.gptq_oracle(W, X, bits=3, group=8, act_order=True)
     assert np.array_equal(fl["ref"]["codes"], ref["codes"])
     assert fl["fp32_U"]["f"] <= 0.01
+
+
+def test_fp32_chain_model_equals_scalar_loop_and_is_exact_on_integers():
+    """The plain fp32 accumulation model against a brute-force loop of numpy float32 scalars: per chain,
+    run = float32(run + exact sum of the group's 16 products), chains summed in fp64. Bitwise on a tiny
+    block with ragged chains and groups; exact on integer data (no rounding happens at all)."""
+    rng = np.random.default_rng(37)
+    X = rng.standard_normal((101, 3)).astype(np.float32).astype(np.float64)
+    got = O.fp32_chain_block(X, X, chain_rows=48, group_rows=16)
+    want = np.zeros((3, 3))
+    for i in range(3):
+        for j in range(3):
+            total = 0.0
+            for c0 in range(0, 101, 48):
+                run = np.float32(0.0)
+                for g0 in range(c0, min(101, c0 + 48), 16):
+                    exact = sum(Fraction(float(X[k, i])) * Fraction(float(X[k, j])) for k in range(g0, min(101, c0 + 48, g0 + 16)))
+                    run = np.float32(float(Fraction(float(run)) + exact))  # one rounding of the exact step
+                total += float(run)
+            want[i, j] = total
+    assert np.array_equal(got, want)
+    Xi = rng.integers(-9, 10, size=(3000, 20)).astype(np.float64)
+    S64, c64, _ = O.hessian_from_x(Xi)
+    S, c = np.zeros((20, 20)), np.zeros(20)
+    O.accumulate_fp32_chains(S, c, Xi, chain_rows=1024, tile=8)
+    low = np.tril_indices(20)
+    assert np.array_equal(S[low], S64[low]) and np.array_equal(c, c64)
+    assert np.all(S[np.triu_indices(20, 1)] == 0.0)
+
+
+def test_fp32_chain_model_error_is_within_the_sequential_bound():
+    """Each step rounds once to fp32, so |S_chain - S| <= u * sum over steps of |running value| (u = 2^-24,
+    plus the fp64 sums); on N(0,1) data the error is not zero and grows with the chain length."""
+    rng = np.random.default_rng(41)
+    X = rng.standard_normal((4096, 8)).astype(np.float32).astype(np.float64)
+    S64 = X.T @ X
+    errs = {}
+    for chain in (256, 4096):
+        Sc = O.fp32_chain_block(X, X, chain_rows=chain)
+        bound = np.zeros((8, 8))
+        for c0 in range(0, 4096, chain):
+            part = np.cumsum(np.einsum("ki,kj->kij", X[c0:c0 + chain], X[c0:c0 + chain]).reshape(-1, 16, 8, 8).sum(1), axis=0)
+            bound += np.abs(part).sum(0)
+        dS = np.abs(Sc - S64)
+        assert (dS <= 2.0 ** -24 * bound * (1 + 1e-6) + 1e-12).all()
+        assert dS.max() > 0
+        errs[chain] = np.median(dS / np.sqrt(np.outer(np.diag(S64), np.diag(S64))))
+    assert errs[4096] > errs[256]
