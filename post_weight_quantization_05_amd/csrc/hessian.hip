@@ -772,10 +772,13 @@ __global__ __launch_bounds__(256, 1) void k_xtx_f32(const float* __restrict__ X,
 }  // namespace
 
 // Rows of X that one fp32 partial sum may cover: every (slice, tile) item sums at most this many rows on
-// the matrix cores before its partial goes to the fp64 combine. Longer fp32 sums move S by enough to flip
-// near-tie codes of sensitive layers (3-bit, groups, act_order at in = 11008).
+// the matrix cores before its partial goes to the fp64 combine. The fp32 rounding error of S grows with
+// the square root of the chain length, and it decides how many near-tie codes of a sensitive layer flip
+// (3-bit, groups, act_order at in = 11008: 193 / 1135 / 556 of 2.8 M sampled codes with 4096 / 8192 /
+// ~12k-row slices, the spread being the cascades that follow a flip). Shorter slices cost partial-sum
+// traffic: q_proj's Hessian took 5.04 / 4.62 / 4.69 ms with a cap of 4096 / 8192 / 16384 rows.
 #ifndef GPTQ_XTX_SLICE_ROWS
-#define GPTQ_XTX_SLICE_ROWS 4096
+#define GPTQ_XTX_SLICE_ROWS 8192
 #endif
 constexpr int64_t SLICE_ROWS = GPTQ_XTX_SLICE_ROWS;
 static_assert(SLICE_ROWS % BK == 0 && SLICE_ROWS % FK == 0 && SLICE_ROWS >= 1024, "slice length");

@@ -31,6 +31,17 @@ def dev64(a: np.ndarray, device="cuda") -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(a)).to(device)
 
 
+def plan_rows_per_slice(n: int, d: int) -> int:
+    """Rows per fp32 slice the library plans for a bf16 Hessian accumulation of n rows (one launch), read
+    from its workspace size: fp32 256 x 256 partials of every lower tile plus fp64 column sums, per slice."""
+    import post_weight_quantization_05_amd as G
+
+    tb = -(-d // 256)
+    per_slice = tb * (tb + 1) // 2 * 256 * 256 * 4 + tb * 256 * 8
+    slices = round(G.load().gptq_hessian_workspace_bytes(n, d, G.GPTQ_BF16) / per_slice)
+    return -(-(-(-n // slices)) // 32) * 32
+
+
 def dequantized(res_gpu) -> np.ndarray:
     """Q of a GPU result (QuantResult), formed on the host in fp64 from its codes, scales (zeros) and
     g_idx with the oracle's dequantize."""

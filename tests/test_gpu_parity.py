@@ -11,7 +11,8 @@ import torch
 import post_weight_quantization_05_amd as G
 from oracle import gptq_oracle as O
 import synthetic as syn
-from tests.parity import assert_gates, compare, compare_asym, dequantized, dev64, layer_inputs, to_device
+from tests.parity import (assert_gates, compare, compare_asym, dequantized, dev64, layer_inputs,
+                          plan_rows_per_slice, to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -59,15 +60,6 @@ def test_hessian_matches_oracle(cfg):
     assert st.n_total == n_ref
 
 
-def _plan_rows_per_slice(n, d):
-    """Rows per fp32 slice the library plans for a bf16 accumulation of n rows, from its workspace size
-    (fp32 256 x 256 partials of every lower tile plus fp64 column sums, per slice)."""
-    tb = -(-d // 256)
-    per_slice = tb * (tb + 1) // 2 * 256 * 256 * 4 + tb * 256 * 8
-    slices = round(G.load().gptq_hessian_workspace_bytes(n, d, G.GPTQ_BF16) / per_slice)
-    return -(-(-(-n // slices)) // 32) * 32
-
-
 @pytest.mark.parametrize("kind,n,d", [("normal", 4096, 256), ("relu", 9000, 512), ("outliers", 20000, 768)])
 def test_hessian_arithmetic_is_the_fp32_chain_model(kind, n, d):
     """The Hessian kernel's S against the oracle's model of fp32 matrix-core accumulation with the same
@@ -83,7 +75,7 @@ def test_hessian_arithmetic_is_the_fp32_chain_model(kind, n, d):
     torch.cuda.synchronize()
     S = st.S.cpu().numpy()
     X64 = O.to_f64(X, "bf16")
-    rps = _plan_rows_per_slice(n, d)
+    rps = plan_rows_per_slice(n, d)
     Sm, c = np.zeros((d, d)), np.zeros(d)
     O.accumulate_fp32_chains(Sm, c, X64, chain_rows=rps, group_rows=8)
     low = np.tril_indices(d)
