@@ -66,8 +66,37 @@ def hessian_traffic():
         return None
 
 
+def host_info():
+    """CPU model (lscpu) and numpy's BLAS, for the CPU-baseline record."""
+    import io
+    import subprocess
+    from contextlib import redirect_stdout
+
+    model = None
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except (OSError, subprocess.SubprocessError):
+        pass
+    blas = None
+    try:
+        cfg = np.show_config(mode="dicts")
+        b = (cfg or {}).get("Build Dependencies", {}).get("blas", {})
+        blas = " ".join(str(b.get(k, "")) for k in ("name", "version", "openblas configuration")).strip() or None
+    except TypeError:  # older numpy: text only
+        buf = io.StringIO()
+        with redirect_stdout(buf):
+            np.show_config()
+        blas = buf.getvalue().split("blas", 1)[-1][:80].strip() or None
+    return model, blas
+
+
 def cpu_baseline(cfg, W, X, sample_rows, loop_rows):
-    """The oracle as it stands, timed on this host on a bounded sample of the workload, scaled to one layer."""
+    """The oracle as it stands, timed on this host on a bounded sample of the workload; the stage times
+    are extrapolated to one whole layer (the sample is stated in the record)."""
     from oracle import gptq_oracle as O
 
     t_all = time.perf_counter()
@@ -92,15 +121,18 @@ def cpu_baseline(cfg, W, X, sample_rows, loop_rows):
         cores = len(os.sched_getaffinity(0))
     except AttributeError:
         cores = os.cpu_count()
+    model, blas = host_info()
     return {
         "value": round(total_ms, 1),
         "unit": "ms",
         "cores": cores,
         "kind": "oracle",
-        "sample": (f"numpy fp64 oracle: X^T X over {rows} of {cfg.n} rows (scaled x{cfg.n / rows:g}), "
-                   f"inv+cholesky at full in={cfg.d_in}, compensation loop on {lr} of {cfg.out} rows "
-                   f"(scaled x{cfg.out / lr:g}; the loop is numpy element-wise, one core); "
-                   f"measured {time.perf_counter() - t_all:.1f} s"),
+        "sample": (f"extrapolated from a sampled run of the numpy fp64 oracle: X^T X over {rows} of {cfg.n} rows "
+                   f"(time x{cfg.n / rows:g}), inv+cholesky at full in={cfg.d_in} (not scaled), the sweep on {lr} "
+                   f"of {cfg.out} rows (time x{cfg.out / lr:g}; a per-row Python loop, one core); "
+                   f"sampled run took {time.perf_counter() - t_all:.1f} s"),
+        "cpu_model": model,
+        "numpy_blas": blas,
         "stages_ms": {"hessian": round(t_hess * 1e3, 1), "factor": round(t_factor * 1e3, 1),
                       "loop": round(t_loop * 1e3, 1)},
     }
@@ -172,6 +204,24 @@ def main():
             for i, k in enumerate(("zero", "hessian", "prepare", "quantize")):
                 ev[k].append((marks[i], marks[i + 1]))
         return res
+
+    def streamed_hessian_ms(reps=3):
+        """The same accumulation as 2048-row calls (the workload's segments), on the same stream: the
+        first call writes S, the others add to it. Median of `reps` passes over all of X, HIP events."""
+        seg = 2048
+        ws = st.workspace(seg, G.GPTQ_BF16 if cfg.dtype == "bf16" else G.GPTQ_F32)
+        times = []
+        for _ in range(reps):
+            a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            st.n_total = 0
+            a.record(stream)
+            for r0 in range(0, cfg.n, seg):
+                G.hessian_accumulate(Xd[r0:r0 + seg], st)
+            b_.record(stream)
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b_))
+        del ws
+        return float(np.median(times)), -(-cfg.n // seg)
 
     if args.mode == "hessian":
         for _ in range(max(1, args.steps)):
@@ -254,6 +304,11 @@ def main():
         "wall_s_timed": round(wall, 3),
         "gen_s": round(gen_s, 2),
     }
+    if cfg.n >= 2048:
+        s_ms, calls = streamed_hessian_ms()
+        line["hessian_streamed"] = {"calls": calls, "rows_per_call": 2048, "ms": round(s_ms, 4),
+                                    "achieved_tflops": round(hess_flops / (s_ms * 1e-3) / 1e12, 1),
+                                    "frac_of_bf16_peak": round(hess_flops / (s_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, W, X, args.cpu_sample_rows, args.cpu_loop_rows)
     print(json.dumps(line), flush=True)
