@@ -352,7 +352,7 @@ __global__ __launch_bounds__(256) void k_colstep(DgemmArgs a, DgemmArgs xa, int 
   // other K and for deferred tiles); later the tile X
   constexpr int AB_SZ = (2 * T * K64S > 4 * L::SZ) ? 2 * T * K64S : 4 * L::SZ;
   __shared__ __attribute__((aligned(16))) double ABs[AB_SZ];
-  __shared__ diagblock::DiagSmem dsm;
+  __shared__ diagblock::BlockSmem bsm;
   static_assert(AB_SZ >= T * (T + 1), "tile buffer");
   double(*As)[L::SZ] = reinterpret_cast<double(*)[L::SZ]>(ABs);
   double(*Bs)[L::SZ] = reinterpret_cast<double(*)[L::SZ]>(ABs + 2 * L::SZ);
@@ -449,7 +449,7 @@ __global__ __launch_bounds__(256) void k_colstep(DgemmArgs a, DgemmArgs xa, int 
     return;
   }
 
-  // the updated diagonal block, staged for the factorization (identity past the edge)
+  // the updated diagonal block, staged for the factorization (lower part; identity past the edge)
   auto stage_diag = [&](const f64x4 (&d)[FR][FC]) {
 #pragma unroll
     for (int r = 0; r < FR; ++r)
@@ -460,18 +460,25 @@ __global__ __launch_bounds__(256) void k_colstep(DgemmArgs a, DgemmArgs xa, int 
           const int i = ti(r, e), j = tj(q);
           double v = (i == j) ? 1.0 : 0.0;
           if (i < m && j < m && j <= i) v = fma(a.beta, cdiag[r][q][e], a.alpha * d[r][q][e]);
-          dsm.Ls[i][j] = v;
+          bsm.A[i][j] = v;
         }
   };
   if (I == 0) {
     stage_diag(acc);
     __syncthreads();
-    diagblock::diag_factor(dsm, m, a.diag_Lstage + (int64_t)a.diag_kb * T * T, T,
-                           a.diag_Dinv + (int64_t)a.diag_kb * T * T, a.diag_status);
+    const unsigned flags = diagblock::factor_invert_blocked(bsm);
+    double* Lout = a.diag_Lstage + (int64_t)a.diag_kb * T * T;
+    double* Dout = a.diag_Dinv + (int64_t)a.diag_kb * T * T;
+    for (int e = tid; e < T * T; e += 256) {
+      const int i = e / T, j = e % T;
+      if (i < m && j < m) Lout[i * T + j] = bsm.A[i][j];
+      Dout[e] = bsm.M[i][j];  // the identity past the edge
+    }
+    if (flags && tid == 0) atomicOr(a.diag_status, flags);
     return;
   }
-  // this tile, updated (kept in registers through the factorization)
-  f64x4 x[FR][FC];
+  // this tile, updated, into LDS as the left operand of the solve ([i][k], rows of K64S doubles)
+  double* Xa = ABs;
 #pragma unroll
   for (int r = 0; r < FR; ++r)
 #pragma unroll
@@ -479,21 +486,40 @@ __global__ __launch_bounds__(256) void k_colstep(DgemmArgs a, DgemmArgs xa, int 
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int gi = i0 + ti(r, e), gj = tj(q);
-        x[r][q][e] = (gi < M && gj < m) ? fma(a.beta, cown[r][q][e], a.alpha * acc[r][q][e]) : 0.0;
+        Xa[ti(r, e) * K64S + tj(q)] = (gi < M && gj < m) ? fma(a.beta, cown[r][q][e], a.alpha * acc[r][q][e]) : 0.0;
       }
-  // X into LDS (row-major, stride T + 1) and the diagonal block staged; the factorization then solves
-  // X L^T = X in place of forming L^-1 (a forward substitution per row of X) and writes the panel tile
-  double(*Xs)[T + 1] = reinterpret_cast<double(*)[T + 1]>(ABs);
+  // the diagonal block again from the same inputs (no waiting on tile (0, 0)), factored and inverted
+  stage_diag(dacc);
+  __syncthreads();
+  diagblock::factor_invert_blocked(bsm);
+  // the panel tile X L^-T = X (L^-1)^T: out[i][j] = sum_k X[i][k] L^-1[j][k], on the matrix cores
+  f64x4 sol[FR][FC];
+#pragma unroll
+  for (int p = 0; p < FR; ++p)
+#pragma unroll
+    for (int q = 0; q < FC; ++q) sol[p][q] = f64x4{0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int k4 = 0; k4 < T; k4 += 4) {
+    const int kr = k4 + lk;
+    double fa[FR], fb[FC];
+#pragma unroll
+    for (int r = 0; r < FR; ++r) fa[r] = Xa[(wm * (T / 2) + r * 16 + lc) * K64S + kr];
+#pragma unroll
+    for (int q = 0; q < FC; ++q) fb[q] = bsm.M[wn * (T / 2) + q * 16 + lc][kr];
+#pragma unroll
+    for (int r = 0; r < FR; ++r)
+#pragma unroll
+      for (int q = 0; q < FC; ++q) sol[r][q] = __builtin_amdgcn_mfma_f64_16x16x4f64(fa[r], fb[q], sol[r][q], 0, 0, 0);
+  }
 #pragma unroll
   for (int r = 0; r < FR; ++r)
 #pragma unroll
     for (int q = 0; q < FC; ++q)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) Xs[ti(r, e)][tj(q)] = x[r][q][e];
-  stage_diag(dacc);
-  __syncthreads();
-  diagblock::diag_factor(dsm, m, nullptr, 0, nullptr, nullptr, &Xs[0][0], C + (int64_t)i0 * a.ldc, a.ldc,
-                         min(T, M - i0));
+      for (int e = 0; e < 4; ++e) {
+        const int gi = i0 + ti(r, e), gj = tj(q);
+        if (gi < M && gj < m) C[(int64_t)gi * a.ldc + gj] = sol[r][q][e];
+      }
 }
 
 }  // namespace

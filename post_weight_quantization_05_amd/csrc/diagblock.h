@@ -1,6 +1,6 @@
 // Factorization of one 64 x 64 diagonal block (fp64, gfx950): its Cholesky factor and the inverse of
 // the factor. Used by the block-column step of the blocked factorization (k_colstep), where the
-// workgroups of the next panel each factor the block from the same inputs.
+// workgroups of the panel each factor the block from the same inputs.
 //
 // GPTQ guide ("GPTQ", herodthegreater.github.io/pigeon/guide/gptq/), "GPTQ's two tricks", trick 2: U is
 // a Cholesky factor; these blocks are the diagonal steps of the blocked factorization that yields it.
@@ -14,21 +14,13 @@ namespace diagblock {
 
 constexpr int NB = 64;
 
-// compile-time loop (the 64-step elimination loops are too large for the unroller, and a runtime index
-// into the register-resident row would move it to scratch memory)
+// compile-time loop (a runtime index into a register-resident row would move it to scratch memory)
 template <int K, int N, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
   if constexpr (K < N) {
     f(std::integral_constant<int, K>{});
     static_for<K + 1, N>(f);
   }
-}
-
-__device__ __forceinline__ double readlane_d(double v, int l) {
-  const long long x = __double_as_longlong(v);
-  const int lo = __builtin_amdgcn_readlane((int)(x & 0xFFFFFFFFll), l);
-  const int hi = __builtin_amdgcn_readlane((int)(x >> 32), l);
-  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
 }
 
 // 1/sqrt(a) for finite a >= 2^-1000, to about 1 ulp without an IEEE square root or division: the
@@ -41,198 +33,165 @@ __device__ __forceinline__ double rsqrt_refined(double a) {
   return fma(y * e, p, y);
 }
 
-// v from lane 4q + R of each quad of lanes (DPP quad_perm [R, R, R, R]), both halves of the double
-template <int R>
-__device__ __forceinline__ double quad_bcast(double v) {
-  const long long x = __double_as_longlong(v);
-  const int lo = __builtin_amdgcn_update_dpp(0, (int)(x & 0xFFFFFFFFll), R * 0x55, 0xF, 0xF, false);
-  const int hi = __builtin_amdgcn_update_dpp(0, (int)(x >> 32), R * 0x55, 0xF, 0xF, false);
-  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
-}
+// ------------------------------------------------------------------------------------------------------
+// Blocked factorization of one 64 x 64 diagonal block, L and L^-1 both (256 threads, 4 waves).
+//
+// The block goes through four 16-column sub-blocks b. Each wave factors the 16 x 16 diagonal sub-block
+// in registers (all four DPP rows of every wave redundantly, so no barrier sits between the waves): lane
+// i of a row of 16 lanes holds row i; pivot k is broadcast from lane k (DPP row_newbcast), its 1/sqrt
+// comes from rsqrt_refined, and L's column k reaches the lanes that update with it by further row
+// broadcasts (one v_mov_b64_dpp each; fp64 matrix cores run no faster than the vector unit on this
+// part, so the 16 x 16 steps gain nothing from them). The inverse of the sub-block's factor follows by
+// forward substitution on its unit-diagonal form, each DPP row g solving columns g, g + 4, g + 8,
+// g + 12: lane (i, g) then holds exactly the v_mfma_f64_16x16x4f64 operand fragments of that inverse
+// (A[i][4t + g] or B[4t + g][i] in k-step t). With it the panel below is solved on the matrix cores
+// (P = A_panel L_bb^-T, one 16-row tile per wave) and the trailing lower tiles are updated (A -= P P^T).
+// Last, the blocks of L^-1 below the diagonal, M_ij = -M_ii sum_k L_ik M_kj, in three dependent levels
+// of 16 x 16 products. Rows/columns past the matrix edge are staged as the identity and stay the
+// identity in L and L^-1. About 28k cycles per block (the one-wave elimination it replaces: 49k).
+// ------------------------------------------------------------------------------------------------------
+constexpr int BS = 65;  // LDS row stride (doubles)
 
-// Factorization of one diagonal block staged in LDS (lower part; rows/columns past the matrix edge as
-// the identity): its Cholesky factor L and L^-1. 256 threads. Outputs are optional: L to global memory,
-// L^-1 to global memory, the status bits; or, instead of L^-1, the solution X of X L^T = T for a 64-row
-// tile T staged in LDS.
-//  Cholesky (wave 0): lane i holds row i in registers and eliminates right-looking. Pivot k is
-//  r_k[k]; 1/L[k][k] comes from rsqrt_refined, so no square root or division sits on the chain. After
-//  scaling column k, every lane updates its entries j > k with column k, which goes through LDS. The
-//  next pivot r_{k+1}[k+1] - L[k+1][k]^2 uses lane k+1's own registers only, so its square-root
-//  estimate overlaps the LDS round trip of the column.
-//  Inverse (all 4 waves): a quad of lanes owns column j of L^-1 (lane 4j + r holds rows i = r mod 4) and
-//  eliminates right-looking; the finished entry (L^-1)[k][j] reaches the other lanes of its quad by
-//  DPP. Column k of L is kept in LDS as Lc[k][r][m] = L[4m + r][k], with the four r-rows 144 bytes apart
-//  so a quad's four reads hit distinct banks.
-// Rows/columns past the matrix edge act as the identity. Pivots below 2^-1000 or not finite set the
-// status bits (and are treated as 1 from there on).
-constexpr int LC_STRIDE = 18;  // doubles per (k, r) row of Lc
-
-struct DiagSmem {
-  double Ls[NB][NB + 1];                                // the block, later L (row-major)
-  __attribute__((aligned(16))) double Lc[NB][4][LC_STRIDE];  // Lc[k][r][m] = L[4m + r][k]
-  double col[NB];                                       // column k during the elimination
-  double rdg[NB];                                       // 1 / L[k][k]
+struct BlockSmem {
+  double A[NB][BS];  // the block (lower part, zeros above), then L
+  double M[NB][BS];  // L^-1 (lower part, zeros above)
 };
 
-// Factor the block in sm.Ls (staged by the caller, followed by a barrier). m is the block's size.
-//   Lout (nullable): L written to Lout[i * ldo + j] for i, j < m, zeros above the diagonal;
-//   Dout (nullable): L^-1 as a row-major 64 x 64 block, the identity past the edge;
-//   status (nullable): flags of bad pivots;
-//   rhs (nullable, LDS, 64 rows of stride NB + 1): instead of L^-1, the substitution solves
-//   X L^T = rhs (each row x of X from L x^T = row^T), and row i < xrows, column j < m of X goes to
-//   Xout[i * ldx + j]. Dout must then be null.
-__device__ __forceinline__ void diag_factor(DiagSmem& sm, int m, double* __restrict__ Lout, int64_t ldo,
-                                            double* __restrict__ Dout, unsigned* status,
-                                            const double* rhs = nullptr, double* Xout = nullptr, int64_t ldx = 0,
-                                            int xrows = 0) {
-  auto& Ls = sm.Ls;
-  auto& Lc = sm.Lc;
-  auto& col = sm.col;
-  auto& rdg = sm.rdg;
-  const int tid = threadIdx.x;
-  if (tid < 64) {
-    const int i = tid;
-    unsigned flags = 0;
-    double r[NB];
-    int ir = i;
-    asm volatile("" : "+v"(ir));
+template <int K>
+__device__ __forceinline__ double row_bcast(double v) {  // value of lane K of this lane's row of 16
+  return __builtin_amdgcn_mov_dpp(v, 0x150 + K, 0xF, 0xF, false);  // one v_mov_b64_dpp (row_newbcast)
+}
+
+__device__ __forceinline__ f64x4 mfma16(double a, double b, f64x4 c) {
+  return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
+}
+
+// Factor sm.A (staged by the caller, followed by a barrier) into L (in sm.A) and L^-1 (in sm.M). Returns
+// the bad-pivot flags (the same in every lane). Ends with a barrier.
+__device__ __forceinline__ unsigned factor_invert_blocked(BlockSmem& sm) {
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int i = lane & 15, g = lane >> 4;
+  // L^-1 starts as zeros (its diagonal and lower blocks are written below)
+  for (int e = tid; e < NB * BS; e += 256) (&sm.M[0][0])[e] = 0.0;
+  double xb[4][4];  // xb[b][t] = (L_bb^-1)[i][4t + g]
+  static_for<0, 4>([&](auto bc) {
+    constexpr int b = decltype(bc)::value;
+    constexpr int o = 16 * b;
+    // ---- the 16 x 16 diagonal sub-block: factor and inverse, in registers ----
+    // Pivot k comes from lane k; a pivot that is not finite or below 2^-1000 takes 1/sqrt = 1, so the
+    // values stay finite, and it shows on L's diagonal (checked at the end).
+    double r[16];
 #pragma unroll
-    for (int j = 0; j < NB; ++j) r[j] = Ls[ir][j];
-    // A pivot that is not finite, or below 2^-1000 (not > 0 in particular), is flagged and its 1/sqrt
-    // replaced by 1, so a matrix that is not positive definite leaves finite values behind; the caller
-    // reports the status. The test runs beside the pivot chain and only the final select joins it.
-    auto inv_sqrt = [&](double p) {
-      const bool ok = (p >= 0x1p-1000) && (p < INFINITY);
-      flags |= ok ? 0u : (isfinite(p) ? DEV_STATUS_NOT_SPD : DEV_STATUS_NONFINITE);
-      const double yr = rsqrt_refined(p);
-      return ok ? yr : 1.0;
-    };
-    double piv = readlane_d(r[0], 0);
-    double y = inv_sqrt(piv);
-    double ydiag = 0.0;
-    static_for<0, NB>([&](auto kc) {
+    for (int k = 0; k < 16; ++k) r[k] = sm.A[o + i][o + k];
+    double yown = 1.0;  // 1 / L[i][i]
+    double lh[16];      // lh[k] = L[i][k] / L[k][k] below the diagonal, 0 on and above it
+    static_for<0, 16>([&](auto kc) {
       constexpr int k = decltype(kc)::value;
-      r[k] = r[k] * y;  // lane k: piv y = L[k][k]; lanes below: L[i][k]
-      ydiag = (i == k) ? y : ydiag;
-      if constexpr (k + 1 < NB) {
-        // next pivot from lane k+1's own entries: r[k+1] - L[k+1][k]^2 (no LDS on this path)
-        const double pn = readlane_d(fma(-r[k], r[k], r[k + 1]), k + 1);
-        col[i] = r[k];
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        constexpr int F = ((k + 1) & ~7), NC = (NB - F) / 8;  // chunks of 8 holding the entries > k
-        double buf[4][8];
-        auto rd = [&](auto cc) {
-          constexpr int c = decltype(cc)::value;
-#pragma unroll
-          for (int q = 0; q < 8; ++q) buf[c & 3][q] = col[F + 8 * c + q];
-        };
-        static_for<0, (NC < 3 ? NC : 3)>(rd);
-        __builtin_amdgcn_sched_barrier(0);
-        // the next pivot's 1/sqrt runs while the column reads are in flight
-        const double yn = inv_sqrt(pn);
-        __builtin_amdgcn_sched_barrier(0);
-        static_for<0, NC>([&](auto cc) {
-          constexpr int c = decltype(cc)::value;
-          if constexpr (c + 3 < NC) rd(std::integral_constant<int, c + 3>{});
-          __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-          for (int q = 0; q < 8; ++q) {
-            if (F + 8 * c + q > k) r[F + 8 * c + q] = fma(-r[k], buf[c & 3][q], r[F + 8 * c + q]);
-          }
-        });
-        __builtin_amdgcn_wave_barrier();
-#pragma unroll
-        for (int j = k + 1; j < NB; ++j) asm volatile("" : "+v"(r[j]));
-        piv = pn;
-        y = yn;
-      }
+      const double piv = row_bcast<k>(r[k]);
+      const bool ok = (piv >= 0x1p-1000) && (piv < INFINITY);
+      const double y = ok ? rsqrt_refined(piv) : 1.0;  // a select (nothing to skip in a branch)
+      const double l = r[k] * y;  // lane k: L[k][k]; lanes below: L[i][k]; lanes above: unused
+      r[k] = l;
+      yown = (i == k) ? y : yown;
+      lh[k] = (i > k) ? l * y : 0.0;
+      static_for<k + 1, 16>([&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+        r[j] = fma(-l, row_bcast<j>(l), r[j]);
+      });
     });
-    rdg[i] = ydiag;
-    // a fresh copy of the row index, so the compiler forms these addresses here instead of keeping the
-    // load addresses of the same rows alive through the elimination
-    int iw = i;
-    asm volatile("" : "+v"(iw));
+    // L^-1 = D^-1 Lh^-1 with Lh = L D^-1 unit lower (D = diag L): forward substitution on the unit factor
+    // (no division, no select), then row i scaled by 1 / L[i][i]. Lane (i, g) holds columns g + 4t.
+    double x[4];
 #pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      Ls[iw][j] = (j <= iw) ? r[j] : 0.0;
-      Lc[j][iw & 3][iw >> 2] = (j < iw) ? r[j] : 0.0;
+    for (int t = 0; t < 4; ++t) x[t] = (i == g + 4 * t) ? 1.0 : 0.0;
+    static_for<0, 15>([&](auto kc) {
+      constexpr int k = decltype(kc)::value;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) x[t] = fma(-lh[k], row_bcast<k>(x[t]), x[t]);
+    });
+#pragma unroll
+    for (int t = 0; t < 4; ++t) x[t] *= yown;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) xb[b][t] = x[t];
+    if constexpr (b < 3) {
+      // ---- panel below: P = A[p0:p0+16][o:o+16] L_bb^-T, one tile per wave, in place ----
+      if (w < 3 - b) {
+        const int p0 = 16 * (b + 1 + w);
+        double a[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) a[t] = sm.A[p0 + i][o + 4 * t + g];
+        f64x4 acc = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc = mfma16(a[t], x[t], acc);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) sm.A[p0 + 4 * q + g][o + i] = acc[q];
+      }
     }
-    if (status && flags && i == 0) atomicOr(status, flags);
-  }
-  __syncthreads();
-  // a fresh copy of the thread index for the later phases (keeps the first phase's addresses from
-  // staying alive, and spilling, across the elimination)
-  int tw = tid;
-  asm volatile("" : "+v"(tw));
-  if (Lout) {
-    double v[NB * NB / 256];
+    // every wave has read the diagonal sub-block (and its panel tile) before L_bb replaces it
+    __syncthreads();
+    if (w == 0) {
+      if (g == 0) {
 #pragma unroll
-    for (int t = 0; t < NB * NB / 256; ++t) {
-      const int e = tw + 256 * t;
-      v[t] = Ls[e / NB][e % NB];
-    }
-#pragma unroll
-    for (int t = 0; t < NB * NB / 256; ++t) {
-      const int e = tw + 256 * t, i = e / NB, j = e % NB;
-      if (i < m && j < m) Lout[(int64_t)i * ldo + j] = v[t];
-    }
-  }
-  // inverse: lane 4j + r holds c[q] = (L^-1)[4q + r][j], starting from e_j (or, with rhs, the solution
-  // of L x = (row j of rhs)^T, starting from that row)
-  const int jc = tw >> 2, rr = tw & 3;
-  double c[16];
-  if (rhs) {
-#pragma unroll
-    for (int q = 0; q < 16; ++q) c[q] = rhs[jc * (NB + 1) + 4 * q + rr];
-  } else {
-#pragma unroll
-    for (int q = 0; q < 16; ++q) c[q] = (4 * q + rr == jc) ? 1.0 : 0.0;
-  }
-  // column k of L and 1/L[k][k] are read one step ahead, so their LDS latency is off the chain. Every
-  // read goes through one per-lane base (Lc[0][rr]) with a constant offset.
-  const double* lb = &Lc[0][rr][0];
-  double lcur[16], lnext[16];
-  double dcur = rdg[0], dnext = 0.0;
-#pragma unroll
-  for (int q = 0; q < 16; ++q) lcur[q] = lb[q];
-  static_for<0, NB>([&](auto kc) {
-    constexpr int k = decltype(kc)::value;
-    constexpr int mk = k >> 2, rk = k & 3;
-    if constexpr (k + 1 < NB) {
-#pragma unroll
-      for (int q = (k + 1) >> 2; q < 16; ++q) lnext[q] = lb[(k + 1) * 4 * LC_STRIDE + q];
-      dnext = rdg[k + 1];
-    }
-    const double own = c[mk] * dcur;
-    c[mk] = (rr == rk) ? own : c[mk];
-    if constexpr (k + 1 < NB) {
-      const double b = quad_bcast<rk>(c[mk]);  // (L^-1)[k][j]
-#pragma unroll
-      for (int q = mk; q < 16; ++q) {
-        const double t = fma(-lcur[q], b, c[q]);
-        c[q] = (q > mk || rr > rk) ? t : c[q];
+        for (int k = 0; k < 16; ++k) sm.A[o + i][o + k] = (k <= i) ? r[k] : 0.0;
       }
 #pragma unroll
-      for (int q = (k + 1) >> 2; q < 16; ++q) lcur[q] = lnext[q];
-      dcur = dnext;
+      for (int t = 0; t < 4; ++t) sm.M[o + i][o + 4 * t + g] = x[t];
     }
+    if constexpr (b < 3) {
+      // ---- trailing lower tiles: A[I][J] -= P_I P_J^T for b < J <= I < 4 (rows and columns past o + 16,
+      // apart from the sub-block L_bb and L^-1 that wave 0 writes meanwhile) ----
+      constexpr int NT = (3 - b) * (4 - b) / 2;
+      for (int tt = w; tt < NT; tt += 4) {
+        int I = b + 1, J = b + 1, c = tt;
+        while (c >= I - b) {  // tiles in order (b+1,b+1), (b+2,b+1), (b+2,b+2), ...
+          c -= I - b;
+          ++I;
+        }
+        J = b + 1 + c;
+        double a[4], bb[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          a[t] = sm.A[16 * I + i][o + 4 * t + g];
+          bb[t] = sm.A[16 * J + i][o + 4 * t + g];
+        }
+        f64x4 acc = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc = mfma16(a[t], bb[t], acc);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int row = 4 * q + g;
+          if (I != J || row >= i) sm.A[16 * I + row][16 * J + i] -= acc[q];
+        }
+      }
+    }
+    __syncthreads();
   });
-  if (Dout) {
+  // ---- blocks of L^-1 below the diagonal, level by level: M_ij = -M_ii sum_{k=j}^{i-1} L_ik M_kj ----
+  static_for<1, 4>([&](auto ic) {
+    constexpr int bi = decltype(ic)::value;
+    if (w < bi) {
+      const int bj = w;
+      f64x4 T = {0.0, 0.0, 0.0, 0.0};
+      for (int bk = bj; bk < bi; ++bk) {
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int row = 4 * q + rr;
-      Dout[row * NB + jc] = (row < m && jc < m) ? c[q] : ((row == jc) ? 1.0 : 0.0);
-    }
-  }
-  if (rhs && jc < xrows) {
+        for (int t = 0; t < 4; ++t)
+          T = mfma16(sm.A[16 * bi + i][16 * bk + 4 * t + g], sm.M[16 * bk + 4 * t + g][16 * bj + i], T);
+      }
+      f64x4 R = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int col = 4 * q + rr;
-      if (col < m) Xout[(int64_t)jc * ldx + col] = c[q];
+      for (int t = 0; t < 4; ++t) R = mfma16(xb[bi][t], T[t], R);  // T's acc layout is the B operand of k-step t
+#pragma unroll
+      for (int q = 0; q < 4; ++q) sm.M[16 * bi + 4 * q + g][16 * bj + i] = -R[q];
     }
-  }
+    __syncthreads();
+  });
+  // bad pivots, read off L's diagonal: a good pivot p >= 2^-1000 leaves L[k][k] = sqrt(p) > 2^-501 (and
+  // finite); a bad one leaves p itself (1/sqrt taken as 1): below 2^-1000, infinite or NaN
+  const double dg = sm.A[lane][lane];
+  const bool good = (dg > 0x1p-501) && (dg < INFINITY);
+  const unsigned long long nonfinite = __ballot(!good && !isfinite(dg));
+  const unsigned long long small = __ballot(!good && isfinite(dg));
+  return (nonfinite ? DEV_STATUS_NONFINITE : 0u) | (small ? DEV_STATUS_NOT_SPD : 0u);
 }
 
 }  // namespace diagblock
