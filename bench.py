@@ -35,6 +35,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-rows", type=int, default=65536)
     ap.add_argument("--cpu-loop-rows", type=int, default=64)
+    ap.add_argument("--no-streamed-hessian", action="store_true",
+                    help="skip the second Hessian figure (the same rows as 2048-row calls), e.g. for kernel traces")
     ap.add_argument("--mode", choices=["layer", "hessian", "copy"], default="layer",
                     help="layer: the timed benchmark; hessian: only the accumulate calls (for counter "
                          "passes); copy: a plain 1 GiB device copy (calibrates FETCH_SIZE/WRITE_SIZE)")
@@ -304,7 +306,7 @@ def main():
         "wall_s_timed": round(wall, 3),
         "gen_s": round(gen_s, 2),
     }
-    if cfg.n >= 2048:
+    if cfg.n >= 2048 and not args.no_streamed_hessian:
         s_ms, calls = streamed_hessian_ms()
         line["hessian_streamed"] = {"calls": calls, "rows_per_call": 2048, "ms": round(s_ms, 4),
                                     "achieved_tflops": round(hess_flops / (s_ms * 1e-3) / 1e12, 1),
