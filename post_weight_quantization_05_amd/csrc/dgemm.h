@@ -40,11 +40,31 @@ struct DgemmArgs {
 // and op(B) = B^T with K <= 256 and no tile list. Everything else (batches, triangular K ranges, tile lists, op(A) = A^T, larger
 // K) takes the chunked-ring GEMM.
 hipError_t dgemm_launch(const DgemmArgs& a, bool ta, bool tb, int batches, hipStream_t stream);
+// The inverse Z = L^-1 of the factor, formed by the block-column steps as work that fills the CUs their
+// chain leaves idle (see inv_fill_tile in dgemm.hip). Row block t of L Z = I is eliminated right-looking:
+//   G_{i,t} = L_{i,t} L_tt^-1 for the blocks i > t below step t (launch t + 1),
+//   Z_{i,j} -= G_{i,t} Z_{t,j} for j < t, Z_{i,t} = -G_{i,t} (launch t + 2; Z holds unscaled rows),
+//   Z_{t,j} = L_tt^-1 Z_{t,j} for j < t, Z_{t,t} = L_tt^-1 (launch t + 3),
+// where launch k is the step that factors diagonal block k, and launches S .. S + 2 (S = number of
+// 64-blocks) come after the last step. Every input of a launch's tiles is final by the end of the
+// launch before it.
+struct InvFill {
+  const double* L;     // the matrix being factored (its lower part is L once the step has passed), ld d
+  const double* Dinv;  // the steps' diagonal-block inverses, 64 x 64 row-major each
+  double* Z;           // d x d, ld d; its lower part becomes L^-1
+  double* G[2];        // d x 64 each, used in turn by steps of even and odd t
+  int d, S;
+  int k;               // the launch
+};
+int inv_fill_tiles(const InvFill& f);
 // One block-column step of the blocked Cholesky factorization (see k_colstep in dgemm.hip): C -= A B^T
 // on the lower tiles of the M x N region C, the diagonal block at its origin factored and inverted, and
 // the column-0 tiles below it solved against that factor. The same launch also computes lower tiles
 // x_first .. x_first + x_count - 1 (in tile order) of x, an independent A B^T update of a square region
-// (x may be null when x_count is 0).
-hipError_t colstep_launch(const DgemmArgs& a, const DgemmArgs* x, int x_first, int x_count, hipStream_t stream);
+// (x may be null when x_count is 0), and, when f is not null, the tiles of launch f->k of the inverse.
+hipError_t colstep_launch(const DgemmArgs& a, const DgemmArgs* x, int x_first, int x_count, const InvFill* f,
+                          hipStream_t stream);
+// The inverse's tiles of a launch after the last step (f.k = S, S + 1, S + 2).
+hipError_t inv_fill_launch(const InvFill& f, hipStream_t stream);
 
 }  // namespace gptq

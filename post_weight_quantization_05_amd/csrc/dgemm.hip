@@ -50,11 +50,11 @@ struct Lds {
 // (zero outside M x N x K). 4 waves in 2 x 2, each (T/2) x (T/2). Operand chunks of T x 16 are fetched
 // as 16-byte vectors into registers while the MFMAs of earlier chunks run, then stored to the other LDS
 // buffer. Ends with a barrier, so the LDS buffers may be reused at once.
-template <bool TA, bool TB, int T, bool BB = false>
+template <bool TA, bool TB, int T>
 __device__ __forceinline__ void tile_product(const DgemmArgs& a, const double* A, const double* B, int M, int N,
                                              int K, int i0, int j0, int klo, int khi,
                                              double (*As)[Lds<T>::SZ], double (*Bs)[Lds<T>::SZ],
-                                             f64x4 (&acc)[T / 32][T / 32], f64x4 (*acc_bb)[T / 32] = nullptr) {
+                                             f64x4 (&acc)[T / 32][T / 32]) {
   constexpr int NV = T * TK / 2 / 256;   // 16-byte loads per thread per operand and chunk
   using L = Lds<T>;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -123,10 +123,7 @@ __device__ __forceinline__ void tile_product(const DgemmArgs& a, const double* A
 #pragma unroll
   for (int p = 0; p < FR; ++p)
 #pragma unroll
-    for (int q = 0; q < FC; ++q) {
-      acc[p][q] = f64x4{0.0, 0.0, 0.0, 0.0};
-      if constexpr (BB) acc_bb[p][q] = f64x4{0.0, 0.0, 0.0, 0.0};
-    }
+    for (int q = 0; q < FC; ++q) acc[p][q] = f64x4{0.0, 0.0, 0.0, 0.0};
 
   const int nk = (khi > klo) ? (khi - klo + TK - 1) / TK : 0;
   static_for_d<0, PD>([&](auto pc) {
@@ -161,19 +158,6 @@ __device__ __forceinline__ void tile_product(const DgemmArgs& a, const double* A
       for (int r = 0; r < FR; ++r)
 #pragma unroll
         for (int q = 0; q < FC; ++q) acc[r][q] = __builtin_amdgcn_mfma_f64_16x16x4f64(fa[r], fb[q], acc[r][q], 0, 0, 0);
-      if constexpr (BB) {
-        // acc_bb += B's tile rows times themselves transposed (B^T stored as [j][k]): the product of the
-        // tile at (j0, j0), from the operand already in LDS
-        static_assert(TB, "B^T operand");
-        double fbb[FR];
-#pragma unroll
-        for (int r = 0; r < FR; ++r) fbb[r] = Bs[st][(wm * (T / 2) + r * 16 + lc) * L::IK + kr];
-#pragma unroll
-        for (int r = 0; r < FR; ++r)
-#pragma unroll
-          for (int q = 0; q < FC; ++q)
-            acc_bb[r][q] = __builtin_amdgcn_mfma_f64_16x16x4f64(fbb[r], fb[q], acc_bb[r][q], 0, 0, 0);
-      }
     }
     if (kt + 1 < nk) lstore(std::integral_constant<int, (p + 1) % PD>{}, st ^ 1);
     __syncthreads();
@@ -264,17 +248,12 @@ __global__ __launch_bounds__(256) void k_dgemm(DgemmArgs a) {
 // Single-shot form of tile_product for the block-column step (A B^T, T = 64, K = 64): all operand loads
 // in flight at once, one LDS store, one barrier, then the whole K, unrolled, on the matrix cores. The
 // operands sit in LDS as [row][k] with rows of 68 doubles (a 16 x 4 fragment read touches each bank pair
-// twice). With BB, acc_bb also receives the (j0, j0) tile from B alone, as in tile_product. Ends with a
-// barrier.
+// twice). k64_stage loads and stores them (rows i0.. of A to As, rows j0.. of B to Bs) and ends with a
+// barrier; the products read them.
 constexpr int K64S = 68;
-template <bool BB>
-__device__ __forceinline__ void tile_product_k64(const double* A, const double* B, int64_t lda, int64_t ldb, int M,
-                                                 int N, int i0, int j0, double* As, double* Bs,
-                                                 f64x4 (&acc)[2][2], f64x4 (*acc_bb)[2] = nullptr) {
-  constexpr int T = 64;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int lk = lane >> 4, lc = lane & 15;
+__device__ __forceinline__ void k64_stage(const double* A, const double* B, int64_t lda, int64_t ldb, int M, int N,
+                                          int i0, int j0, double* As, double* Bs) {
+  const int tid = threadIdx.x;
   const bool a_vec = ((lda & 1) == 0) && ((reinterpret_cast<uintptr_t>(A) & 15) == 0);
   const bool b_vec = ((ldb & 1) == 0) && ((reinterpret_cast<uintptr_t>(B) & 15) == 0);
   auto ld2 = [&](const double* P, int64_t ld, int r, int rlim, int c2, bool vec) {
@@ -298,40 +277,213 @@ __device__ __forceinline__ void tile_product_k64(const double* A, const double* 
     rb[v] = ld2(B, ldb, j0 + r, N, c2, b_vec);
   }
 #pragma unroll
-  for (int p = 0; p < 2; ++p)
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      acc[p][q] = f64x4{0.0, 0.0, 0.0, 0.0};
-      if constexpr (BB) acc_bb[p][q] = f64x4{0.0, 0.0, 0.0, 0.0};
-    }
-#pragma unroll
   for (int v = 0; v < 8; ++v) {
     const int e = tid + 256 * v, r = e >> 5, c2 = (e & 31) * 2;
     *reinterpret_cast<double2*>(&As[r * K64S + c2]) = ra[v];
     *reinterpret_cast<double2*>(&Bs[r * K64S + c2]) = rb[v];
   }
   __syncthreads();
+}
+
+// acc = the T x T tile of A B^T from the staged operands; 4 waves in 2 x 2, each 32 x 32. Ends with a
+// barrier.
+__device__ __forceinline__ void tile_product_k64(const double* A, const double* B, int64_t lda, int64_t ldb, int M,
+                                                 int N, int i0, int j0, double* As, double* Bs,
+                                                 f64x4 (&acc)[2][2]) {
+  constexpr int T = 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int lk = lane >> 4, lc = lane & 15;
+  k64_stage(A, B, lda, ldb, M, N, i0, j0, As, Bs);
+#pragma unroll
+  for (int p = 0; p < 2; ++p)
+#pragma unroll
+    for (int q = 0; q < 2; ++q) acc[p][q] = f64x4{0.0, 0.0, 0.0, 0.0};
 #pragma unroll
   for (int k4 = 0; k4 < T; k4 += 4) {
     const int kr = k4 + lk;
-    double fa[2], fb[2], fbb[2];
+    double fa[2], fb[2];
 #pragma unroll
     for (int r = 0; r < 2; ++r) fa[r] = As[(wm * (T / 2) + r * 16 + lc) * K64S + kr];
 #pragma unroll
     for (int q = 0; q < 2; ++q) fb[q] = Bs[(wn * (T / 2) + q * 16 + lc) * K64S + kr];
-    if constexpr (BB) {
-#pragma unroll
-      for (int r = 0; r < 2; ++r) fbb[r] = Bs[(wm * (T / 2) + r * 16 + lc) * K64S + kr];
-    }
 #pragma unroll
     for (int r = 0; r < 2; ++r)
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        acc[r][q] = __builtin_amdgcn_mfma_f64_16x16x4f64(fa[r], fb[q], acc[r][q], 0, 0, 0);
-        if constexpr (BB) acc_bb[r][q] = __builtin_amdgcn_mfma_f64_16x16x4f64(fbb[r], fb[q], acc_bb[r][q], 0, 0, 0);
-      }
+      for (int q = 0; q < 2; ++q) acc[r][q] = __builtin_amdgcn_mfma_f64_16x16x4f64(fa[r], fb[q], acc[r][q], 0, 0, 0);
   }
   __syncthreads();
+}
+
+// The two products of a panel workgroup of the block-column step, from one staging of the previous
+// panel's rows (this tile's rows i0.. as A, the diagonal block's rows 0.. as B):
+//   dacc: the diagonal block's update B B^T, 2 x 2 waves of 32 x 32 as in tile_product_k64;
+//   xt:   this tile's update A B^T, transposed: wave w forms the 64 x 16 strip (B A^T)[:, 16w .. 16w + 15],
+//         so entry r of xt[jb] in lane l is (A B^T)[16w + l % 16][16 jb + 4 r + l / 16], exactly the A-operand
+//         fragment of k-step 4 jb + r of a product whose left factor is that tile's rows 16w .. 16w + 15.
+// Ends with a barrier.
+__device__ __forceinline__ void panel_products_k64(const double* A, const double* B, int64_t lda, int64_t ldb,
+                                                   int M, int N, int i0, double* As, double* Bs,
+                                                   f64x4 (&dacc)[2][2], f64x4 (&xt)[4]) {
+  constexpr int T = 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int lk = lane >> 4, lc = lane & 15;
+  k64_stage(A, B, lda, ldb, M, N, i0, 0, As, Bs);
+#pragma unroll
+  for (int p = 0; p < 2; ++p)
+#pragma unroll
+    for (int q = 0; q < 2; ++q) dacc[p][q] = f64x4{0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int jb = 0; jb < 4; ++jb) xt[jb] = f64x4{0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int k4 = 0; k4 < T; k4 += 4) {
+    const int kr = k4 + lk;
+    double fb[4], fo;
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb) fb[jb] = Bs[(jb * 16 + lc) * K64S + kr];
+    fo = As[(wave * 16 + lc) * K64S + kr];
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+        dacc[r][q] = __builtin_amdgcn_mfma_f64_16x16x4f64(fb[2 * wm + r], fb[2 * wn + q], dacc[r][q], 0, 0, 0);
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb) xt[jb] = __builtin_amdgcn_mfma_f64_16x16x4f64(fb[jb], fo, xt[jb], 0, 0, 0);
+  }
+  __syncthreads();
+}
+
+// C = alpha A B + beta C for one 64 x 64 tile with K = 64, A (64 x 64) and B (64 x 64) row-major: rows of A
+// and C at or past mrows are zero / not stored, rows of B at or past krows are zero. A is staged as [i][k]
+// with rows of 68 doubles, B as [k][j] with rows of 80 (as in k_dgemm_nn_smallk); 4 waves in 2 x 2. C may
+// be B itself: all of B is in LDS before C is written. beta == 0 reads no C.
+constexpr int NN_BS = 80;
+constexpr int NN64_LDS = 64 * K64S + 64 * NN_BS;  // doubles
+__device__ __forceinline__ void nn64(const double* A, int64_t lda, const double* B, int64_t ldb, double* C,
+                                     int64_t ldc, int mrows, int krows, double alpha, double beta, double* As,
+                                     double* Bs) {
+  constexpr int T = 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int lk = lane >> 4, lc = lane & 15;
+  double2 ra[8], rb[8];
+#pragma unroll
+  for (int v = 0; v < 8; ++v) {
+    const int e = tid + 256 * v, r = e >> 5, c2 = (e & 31) * 2;
+    ra[v] = (r < mrows) ? make_double2(A[(int64_t)r * lda + c2], A[(int64_t)r * lda + c2 + 1]) : make_double2(0.0, 0.0);
+    rb[v] = (r < krows) ? make_double2(B[(int64_t)r * ldb + c2], B[(int64_t)r * ldb + c2 + 1]) : make_double2(0.0, 0.0);
+  }
+#pragma unroll
+  for (int v = 0; v < 8; ++v) {
+    const int e = tid + 256 * v, r = e >> 5, c2 = (e & 31) * 2;
+    *reinterpret_cast<double2*>(&As[r * K64S + c2]) = ra[v];
+    *reinterpret_cast<double2*>(&Bs[r * NN_BS + c2]) = rb[v];
+  }
+  __syncthreads();
+  f64x4 acc[2][2];
+#pragma unroll
+  for (int p = 0; p < 2; ++p)
+#pragma unroll
+    for (int q = 0; q < 2; ++q) acc[p][q] = f64x4{0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int k4 = 0; k4 < T; k4 += 4) {
+    const int kr = k4 + lk;
+    double fa[2], fb[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) fa[r] = As[(wm * 32 + r * 16 + lc) * K64S + kr];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) fb[q] = Bs[kr * NN_BS + wn * 32 + q * 16 + lc];
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int q = 0; q < 2; ++q) acc[r][q] = __builtin_amdgcn_mfma_f64_16x16x4f64(fa[r], fb[q], acc[r][q], 0, 0, 0);
+  }
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = wm * 32 + r * 16 + 4 * e + lk, j = wn * 32 + q * 16 + lc;
+        if (i < mrows) {
+          double* ptr = C + (int64_t)i * ldc + j;
+          const double v = alpha * acc[r][q][e];
+          *ptr = (beta == 0.0) ? v : fma(beta, *ptr, v);
+        }
+      }
+}
+
+}  // namespace
+
+// Tiles of launch f.k of the inverse: G tiles of step k - 1, update tiles of step k - 2, scaling tiles of
+// step k - 3 (see InvFill in dgemm.h).
+__host__ __device__ inline void inv_fill_counts(const InvFill& f, int& na, int& nb, int& nc) {
+  const int ta = f.k - 1, tb = f.k - 2, tc = f.k - 3;
+  na = (ta >= 0 && ta < f.S - 1) ? f.S - 1 - ta : 0;               // blocks i > ta
+  nb = (tb >= 0 && tb < f.S - 1) ? (f.S - 1 - tb) * (tb + 1) : 0;  // i > tb, j <= tb
+  nc = (tc >= 0 && tc < f.S) ? tc + 1 : 0;                         // j <= tc
+}
+
+int inv_fill_tiles(const InvFill& f) {
+  int na, nb, nc;
+  inv_fill_counts(f, na, nb, nc);
+  return na + nb + nc;
+}
+
+namespace {
+
+__device__ __forceinline__ void inv_fill_tile(const InvFill& f, int t, double* lds) {
+  constexpr int T = 64;
+  int na, nb, nc;
+  inv_fill_counts(f, na, nb, nc);
+  double* As = lds;
+  double* Bs = lds + 64 * K64S;
+  const int d = f.d;
+  if (t < na) {
+    // G_{i,ta} = L_{i,ta} Dinv_ta, block row i > ta (rows past d skipped)
+    const int ta = f.k - 1, i = ta + 1 + t;
+    double* G = f.G[ta & 1] + (int64_t)i * T * T;
+    nn64(f.L + (int64_t)i * T * d + (int64_t)ta * T, d, f.Dinv + (int64_t)ta * T * T, T, G, T, min(T, d - i * T), T,
+         1.0, 0.0, As, Bs);
+    return;
+  }
+  t -= na;
+  if (t < nb) {
+    // Z_{i,j} -= G_{i,tb} Z_{tb,j} (j < tb), Z_{i,tb} = -G_{i,tb}
+    const int tb = f.k - 2, i = tb + 1 + t / (tb + 1), j = t % (tb + 1);
+    const double* G = f.G[tb & 1] + (int64_t)i * T * T;
+    double* Zij = f.Z + (int64_t)i * T * d + (int64_t)j * T;
+    const int mrows = min(T, d - i * T);
+    if (j < tb) {
+      nn64(G, T, f.Z + (int64_t)tb * T * d + (int64_t)j * T, d, Zij, d, mrows, T, -1.0, 1.0, As, Bs);
+    } else {
+      for (int e = threadIdx.x; e < T * T; e += 256) {
+        const int r = e / T, c = e % T;
+        if (r < mrows) Zij[(int64_t)r * d + c] = -G[e];
+      }
+    }
+    return;
+  }
+  t -= nb;
+  // Z_{tc,j} = Dinv_tc Z_{tc,j} (j < tc, in place), Z_{tc,tc} = Dinv_tc
+  const int tc = f.k - 3, j = t;
+  const double* D = f.Dinv + (int64_t)tc * T * T;
+  double* Ztj = f.Z + (int64_t)tc * T * d + (int64_t)j * T;
+  const int rows = min(T, d - tc * T);
+  if (j < tc) {
+    nn64(D, T, Ztj, d, Ztj, d, rows, rows, 1.0, 0.0, As, Bs);
+  } else {
+    for (int e = threadIdx.x; e < T * T; e += 256) {
+      const int r = e / T, c = e % T;
+      if (r < rows && c < rows) Ztj[(int64_t)r * d + c] = D[e];
+    }
+  }
+}
+
+__global__ __launch_bounds__(256, 2) void k_inv_fill(InvFill f) {
+  __shared__ __attribute__((aligned(16))) double lds[NN64_LDS];
+  inv_fill_tile(f, (int)blockIdx.x, lds);
 }
 
 // Block-column step of the factorization (T = 64, C = A B^T update with beta = 1, kmode FULL). C is the
@@ -342,21 +494,32 @@ __device__ __forceinline__ void tile_product_k64(const double* A, const double* 
 //    diag_Dinv[kb], bad pivots to diag_status. The block in C itself is not written in this launch;
 //  * tiles (I >= 1, 0): the updated tile X and, again, D from the same inputs (so every one of these
 //    workgroups gets the same factor as tile (0, 0) without waiting for it); X is then solved,
-//    X L^T = X by forward substitution, and written in place: the panel of the next step.
-// With K = 0 the update is empty and the launch only factors the block and solves the panel.
+//    X (L^-1)^T on the matrix cores from X held in registers, and written in place: the panel of the
+//    next step.
+// K is 64, or 0 for the first step of an outer block (no update: the launch only factors the block and
+// solves the panel). Further workgroups past the step's own tiles take tiles of a deferred update xa.
 template <int T>
-__global__ __launch_bounds__(256) void k_colstep(DgemmArgs a, DgemmArgs xa, int x_first, int n_own) {
+__global__ __launch_bounds__(256, 2) void k_colstep(DgemmArgs a, DgemmArgs xa, int x_first, int n_own,
+                                                   int x_count, InvFill fl) {
   static_assert(T == diagblock::NB, "the diagonal block is one tile");
   using L = Lds<T>;
-  // operands (2 x 64 rows of K64S for the step's own K = 64 product, or the ring of tile_product for
-  // other K and for deferred tiles); later the tile X
+  // One LDS buffer, two uses in turn: the operands (2 x 64 rows of K64S for the step's own K = 64
+  // products, or the ring of tile_product for the deferred tiles), then the diagonal block and its
+  // inverse for the factorization (the products end with a barrier). About 70 KB, so two workgroups
+  // share a CU.
   constexpr int AB_SZ = (2 * T * K64S > 4 * L::SZ) ? 2 * T * K64S : 4 * L::SZ;
-  __shared__ __attribute__((aligned(16))) double ABs[AB_SZ];
-  __shared__ diagblock::BlockSmem bsm;
-  static_assert(AB_SZ >= T * (T + 1), "tile buffer");
+  constexpr int BSM_SZ = (int)(sizeof(diagblock::BlockSmem) / sizeof(double));
+  constexpr int SZ1 = AB_SZ > BSM_SZ ? AB_SZ : BSM_SZ;
+  __shared__ __attribute__((aligned(16))) double ABs[SZ1 > NN64_LDS ? SZ1 : NN64_LDS];
+  diagblock::BlockSmem& bsm = *reinterpret_cast<diagblock::BlockSmem*>(ABs);
   double(*As)[L::SZ] = reinterpret_cast<double(*)[L::SZ]>(ABs);
   double(*Bs)[L::SZ] = reinterpret_cast<double(*)[L::SZ]>(ABs + 2 * L::SZ);
 
+  if ((int)blockIdx.x >= n_own + x_count) {
+    // a tile of the inverse L^-1 (independent of this step's own work)
+    inv_fill_tile(fl, (int)blockIdx.x - n_own - x_count, ABs);
+    return;
+  }
   if ((int)blockIdx.x >= n_own) {
     // a tile of the deferred trailing update xa (lower tiles of a square region, in tile order from
     // x_first): independent of this step's own work, it fills CUs the step leaves idle
@@ -389,7 +552,7 @@ __global__ __launch_bounds__(256) void k_colstep(DgemmArgs a, DgemmArgs xa, int 
   const int ntn = (a.N + T - 1) / T;
   const int I = blockIdx.x / ntn, J = blockIdx.x - I * ntn;
   if (I < J) return;
-  const int M = a.M, N = a.N, K = a.K;
+  const int M = a.M, N = a.N, K = a.K;  // K is 0 or 64
   const int i0 = I * T, j0 = J * T;
   if (i0 >= M || j0 >= N) return;
   const double* A = a.A;
@@ -400,39 +563,16 @@ __global__ __launch_bounds__(256) void k_colstep(DgemmArgs a, DgemmArgs xa, int 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int lk = lane >> 4, lc = lane & 15;
-  // element (r, q, e) of a thread's fragments is tile entry (ti(r, e), tj(q))
+  // element (r, q, e) of a 2 x 2-wave accumulator is tile entry (ti(r, e), tj(q))
   auto ti = [&](int r, int e) { return wm * (T / 2) + r * 16 + 4 * e + lk; };
   auto tj = [&](int q) { return wn * (T / 2) + q * 16 + lc; };
   const int m = min(T, N);  // size of the diagonal block
-  // column 0: the old values of this tile and of the diagonal block are loaded before the products,
-  // so their latency overlaps them
-  double cown[FR][FC][4], cdiag[FR][FC][4];
-  if (J == 0) {
-#pragma unroll
-    for (int r = 0; r < FR; ++r)
-#pragma unroll
-      for (int q = 0; q < FC; ++q)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = ti(r, e), j = tj(q);
-          const bool din = (i < m && j < m && j <= i);
-          cdiag[r][q][e] = din ? C[(int64_t)i * a.ldc + j] : 0.0;
-          const bool oin = (i0 + i < M && j < m);
-          cown[r][q][e] = (I > 0 && oin) ? C[(int64_t)(i0 + i) * a.ldc + j] : 0.0;
-        }
-  }
-  f64x4 acc[FR][FC];
-  f64x4 dacc[FR][FC];  // column 0 below the diagonal: the diagonal block's product, from the same B
-  if (K == T) {
-    if (J == 0 && I > 0) tile_product_k64<true>(A, B, a.lda, a.ldb, M, N, i0, j0, ABs, ABs + T * K64S, acc, dacc);
-    else tile_product_k64<false>(A, B, a.lda, a.ldb, M, N, i0, j0, ABs, ABs + T * K64S, acc);
-  } else if (J == 0 && I > 0) {
-    tile_product<false, true, T, true>(a, A, B, M, N, K, i0, j0, 0, K, As, Bs, acc, dacc);
-  } else {
-    tile_product<false, true, T>(a, A, B, M, N, K, i0, j0, 0, K, As, Bs, acc);
-  }
 
   if (J != 0) {
+    // the update C -= A B^T of a tile to the right of the panel
+    if (K == 0) return;
+    f64x4 acc[FR][FC];
+    tile_product_k64(A, B, a.lda, a.ldb, M, N, i0, j0, ABs, ABs + T * K64S, acc);
     const bool diag_tile = (I == J);
 #pragma unroll
     for (int r = 0; r < FR; ++r)
@@ -449,6 +589,18 @@ __global__ __launch_bounds__(256) void k_colstep(DgemmArgs a, DgemmArgs xa, int 
     return;
   }
 
+  // column 0: the diagonal block's old values (2 x 2-wave layout) are loaded before the products, so
+  // their latency overlaps them
+  double cdiag[FR][FC][4];
+#pragma unroll
+  for (int r = 0; r < FR; ++r)
+#pragma unroll
+    for (int q = 0; q < FC; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = ti(r, e), j = tj(q);
+        cdiag[r][q][e] = (i < m && j < m && j <= i) ? C[(int64_t)i * a.ldc + j] : 0.0;
+      }
   // the updated diagonal block, staged for the factorization (lower part; identity past the edge)
   auto stage_diag = [&](const f64x4 (&d)[FR][FC]) {
 #pragma unroll
@@ -464,6 +616,15 @@ __global__ __launch_bounds__(256) void k_colstep(DgemmArgs a, DgemmArgs xa, int 
         }
   };
   if (I == 0) {
+    f64x4 acc[FR][FC];
+    if (K == T) {
+      tile_product_k64(A, B, a.lda, a.ldb, M, N, 0, 0, ABs, ABs + T * K64S, acc);
+    } else {
+#pragma unroll
+      for (int r = 0; r < FR; ++r)
+#pragma unroll
+        for (int q = 0; q < FC; ++q) acc[r][q] = f64x4{0.0, 0.0, 0.0, 0.0};
+    }
     stage_diag(acc);
     __syncthreads();
     const unsigned flags = diagblock::factor_invert_blocked(bsm);
@@ -477,49 +638,61 @@ __global__ __launch_bounds__(256) void k_colstep(DgemmArgs a, DgemmArgs xa, int 
     if (flags && tid == 0) atomicOr(a.diag_status, flags);
     return;
   }
-  // this tile, updated, into LDS as the left operand of the solve ([i][k], rows of K64S doubles)
-  double* Xa = ABs;
+  // A panel tile X (rows i0 .. i0 + 63 of column 0): wave w holds rows 16w .. 16w + 15 of X in the
+  // A-operand layout of the solve, x[jb][r] = X[16w + lc][16 jb + 4 r + lk] (see panel_products_k64).
+  const int xrow = i0 + 16 * wave + lc;
+  double x[4][4];
 #pragma unroll
-  for (int r = 0; r < FR; ++r)
+  for (int jb = 0; jb < 4; ++jb)
 #pragma unroll
-    for (int q = 0; q < FC; ++q)
+    for (int r = 0; r < 4; ++r) {
+      const int j = 16 * jb + 4 * r + lk;
+      x[jb][r] = (xrow < M && j < m) ? C[(int64_t)xrow * a.ldc + j] : 0.0;
+    }
+  f64x4 dacc[FR][FC];
+  if (K == T) {
+    f64x4 xt[4];
+    panel_products_k64(A, B, a.lda, a.ldb, M, N, i0, ABs, ABs + T * K64S, dacc, xt);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int gi = i0 + ti(r, e), gj = tj(q);
-        Xa[ti(r, e) * K64S + tj(q)] = (gi < M && gj < m) ? fma(a.beta, cown[r][q][e], a.alpha * acc[r][q][e]) : 0.0;
+    for (int jb = 0; jb < 4; ++jb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = 16 * jb + 4 * r + lk;
+        x[jb][r] = (xrow < M && j < m) ? fma(a.beta, x[jb][r], a.alpha * xt[jb][r]) : 0.0;
       }
+  } else {
+#pragma unroll
+    for (int r = 0; r < FR; ++r)
+#pragma unroll
+      for (int q = 0; q < FC; ++q) dacc[r][q] = f64x4{0.0, 0.0, 0.0, 0.0};
+  }
   // the diagonal block again from the same inputs (no waiting on tile (0, 0)), factored and inverted
   stage_diag(dacc);
   __syncthreads();
   diagblock::factor_invert_blocked(bsm);
-  // the panel tile X L^-T = X (L^-1)^T: out[i][j] = sum_k X[i][k] L^-1[j][k], on the matrix cores
-  f64x4 sol[FR][FC];
+  // the panel tile X L^-T = X (L^-1)^T: out[i][j'] = sum_j X[i][j] L^-1[j'][j], on the matrix cores, wave w
+  // forming rows 16w .. 16w + 15
+  f64x4 sol[4];
 #pragma unroll
-  for (int p = 0; p < FR; ++p)
+  for (int q = 0; q < 4; ++q) sol[q] = f64x4{0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-    for (int q = 0; q < FC; ++q) sol[p][q] = f64x4{0.0, 0.0, 0.0, 0.0};
+  for (int jb = 0; jb < 4; ++jb)
 #pragma unroll
-  for (int k4 = 0; k4 < T; k4 += 4) {
-    const int kr = k4 + lk;
-    double fa[FR], fb[FC];
+    for (int r = 0; r < 4; ++r) {
+      const int kr = 16 * jb + 4 * r + lk;
+      double fb[4];
 #pragma unroll
-    for (int r = 0; r < FR; ++r) fa[r] = Xa[(wm * (T / 2) + r * 16 + lc) * K64S + kr];
+      for (int q = 0; q < 4; ++q) fb[q] = bsm.M[16 * q + lc][kr];
 #pragma unroll
-    for (int q = 0; q < FC; ++q) fb[q] = bsm.M[wn * (T / 2) + q * 16 + lc][kr];
+      for (int q = 0; q < 4; ++q) sol[q] = __builtin_amdgcn_mfma_f64_16x16x4f64(x[jb][r], fb[q], sol[q], 0, 0, 0);
+    }
 #pragma unroll
-    for (int r = 0; r < FR; ++r)
+  for (int q = 0; q < 4; ++q)
 #pragma unroll
-      for (int q = 0; q < FC; ++q) sol[r][q] = __builtin_amdgcn_mfma_f64_16x16x4f64(fa[r], fb[q], sol[r][q], 0, 0, 0);
-  }
-#pragma unroll
-  for (int r = 0; r < FR; ++r)
-#pragma unroll
-    for (int q = 0; q < FC; ++q)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int gi = i0 + ti(r, e), gj = tj(q);
-        if (gi < M && gj < m) C[(int64_t)gi * a.ldc + gj] = sol[r][q][e];
-      }
+    for (int e = 0; e < 4; ++e) {
+      const int gi = i0 + 16 * wave + 4 * e + lk, gj = 16 * q + lc;
+      if (gi < M && gj < m) C[(int64_t)gi * a.ldc + gj] = sol[q][e];
+    }
 }
 
 }  // namespace
@@ -797,14 +970,26 @@ hipError_t dgemm_launch(const DgemmArgs& a, bool ta, bool tb, int batches, hipSt
   return dgemm_launch_t<64>(a, ta, tb, batches, stream);
 }
 
-hipError_t colstep_launch(const DgemmArgs& a, const DgemmArgs* x, int x_first, int x_count, hipStream_t stream) {
-  if (a.M <= 0 || a.N <= 0 || a.N > a.M || a.K < 0 || !a.diag_Lstage || !a.diag_Dinv || !a.diag_status)
+hipError_t colstep_launch(const DgemmArgs& a, const DgemmArgs* x, int x_first, int x_count, const InvFill* f,
+                          hipStream_t stream) {
+  if (a.M <= 0 || a.N <= 0 || a.N > a.M || (a.K != 0 && a.K != 64) || !a.diag_Lstage || !a.diag_Dinv ||
+      !a.diag_status)
     return hipErrorInvalidValue;
   const int tiles = ((a.M + 63) / 64) * ((a.N + 63) / 64);
   DgemmArgs none{};
   if (!x || x_count < 0) x_count = 0;
   if (x_count > 0 && (x->M != x->N || x->kmode != KMODE_FULL)) return hipErrorInvalidValue;
-  k_colstep<64><<<dim3(tiles + x_count), dim3(256), 0, stream>>>(a, x_count > 0 ? *x : none, x_first, tiles);
+  const InvFill nof{};
+  const int f_count = f ? inv_fill_tiles(*f) : 0;
+  k_colstep<64><<<dim3(tiles + x_count + f_count), dim3(256), 0, stream>>>(a, x_count > 0 ? *x : none, x_first, tiles,
+                                                                           x_count, f ? *f : nof);
+  return hipGetLastError();
+}
+
+hipError_t inv_fill_launch(const InvFill& f, hipStream_t stream) {
+  const int n = inv_fill_tiles(f);
+  if (n <= 0) return hipSuccess;
+  k_inv_fill<<<dim3(n), dim3(256), 0, stream>>>(f);
   return hipGetLastError();
 }
 

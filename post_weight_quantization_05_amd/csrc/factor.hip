@@ -13,13 +13,15 @@
 //  k_perm         act_order permutation by ranks (descending key, ties by index): a stable sort.
 //  k_gather       H_p = P^T H P (optionally index-reversed) from S's lower triangle, lower part only.
 //  k_colstep      (dgemm.hip) one 64-column step of the blocked factorization: block-column update,
-//                 the next 64 x 64 diagonal block factored (one wave, lane = row, rsqrt-refined pivots)
-//                 and inverted (four waves, a quad of lanes per column; diagblock.h), the next panel
-//                 solved; flags pivots that are not > 0 or not finite.
+//                 the next 64 x 64 diagonal block factored and inverted in 16-column sub-blocks
+//                 (diagblock.h), the next panel solved on the matrix cores; flags pivots that are
+//                 not > 0 or not finite. Its spare workgroups carry deferred trailing-update tiles and
+//                 the tiles of L^-1 (InvFill in dgemm.h), two steps behind the factorization.
+//  k_inv_fill     (dgemm.hip) the last tiles of L^-1, after the last step.
 //  k_place_lblocks the staged factors of the diagonal blocks into A.
-//  panel / SYRK / triangular-inverse levels / H^-1 = L^-T L^-1 use the fp64 MFMA GEMM core (dgemm.hip).
-// Routes (flags): INVERSE_RECHOL = potrf, trtri, lauum, potrf, transpose (the guide's order);
-// REVERSED = potrf and trtri of J H J, then U = J L^-1 J (same unique U, half the work).
+//  trailing SYRK updates and H^-1 = L^-T L^-1 use the fp64 MFMA GEMM core (dgemm.hip).
+// Routes (flags): INVERSE_RECHOL = potrf with L^-1, lauum, potrf, transpose (the guide's order);
+// REVERSED = potrf with L^-1 of J H J, then U = J L^-1 J (same unique U, half the work).
 #include <algorithm>
 #include <type_traits>
 
@@ -160,19 +162,6 @@ __global__ __launch_bounds__(256) void k_place_lblocks(const double* __restrict_
   }
 }
 
-// Copy the inverted diagonal blocks into the diagonal of A (start of the triangular inverse).
-__global__ __launch_bounds__(256) void k_place_dinv(const double* __restrict__ Dinv, double* __restrict__ A,
-                                                    int64_t lda, int d) {
-  const int kb = blockIdx.x;
-  const int o = kb * NB;
-  const int m = min(NB, d - o);
-  const double* D = Dinv + (int64_t)kb * NB * NB;
-  for (int e = threadIdx.x; e < NB * NB; e += 256) {
-    const int k = e / NB, j = e % NB;
-    if (k < m && j < m) A[(int64_t)(o + k) * lda + o + j] = D[e];
-  }
-}
-
 // U = L^T in place: lower triangle moved to the upper, lower set to 0 (32 x 32 tiles through LDS).
 __global__ __launch_bounds__(256) void k_transpose_lower_to_upper(double* __restrict__ U, int d) {
   __shared__ double t1[32][33];
@@ -229,10 +218,20 @@ constexpr int NBO = GPTQ_FACTOR_NBO;  // outer block width (a multiple of 64)
 #endif
 constexpr int DEFER_PER_STEP = GPTQ_FACTOR_DEFER;  // deferred trailing tiles per block-column step
 
-// place_l: copy the diagonal blocks' factors into A at the end (not needed when the caller next replaces
-// those blocks with their inverses, as the triangular inverse does)
-hipError_t potrf_lower(double* A, int d, double* Dinv, double* Lst, unsigned* status, bool place_l,
-                       hipStream_t stream) {
+// place_l: copy the diagonal blocks' factors into A at the end.
+// Z, G (both null, or Z d x d and G two buffers of 64 rows per block x 64): also form Z = L^-1 (lower part)
+// with the steps' idle CUs (InvFill in dgemm.h), finished by three launches after the last step.
+hipError_t potrf_lower(double* A, int d, double* Dinv, double* Lst, unsigned* status, bool place_l, double* Z,
+                       double* G, hipStream_t stream) {
+  const int S = (d + NB - 1) / NB;
+  InvFill inv{};
+  inv.L = A;
+  inv.Dinv = Dinv;
+  inv.Z = Z;
+  inv.G[0] = G;
+  inv.G[1] = G ? G + (int64_t)S * NB * NB : nullptr;
+  inv.d = d;
+  inv.S = S;
   // The trailing update of an outer block is split in two: the next outer block's columns right away
   // (its first step needs them), the rest (columns from the block after that on) deferred and spread over
   // the next outer block's steps as extra workgroups. Per tile the arithmetic is unchanged.
@@ -251,7 +250,8 @@ hipError_t potrf_lower(double* A, int d, double* Dinv, double* Lst, unsigned* st
     s.kmode = KMODE_FULL;
     s.diag_kb = c1 / NB; s.diag_Lstage = Lst; s.diag_Dinv = Dinv; s.diag_status = status;
     share = min(share, pend_tiles - pend_done);
-    const hipError_t e = colstep_launch(s, &pend, pend_done, share, stream);
+    inv.k = c1 / NB;
+    const hipError_t e = colstep_launch(s, &pend, pend_done, share, Z ? &inv : nullptr, stream);
     pend_done += share;
     return e;
   };
@@ -314,43 +314,16 @@ hipError_t potrf_lower(double* A, int d, double* Dinv, double* Lst, unsigned* st
       }
     }
   }
+  if (Z) {
+    for (inv.k = S; inv.k < S + 3; ++inv.k) {
+      e = inv_fill_launch(inv, stream);
+      if (e != hipSuccess) return e;
+    }
+  }
   if (!place_l) return hipSuccess;
   const int nblk = (d + NB - 1) / NB;
   hipLaunchKernelGGL(k_place_lblocks, dim3(nblk), dim3(256), 0, stream, Lst, A, (int64_t)d, d);
   return hipGetLastError();
-}
-
-// L (lower, in A, diagonal blocks already replaced by their inverses) -> L^-1 in place. T is scratch of
-// at least d*d doubles. Level s joins diagonal blocks of size s into 2s:
-//   [L11 0; L21 L22]^-1 = [L11^-1 0; -L22^-1 L21 L11^-1  L22^-1]
-hipError_t trtri_lower(double* A, int d, double* T, hipStream_t stream) {
-  for (int s = NB; s < d; s *= 2) {
-    const int pairs = (d - s + 2 * s - 1) / (2 * s);
-    // T_p = L21_p * Li11_p  (Li11 lower: k >= j)
-    DgemmArgs g1{};
-    g1.A = A + (int64_t)s * d; g1.lda = d; g1.strideA = (int64_t)2 * s * d + 2 * s;
-    g1.B = A; g1.ldb = d; g1.strideB = (int64_t)2 * s * d + 2 * s;
-    g1.C = T; g1.ldc = s; g1.strideC = (int64_t)s * s;
-    g1.M = s; g1.N = s; g1.K = s;
-    g1.m_lim = d - s; g1.m_step = 2 * s;
-    g1.alpha = 1.0; g1.beta = 0.0;
-    g1.kmode = KMODE_GE_J;
-    hipError_t e = dgemm_launch(g1, false, false, pairs, stream);
-    if (e != hipSuccess) return e;
-    // L21_p <- -Li22_p * T_p  (Li22 lower: k <= i; K limited to the block's rows)
-    DgemmArgs g2{};
-    g2.A = A + (int64_t)s * d + s; g2.lda = d; g2.strideA = (int64_t)2 * s * d + 2 * s;
-    g2.B = T; g2.ldb = s; g2.strideB = (int64_t)s * s;
-    g2.C = A + (int64_t)s * d; g2.ldc = d; g2.strideC = (int64_t)2 * s * d + 2 * s;
-    g2.M = s; g2.N = s; g2.K = s;
-    g2.m_lim = d - s; g2.m_step = 2 * s;
-    g2.k_by_m = 1;
-    g2.alpha = -1.0; g2.beta = 0.0;
-    g2.kmode = KMODE_LT_I_END;
-    e = dgemm_launch(g2, false, false, pairs, stream);
-    if (e != hipSuccess) return e;
-  }
-  return hipSuccess;
 }
 
 }  // namespace
@@ -360,6 +333,8 @@ size_t prepare_ws_bytes(int64_t in) {
   const int64_t nblk = ceil_div(d, NB);
   size_t b = 0;
   b += align_up((size_t)d * d * sizeof(double), 256);          // A
+  b += align_up((size_t)d * d * sizeof(double), 256);          // Z = L^-1
+  b += align_up((size_t)2 * nblk * NB * NB * sizeof(double), 256);  // G (two buffers)
   b += align_up((size_t)nblk * NB * NB * sizeof(double), 256);  // Dinv
   b += align_up((size_t)nblk * NB * NB * sizeof(double), 256);  // staged factors of the diagonal blocks
   b += align_up((size_t)d * sizeof(double), 256);              // diag of H
@@ -375,6 +350,10 @@ hipError_t prepare_launch(const double* S, const double* colsq, int64_t n_total,
   char* w = reinterpret_cast<char*>(ws);
   double* A = reinterpret_cast<double*>(w);
   w += align_up((size_t)d * d * sizeof(double), 256);
+  double* Z = reinterpret_cast<double*>(w);
+  w += align_up((size_t)d * d * sizeof(double), 256);
+  double* G = reinterpret_cast<double*>(w);
+  w += align_up((size_t)2 * nblk * NB * NB * sizeof(double), 256);
   double* Dinv = reinterpret_cast<double*>(w);
   w += align_up((size_t)nblk * NB * NB * sizeof(double), 256);
   double* Lst = reinterpret_cast<double*>(w);
@@ -401,26 +380,23 @@ hipError_t prepare_launch(const double* S, const double* colsq, int64_t n_total,
                      d, reversed ? 1 : 0, A);
   GPTQ_TRY(hipGetLastError());
 
-  GPTQ_TRY(potrf_lower(A, d, Dinv, Lst, status, false, stream));  // k_place_dinv follows
-  hipLaunchKernelGGL(k_place_dinv, dim3((unsigned)nblk), dim3(256), 0, stream, Dinv, A, (int64_t)d, d);
-  GPTQ_TRY(hipGetLastError());
-  GPTQ_TRY(trtri_lower(A, d, U /* scratch */, stream));
+  GPTQ_TRY(potrf_lower(A, d, Dinv, Lst, status, false, Z, G, stream));  // and Z = L^-1
   if (reversed) {
     hipLaunchKernelGGL(k_reverse_to_upper, dim3((unsigned)ceil_div(d, 256), (unsigned)std::min(d, 4096)), dim3(256),
-                       0, stream, A, d, U);
+                       0, stream, Z, d, U);
     GPTQ_TRY(hipGetLastError());
   } else {
     // H^-1 = Li^T Li (lower tiles) into U, then its Cholesky factor, then U = Lu^T
     DgemmArgs g{};
-    g.A = A; g.lda = d;
-    g.B = A; g.ldb = d;
+    g.A = Z; g.lda = d;
+    g.B = Z; g.ldb = d;
     g.C = U; g.ldc = d;
     g.M = d; g.N = d; g.K = d;
     g.alpha = 1.0; g.beta = 0.0;
     g.tri_tiles = 1;
     g.kmode = KMODE_GE_I;
     GPTQ_TRY(dgemm_launch(g, true, false, 1, stream));
-    GPTQ_TRY(potrf_lower(U, d, Dinv, Lst, status, true, stream));
+    GPTQ_TRY(potrf_lower(U, d, Dinv, Lst, status, true, nullptr, nullptr, stream));
     const int nt = (d + 31) / 32;
     hipLaunchKernelGGL(k_transpose_lower_to_upper, dim3(nt * (nt + 1) / 2), dim3(256), 0, stream, U, d);
     GPTQ_TRY(hipGetLastError());

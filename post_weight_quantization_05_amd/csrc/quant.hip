@@ -55,20 +55,19 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-// value of lane K of this lane's 16-lane row
+// value of lane K of this lane's 16-lane row (one v_mov_b64_dpp, row_newbcast)
 template <int K>
 __device__ __forceinline__ double bcast16(double v) {
-  const long long x = __double_as_longlong(v);
-  const int lo = __builtin_amdgcn_update_dpp(0, (int)(x & 0xFFFFFFFFll), 0x150 + K, 0xF, 0xF, false);
-  const int hi = __builtin_amdgcn_update_dpp(0, (int)(x >> 32), 0x150 + K, 0xF, 0xF, false);
-  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+  return __builtin_amdgcn_mov_dpp(v, 0x150 + K, 0xF, 0xF, false);
 }
 
+// value of lane (i - R) mod 16 of this lane's 16-lane row (DPP row_ror; 64-bit DPP takes only row_newbcast,
+// so the two halves move separately)
 template <int R>
 __device__ __forceinline__ double ror16(double v) {
   const long long x = __double_as_longlong(v);
-  const int lo = __builtin_amdgcn_update_dpp(0, (int)(x & 0xFFFFFFFFll), 0x120 + R, 0xF, 0xF, false);
-  const int hi = __builtin_amdgcn_update_dpp(0, (int)(x >> 32), 0x120 + R, 0xF, 0xF, false);
+  const int lo = __builtin_amdgcn_mov_dpp((int)(x & 0xFFFFFFFFll), 0x120 + R, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_mov_dpp((int)(x >> 32), 0x120 + R, 0xF, 0xF, false);
   return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
 }
 
