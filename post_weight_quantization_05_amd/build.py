@@ -38,11 +38,11 @@ def sources():
 
 
 # A test build of the same library in which every fp64 product takes the chunked-ring GEMM (the small-K
-# kernels' tile cutoff set to 0), so that parity tests cover those routes at small sizes too. Only the
-# GEMM source differs; the tests load it beside the main library.
+# kernels' tile cutoff set to 0) and the factorization forms L^-1 by the level-wise doubling at every size
+# (the step-carried route's cutoff set to 0), so that parity tests cover those routes at small sizes too.
+# Only these sources differ; the tests load it beside the main library.
 VARIANT_LIB = os.path.join(PKG, "libgptq_mi355x_ringonly.so")
-VARIANT_DEFS = ["-DGPTQ_DGEMM_SMALLK_TILES=0"]
-VARIANT_SRC = "dgemm.hip"
+VARIANT_DEFS = {"dgemm.hip": ["-DGPTQ_DGEMM_SMALLK_TILES=0"], "factor.hip": ["-DGPTQ_FACTOR_FILL_MAX=0"]}
 
 
 def _compile(src: str, defs=(), tag: str = "") -> str:
@@ -64,14 +64,14 @@ def build(verbose: bool = True) -> str:
         raise RuntimeError("hipcc not found; set HIPCC")
     os.makedirs(BUILD, exist_ok=True)
     srcs = sources()
-    var_src = os.path.join(CSRC, VARIANT_SRC)
-    with ThreadPoolExecutor(max_workers=min(8, len(srcs) + 1)) as ex:
+    with ThreadPoolExecutor(max_workers=min(8, len(srcs) + len(VARIANT_DEFS))) as ex:
         objs_f = ex.map(_compile, srcs)
-        var_f = ex.submit(_compile, var_src, VARIANT_DEFS, ".ringonly")
+        var_f = {name: ex.submit(_compile, os.path.join(CSRC, name), defs, ".ringonly")
+                 for name, defs in VARIANT_DEFS.items()}
         objs = list(objs_f)
-        var_obj = var_f.result()
+        var_objs = {name: f.result() for name, f in var_f.items()}
     _link(objs, LIB)
-    _link([var_obj if o.endswith(os.sep + VARIANT_SRC + ".o") else o for o in objs], VARIANT_LIB)
+    _link([var_objs.get(os.path.basename(o)[:-len(".o")], o) for o in objs], VARIANT_LIB)
     if verbose:
         print(f"built {LIB} (and the test build {os.path.basename(VARIANT_LIB)})")
     return LIB

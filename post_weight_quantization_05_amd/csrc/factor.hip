@@ -162,6 +162,19 @@ __global__ __launch_bounds__(256) void k_place_lblocks(const double* __restrict_
   }
 }
 
+// Copy the inverted diagonal blocks into the diagonal of A (start of the level-wise triangular inverse).
+__global__ __launch_bounds__(256) void k_place_dinv(const double* __restrict__ Dinv, double* __restrict__ A,
+                                                    int64_t lda, int d) {
+  const int kb = blockIdx.x;
+  const int o = kb * NB;
+  const int m = min(NB, d - o);
+  const double* D = Dinv + (int64_t)kb * NB * NB;
+  for (int e = threadIdx.x; e < NB * NB; e += 256) {
+    const int k = e / NB, j = e % NB;
+    if (k < m && j < m) A[(int64_t)(o + k) * lda + o + j] = D[e];
+  }
+}
+
 // U = L^T in place: lower triangle moved to the upper, lower set to 0 (32 x 32 tiles through LDS).
 __global__ __launch_bounds__(256) void k_transpose_lower_to_upper(double* __restrict__ U, int d) {
   __shared__ double t1[32][33];
@@ -213,10 +226,15 @@ __global__ __launch_bounds__(256) void k_reverse_to_upper(const double* __restri
 #define GPTQ_FACTOR_NBO 256
 #endif
 constexpr int NBO = GPTQ_FACTOR_NBO;  // outer block width (a multiple of 64)
+// Deferred trailing tiles per block-column step: with L^-1 in the steps (two workgroups per CU carrying
+// it) 640 (prepare at in = 4096: 2.92 ms against 3.00 with 160); without, 160 (in = 8192 / 11008: 13.7 /
+// 29.0 ms against 14.0 / 29.9 with 640).
 #ifndef GPTQ_FACTOR_DEFER
 #define GPTQ_FACTOR_DEFER 160
 #endif
-constexpr int DEFER_PER_STEP = GPTQ_FACTOR_DEFER;  // deferred trailing tiles per block-column step
+#ifndef GPTQ_FACTOR_DEFER_FILL
+#define GPTQ_FACTOR_DEFER_FILL 640
+#endif
 
 // place_l: copy the diagonal blocks' factors into A at the end.
 // Z, G (both null, or Z d x d and G two buffers of 64 rows per block x 64): also form Z = L^-1 (lower part)
@@ -232,6 +250,7 @@ hipError_t potrf_lower(double* A, int d, double* Dinv, double* Lst, unsigned* st
   inv.G[1] = G ? G + (int64_t)S * NB * NB : nullptr;
   inv.d = d;
   inv.S = S;
+  const int defer_per_step = Z ? GPTQ_FACTOR_DEFER_FILL : GPTQ_FACTOR_DEFER;
   // The trailing update of an outer block is split in two: the next outer block's columns right away
   // (its first step needs them), the rest (columns from the block after that on) deferred and spread over
   // the next outer block's steps as extra workgroups. Per tile the arithmetic is unchanged.
@@ -303,7 +322,7 @@ hipError_t potrf_lower(double* A, int d, double* Dinv, double* Lst, unsigned* st
         // the next outer block's steps take as many as they can hide (about one tile per CU that a
         // step leaves idle); the remaining tiles are launched now as a product of their own
         const int next_steps = (b2 - b1 + NB - 1) / NB;
-        pend_tiles = min(all, next_steps * DEFER_PER_STEP);
+        pend_tiles = min(all, next_steps * defer_per_step);
         if (pend_tiles < all) {
           DgemmArgs r = pend;
           r.tri_tiles = 1;
@@ -325,6 +344,49 @@ hipError_t potrf_lower(double* A, int d, double* Dinv, double* Lst, unsigned* st
   hipLaunchKernelGGL(k_place_lblocks, dim3(nblk), dim3(256), 0, stream, Lst, A, (int64_t)d, d);
   return hipGetLastError();
 }
+
+// L (lower, in A, diagonal blocks already replaced by their inverses) -> L^-1 in place. T is scratch of
+// at least d*d doubles. Level s joins diagonal blocks of size s into 2s:
+//   [L11 0; L21 L22]^-1 = [L11^-1 0; -L22^-1 L21 L11^-1  L22^-1]
+hipError_t trtri_lower(double* A, int d, double* T, hipStream_t stream) {
+  for (int s = NB; s < d; s *= 2) {
+    const int pairs = (d - s + 2 * s - 1) / (2 * s);
+    // T_p = L21_p * Li11_p  (Li11 lower: k >= j)
+    DgemmArgs g1{};
+    g1.A = A + (int64_t)s * d; g1.lda = d; g1.strideA = (int64_t)2 * s * d + 2 * s;
+    g1.B = A; g1.ldb = d; g1.strideB = (int64_t)2 * s * d + 2 * s;
+    g1.C = T; g1.ldc = s; g1.strideC = (int64_t)s * s;
+    g1.M = s; g1.N = s; g1.K = s;
+    g1.m_lim = d - s; g1.m_step = 2 * s;
+    g1.alpha = 1.0; g1.beta = 0.0;
+    g1.kmode = KMODE_GE_J;
+    hipError_t e = dgemm_launch(g1, false, false, pairs, stream);
+    if (e != hipSuccess) return e;
+    // L21_p <- -Li22_p * T_p  (Li22 lower: k <= i; K limited to the block's rows)
+    DgemmArgs g2{};
+    g2.A = A + (int64_t)s * d + s; g2.lda = d; g2.strideA = (int64_t)2 * s * d + 2 * s;
+    g2.B = T; g2.ldb = s; g2.strideB = (int64_t)s * s;
+    g2.C = A + (int64_t)s * d; g2.ldc = d; g2.strideC = (int64_t)2 * s * d + 2 * s;
+    g2.M = s; g2.N = s; g2.K = s;
+    g2.m_lim = d - s; g2.m_step = 2 * s;
+    g2.k_by_m = 1;
+    g2.alpha = -1.0; g2.beta = 0.0;
+    g2.kmode = KMODE_LT_I_END;
+    e = dgemm_launch(g2, false, false, pairs, stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// L^-1 two ways: for in <= FILL_MAX as tiles carried by the factorization's steps (their idle CUs hold
+// it: d^2 of spare workgroup slots against d^3 / 3 flops), above it as the level-wise doubling after the
+// factorization (its large products run nearer the GEMM core's rate, and the step launches would
+// otherwise grow longer than they save). Measured prepare (ms), steps / levels: in = 2048 1.17 / 1.45,
+// 4096 2.92 / 3.37, 6144 7.43 / 7.44, 8192 15.8 / 13.7, 11008 38.8 / 29.0.
+#ifndef GPTQ_FACTOR_FILL_MAX
+#define GPTQ_FACTOR_FILL_MAX 6144
+#endif
+constexpr int FILL_MAX = GPTQ_FACTOR_FILL_MAX;
 
 }  // namespace
 
@@ -380,16 +442,24 @@ hipError_t prepare_launch(const double* S, const double* colsq, int64_t n_total,
                      d, reversed ? 1 : 0, A);
   GPTQ_TRY(hipGetLastError());
 
-  GPTQ_TRY(potrf_lower(A, d, Dinv, Lst, status, false, Z, G, stream));  // and Z = L^-1
+  const bool fill = d <= FILL_MAX;
+  GPTQ_TRY(potrf_lower(A, d, Dinv, Lst, status, false, fill ? Z : nullptr, G, stream));
+  double* Li = Z;  // L^-1 (lower part)
+  if (!fill) {
+    hipLaunchKernelGGL(k_place_dinv, dim3((unsigned)nblk), dim3(256), 0, stream, Dinv, A, (int64_t)d, d);
+    GPTQ_TRY(hipGetLastError());
+    GPTQ_TRY(trtri_lower(A, d, Z /* scratch */, stream));
+    Li = A;
+  }
   if (reversed) {
     hipLaunchKernelGGL(k_reverse_to_upper, dim3((unsigned)ceil_div(d, 256), (unsigned)std::min(d, 4096)), dim3(256),
-                       0, stream, Z, d, U);
+                       0, stream, Li, d, U);
     GPTQ_TRY(hipGetLastError());
   } else {
     // H^-1 = Li^T Li (lower tiles) into U, then its Cholesky factor, then U = Lu^T
     DgemmArgs g{};
-    g.A = Z; g.lda = d;
-    g.B = Z; g.ldb = d;
+    g.A = Li; g.lda = d;
+    g.B = Li; g.ldb = d;
     g.C = U; g.ldc = d;
     g.M = d; g.N = d; g.K = d;
     g.alpha = 1.0; g.beta = 0.0;

@@ -1,10 +1,12 @@
-"""GPU parity of the library's test build in which every fp64 product takes the chunked-ring GEMM.
+"""GPU parity of the library's test build in which every fp64 product takes the chunked-ring GEMM and the
+factorization forms L^-1 by the level-wise doubling.
 
 The main library sends small products (at most 1024 tiles, small K) to single-shot kernels, so at the
 sizes the other tests use, the chunked ring's lower-triangle branch (the factorization's update of the
-next outer block) only runs for in > 16640. libgptq_mi355x_ringonly.so is the same source built with
-that cutoff at 0; here it runs the prepare cases (ragged sizes, both factorization routes, act_order)
-and a quantize case through its C ABI, against the CPU oracle.
+next outer block) only runs for in > 16640; and it forms L^-1 inside the factorization's steps up to
+in = 6144, by the doubling levels above. libgptq_mi355x_ringonly.so is the same source built with both
+cutoffs at 0; here it runs the prepare cases (ragged sizes, both factorization routes, act_order) and a
+quantize case through its C ABI, against the CPU oracle.
 """
 import numpy as np
 import pytest
