@@ -37,12 +37,12 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-# A test build of the same library in which every fp64 product takes the chunked-ring GEMM (the small-K
-# kernels' tile cutoff set to 0) and the factorization forms L^-1 by the level-wise doubling at every size
+# A test build of the same library in which every fp64 product takes the chunked-ring GEMM (the small-K and
+# large-product kernels switched off) and the factorization forms L^-1 by the level-wise doubling at every size
 # (the step-carried route's cutoff set to 0), so that parity tests cover those routes at small sizes too.
 # Only these sources differ; the tests load it beside the main library.
 VARIANT_LIB = os.path.join(PKG, "libgptq_mi355x_ringonly.so")
-VARIANT_DEFS = {"dgemm.hip": ["-DGPTQ_DGEMM_SMALLK_TILES=0"], "factor.hip": ["-DGPTQ_FACTOR_FILL_MAX=0"]}
+VARIANT_DEFS = {"dgemm.hip": ["-DGPTQ_DGEMM_SMALLK_TILES=0", "-DGPTQ_DGEMM_BIG=0"], "factor.hip": ["-DGPTQ_FACTOR_FILL_MAX=0"]}
 
 
 def _compile(src: str, defs=(), tag: str = "") -> str:

@@ -697,6 +697,114 @@ __global__ __launch_bounds__(256, 2) void k_colstep(DgemmArgs a, DgemmArgs xa, i
 
 }  // namespace
 
+// Large plain products C = alpha A B + beta C (A M x K, B K x N, both row-major, no options): the quantize
+// loop's updates by a whole outer block (K = 1024). 128 x 128 tiles, 4 waves of 64 x 64, on
+// v_mfma_f64_4x4x4_4b: on gfx950 that instruction sustains about 70 TFLOP/s where v_mfma_f64_16x16x4f64
+// stops near 45, and a wave tile this large keeps the LDS bytes per matrix-core cycle low enough for it
+// (measured on the 4096 x 3072 x 1024 update: 53.5 TFLOP/s against 46.6-48.0 for k_dgemm's 64 x 64
+// tiles). The fragments are those of the 16 x 16 form, lane l supplying A[l % 16][l / 16] and
+// B[l / 16][l % 16]; one 4x4 instruction multiplies, for each lane group g = (l % 16) / 4, the 4 x 4 blocks
+// the group holds in both operands (rows 4g.. of A, columns 4g.. of B) into lane l's entry (row
+// 4g + l / 16, column 4g + l % 4). The other block pairings take B rotated by 4, 8 and 12 lanes within
+// each row of 16 (DPP row_ror), so four instructions form a 16 x 16 product, entry t of lane l being
+// D[bmrow(l)][bmcol(l, t)]. K runs in chunks of 16 through double-buffered LDS (A as [i][k] rows of 20, B as
+// [k][j] rows of 144); fragments are read one k-step ahead.
+template <int N>
+__device__ __forceinline__ double bm_ror(double v) {  // lane i of a row of 16 takes lane (i - N) mod 16
+  return __builtin_amdgcn_mov_dpp(v, 0x120 + N, 0xF, 0xF, false);
+}
+__device__ __forceinline__ int bmrow(int lane) { return 4 * ((lane & 15) >> 2) + (lane >> 4); }
+__device__ __forceinline__ int bmcol(int lane, int t) { return 4 * ((((lane & 15) >> 2) + t) & 3) + (lane & 3); }
+constexpr int BM_T = 128, BM_K = 16;
+constexpr int BM_AS = BM_K + 4, BM_BS = BM_T + 16;
+constexpr int BM_MIN_K = 256;  // products with less K stay on k_dgemm / the small-K kernels
+constexpr int BM_MIN_TILES = 512;  // two rounds of 256 CUs at two workgroups each
+// The launch guarantees K % 16 == 0, even N, even lda and ldb, 16-byte aligned A and B, and strides below
+// 2^31, so every element pair a thread stages is one 16-byte load that lies wholly inside or outside the
+// operand.
+__global__ __launch_bounds__(256, 2) void k_dgemm_nn_big(const double* __restrict__ A, int lda,
+                                                         const double* __restrict__ B, int ldb,
+                                                         double* __restrict__ C, int ldc, int M, int N, int K,
+                                                         double alpha, double beta) {
+  __shared__ __attribute__((aligned(16))) double As[2][BM_T * BM_AS];
+  __shared__ __attribute__((aligned(16))) double Bs[2][BM_K * BM_BS];
+  const int ntn = (N + BM_T - 1) / BM_T;
+  const int I = blockIdx.x / ntn, J = blockIdx.x - I * ntn;
+  const int i0 = I * BM_T, j0 = J * BM_T;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int lk = lane >> 4, lc = lane & 15;
+  // a chunk: A 128 x 16 and B 16 x 128, four element pairs of each per thread
+  double2 ra[4], rb[4];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int e = tid + 256 * v;
+      const int gi = i0 + (e >> 3), gj = j0 + (e & 63) * 2;
+      ra[v] = gi < M ? *reinterpret_cast<const double2*>(A + (int64_t)gi * lda + k0 + (e & 7) * 2)
+                     : make_double2(0.0, 0.0);
+      rb[v] = gj < N ? *reinterpret_cast<const double2*>(B + (int64_t)(k0 + (e >> 6)) * ldb + gj)
+                     : make_double2(0.0, 0.0);
+    }
+  };
+  auto lstore = [&](int st) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int e = tid + 256 * v;
+      *reinterpret_cast<double2*>(&As[st][(e >> 3) * BM_AS + (e & 7) * 2]) = ra[v];
+      *reinterpret_cast<double2*>(&Bs[st][(e >> 6) * BM_BS + (e & 63) * 2]) = rb[v];
+    }
+  };
+  // acc[4 q + r]: row block r (rows 64 wm + 16 r ..) x column block q (columns 64 wn + 16 q ..)
+  f64x4 acc[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = f64x4{0.0, 0.0, 0.0, 0.0};
+  const int nk = K / BM_K;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int st = kt & 1;
+    if (kt + 1 < nk) gload((kt + 1) * BM_K);
+    double fa[2][4], fb[2][4];
+    auto frag = [&](int s2, int k4) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) fa[s2][r] = As[st][(64 * wm + 16 * r + lc) * BM_AS + k4 + lk];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) fb[s2][q] = Bs[st][(k4 + lk) * BM_BS + 64 * wn + 16 * q + lc];
+    };
+    frag(0, 0);
+#pragma unroll
+    for (int ks = 0; ks < BM_K / 4; ++ks) {
+      const int s2 = ks & 1;
+      if (ks + 1 < BM_K / 4) frag(s2 ^ 1, 4 * (ks + 1));
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const double br[4] = {fb[s2][q], bm_ror<12>(fb[s2][q]), bm_ror<8>(fb[s2][q]), bm_ror<4>(fb[s2][q])};
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            acc[4 * q + r][t] = __builtin_amdgcn_mfma_f64_4x4x4f64(fa[s2][r], br[t], acc[4 * q + r][t], 0, 0, 0);
+      }
+    }
+    if (kt + 1 < nk) lstore(st ^ 1);
+    __syncthreads();
+  }
+  const int mr = bmrow(lane);
+#pragma unroll
+  for (int x = 0; x < 16; ++x)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int gi = i0 + 64 * wm + 16 * (x & 3) + mr, gj = j0 + 64 * wn + 16 * (x >> 2) + bmcol(lane, t);
+      if (gi < M && gj < N) {
+        double* ptr = C + (int64_t)gi * ldc + gj;
+        const double v = alpha * acc[x][t];
+        *ptr = (beta == 0.0) ? v : fma(beta, *ptr, v);
+      }
+    }
+}
+
 // Plain products with K <= 128 and both operands row-major, C = alpha A B + beta C (A M x K, B K x N): the
 // quantize loop's updates within an outer block (K = 128). Every operand load of the 64 x 64 tile is in
 // flight at once, then the old C values; per 64 of K one LDS store, one barrier and the MFMA sequence.
@@ -954,7 +1062,20 @@ static hipError_t dgemm_launch_t(const DgemmArgs& a, bool ta, bool tb, int batch
   const bool few = tiles <= SK_TILES;
   const bool smallk = GPTQ_DGEMM_SMALLK && plain && few && !tb && a.K <= SK_MAX && !a.lower_only;
   const bool smallk_t = GPTQ_DGEMM_SMALLK_TB && plain && few && tb && a.K <= SKT_MAX;
-  if (smallk) k_dgemm_nn_smallk<<<grid, dim3(256), 0, stream>>>(a);
+#ifndef GPTQ_DGEMM_BIG
+#define GPTQ_DGEMM_BIG 1
+#endif
+  // large plain A B: 128 x 128 tiles on the 4x4 matrix-core form (at least one round of the chip's
+  // two workgroups per CU, so the larger tile does not leave CUs idle)
+  const int big_tiles = ((a.M + BM_T - 1) / BM_T) * ((a.N + BM_T - 1) / BM_T);
+  const bool big = GPTQ_DGEMM_BIG && plain && !tb && !a.lower_only && a.K >= BM_MIN_K && a.K % BM_K == 0 &&
+                   a.N % 2 == 0 && big_tiles >= BM_MIN_TILES && (a.lda & 1) == 0 && (a.ldb & 1) == 0 &&
+                   a.lda < INT32_MAX && a.ldb < INT32_MAX && a.ldc < INT32_MAX &&
+                   (reinterpret_cast<uintptr_t>(a.A) & 15) == 0 && (reinterpret_cast<uintptr_t>(a.B) & 15) == 0;
+  if (big)
+    k_dgemm_nn_big<<<dim3(big_tiles), dim3(256), 0, stream>>>(a.A, (int)a.lda, a.B, (int)a.ldb, a.C, (int)a.ldc,
+                                                            a.M, a.N, a.K, a.alpha, a.beta);
+  else if (smallk) k_dgemm_nn_smallk<<<grid, dim3(256), 0, stream>>>(a);
   else if (smallk_t) k_dgemm_smallk<true><<<grid, dim3(256), 0, stream>>>(a);
   else if (!ta && !tb) k_dgemm<false, false, T><<<grid, dim3(256), 0, stream>>>(a);
   else if (!ta && tb) k_dgemm<false, true, T><<<grid, dim3(256), 0, stream>>>(a);

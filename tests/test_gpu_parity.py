@@ -38,6 +38,9 @@ WIDE = _cfg("bf16_wide", 40, 2600, 4096, dtype="bf16", w_std=0.02, outlier_chann
 # an odd input width: U's rows (the update products' B operand) and W's rows are not 16-byte aligned, and
 # every update in the quantize loop has a ragged N
 ODD = _cfg("bf16_odd", 33, 389, 1111, dtype="bf16", w_std=0.02, outlier_channels=3, w_seed=19, x_seed=20)
+# enough rows and columns that the quantize loop's first outer-block update (4100 x 1978, K = 1024) takes
+# the large-product kernel (128 x 128 tiles, 528 of them); ragged in both dimensions
+BIG = _cfg("bf16_big", 4100, 3002, 4096, dtype="bf16", w_std=0.02, outlier_channels=6, w_seed=21, x_seed=22)
 
 
 @pytest.mark.parametrize("cfg", HESS_CASES, ids=lambda c: c.name)
@@ -250,6 +253,33 @@ def test_quantize_matches_oracle_given_u(cfg, bits, group, act):
     assert mism <= 0.001 * gc.size
     np.testing.assert_allclose(r.scales.cpu().numpy(), scales.astype(np.float32), rtol=2e-7)
     np.testing.assert_allclose(r.row_loss.cpu().numpy(), loss, rtol=1e-9, atol=1e-12 * max(loss.max(), 1e-18))
+
+
+@pytest.mark.parametrize("bits,group,act", [(4, 0, False), (3, 128, True)])
+def test_quantize_large_products_sampled_rows(bits, group, act):
+    """Stage isolation at a size whose outer-block update takes the large-product GEMM: the oracle's U /
+    perm / dead in, the whole layer quantized on the GPU, the oracle loop on sampled rows (rows are
+    independent given U)."""
+    cfg = BIG
+    print(f"[quantize-big] bits={bits} group={group} act={act}", flush=True)
+    W, W64, S, colsq, n, H_p, perm, dead, U = _oracle_prep(cfg, act)
+    r = G.quantize_layer(to_device(W, cfg.dtype), dev64(U), dev64(perm.astype(np.int32)),
+                         dev64(dead.astype(np.uint8)), bits, group)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.random.default_rng(9).choice(cfg.out, 40, replace=False),
+                                     [0, 1, 127, 128, 4095, 4096, cfg.out - 1]]))
+    W0 = O.start_weights(W64[rows], perm, dead)
+    codes_q, scales, errs, loss = O.compensation_loop(W0, U, bits, group)
+    codes, g_idx, Q = O.finalize(codes_q, scales, perm, group)
+    gc = r.codes.cpu().numpy()[rows].astype(np.int64)
+    assert np.array_equal(r.g_idx.cpu().numpy(), g_idx)
+    mism = int(np.sum(gc != codes))
+    if mism:
+        dist, _ = O.forced_replay(W0, U, bits, group, gc[:, perm])
+        assert dist.max() <= 0.5 + 1e-9, (mism, dist.max())
+    assert mism <= 0.001 * gc.size
+    np.testing.assert_allclose(r.scales.cpu().numpy()[rows], scales.astype(np.float32), rtol=2e-7)
+    np.testing.assert_allclose(r.row_loss.cpu().numpy()[rows], loss, rtol=1e-9, atol=1e-12 * max(loss.max(), 1e-18))
 
 
 E2E_CASES = [
