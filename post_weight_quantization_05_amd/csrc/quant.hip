@@ -11,8 +11,8 @@
 //  k_rowprep   W (bf16/fp32) -> fp64 working copy in quantization order, dead columns zeroed, per-row
 //              start scale (block max reduction), or start scale and zero point (min and max).
 //  k_panel     per panel: 16 lanes per row (lane c holds columns c, c+16, ..., c+112 in registers), the
-//              128 x 128 block of U in LDS. Each step j broadcasts w_j from its owner lane with DPP
-//              (row_newbcast), every lane of the row rounds it (IEEE division, round-half-even), and
+//              upper part of the 128 x 128 block of U in LDS. Each step j broadcasts w_j from its owner
+//              lane with DPP (row_newbcast), every lane of the row rounds it (IEEE division, round-half-even), and
 //              updates its own columns with U[j][col] from LDS. Group maxima are 16-lane DPP max
 //              reductions. Codes and errors stay in registers and are stored once per panel.
 //  trailing    two levels of lazy updates on the fp64 MFMA GEMM core. Panels are grouped into outer
@@ -28,6 +28,7 @@
 // "Simplifications"): codes 0..L, L = 2^b - 1, scale = (max - min) / L (1 when max = min), zero =
 // clip(round(-min / scale), 0, L), code = clip(round(w / scale + zero), 0, L), value = scale (code - zero).
 // Every division is correctly rounded and every rounding is to nearest even, as in the definition.
+#include <atomic>
 #include <type_traits>
 #include <utility>
 
@@ -40,6 +41,12 @@ namespace gptq {
 namespace {
 
 constexpr int PW = 128;  // panel width
+// the panel's U block in LDS, row a stored from column 16 (a / 16) on: urow(a) is where row a starts
+__host__ __device__ constexpr int urow(int a) {
+  return 2048 * (a >> 4) - 128 * (a >> 4) * ((a >> 4) - 1) + (a & 15) * (128 - 16 * (a >> 4));
+}
+constexpr int UPACK = urow(PW);
+static_assert(PW == 128 && UPACK == 9216, "panel layout");
 #ifndef GPTQ_QUANT_OB
 #define GPTQ_QUANT_OB 1024
 #endif
@@ -192,27 +199,30 @@ __global__ __launch_bounds__(256) void k_panel(double* __restrict__ Wq, int out,
                                                double qmax, int group, int n_groups, int8_t* __restrict__ codes,
                                                float* __restrict__ scales, int32_t* __restrict__ zeros,
                                                double* __restrict__ Err, int ld_err, double* __restrict__ row_loss) {
-  __shared__ double Us[PW][PW];
+  // U panel block, upper part only: row a holds columns 16 (a / 16) .. 127 (the 16-column blocks that reach
+  // the diagonal, zeros left of it), 72 KB instead of 128, so two panel workgroups fit in a CU (see
+  // launch_panel)
+  __shared__ double Us[UPACK];
   __shared__ double rdiag[PW];
   __shared__ int pidx[PW];
   const int tid = threadIdx.x;
   const int pw = min(PW, in - b0);
-  // U panel block: loads are issued in batches of 16 per thread before they are stored to LDS
+  // loaded one 16-row block at a time (block k: 16 rows of 128 - 16k stored columns, 8 - k elements per
+  // thread), all of a block's loads in flight before its stores
+  static_for<0, 8>([&](auto kc) {
+    constexpr int k = decltype(kc)::value;
+    constexpr int RL = PW - 16 * k;  // stored length of the block's rows
+    constexpr int NE = RL / 16;      // elements per thread: 16 RL / 256
+    double v[NE];
 #pragma unroll
-  for (int q0 = 0; q0 < PW * PW / 256; q0 += 16) {
-    double v[16];
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int e = tid + 256 * (q0 + q);
-      const int a = e / PW, b = e % PW;
+    for (int q = 0; q < NE; ++q) {
+      const int i = tid + 256 * q;
+      const int a = 16 * k + i / RL, b = 16 * k + i % RL;
       v[q] = (a < pw && b < pw && b >= a) ? U[(int64_t)(b0 + a) * in + b0 + b] : 0.0;
     }
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int e = tid + 256 * (q0 + q);
-      Us[e / PW][e % PW] = v[q];
-    }
-  }
+    for (int q = 0; q < NE; ++q) Us[urow(16 * k) + tid + 256 * q] = v[q];
+  });
   for (int a = tid; a < PW; a += 256) {
     rdiag[a] = (a < pw) ? 1.0 / U[(int64_t)(b0 + a) * in + b0 + a] : 0.0;
     pidx[a] = (a < pw) ? min(max(perm[b0 + a], 0), in - 1) : 0;
@@ -286,7 +296,7 @@ __global__ __launch_bounds__(256) void k_panel(double* __restrict__ Wq, int out,
   double ucur[8], unext[8];
   double dcur = rdiag[0], dnext = 0.0;
 #pragma unroll
-  for (int m = 0; m < 8; ++m) ucur[m] = Us[0][c + 16 * m];
+  for (int m = 0; m < 8; ++m) ucur[m] = Us[c + 16 * m];
 #pragma unroll
   for (int jm = 0; jm < 8; ++jm) {
     // steps past the panel edge (j >= pw) need no guard: there w = 0, U = 0 and 1/U = 0, so they
@@ -297,7 +307,7 @@ __global__ __launch_bounds__(256) void k_panel(double* __restrict__ Wq, int out,
       if (j + 1 < PW) {
 #pragma unroll
         for (int m = 0; m < 8; ++m)
-          if (m >= (j + 1) / 16) unext[m] = Us[j + 1][c + 16 * m];
+          if (m >= (j + 1) / 16) unext[m] = Us[urow(j + 1) + c + 16 * (m - (j + 1) / 16)];
         dnext = rdiag[j + 1];
       }
       {
@@ -403,17 +413,37 @@ static hipError_t launch_rowprep(const void* W, int w_dtype, int out, int in, in
   return hipGetLastError();
 }
 
+// A panel workgroup takes 73.5 KB of LDS, so two fit in a CU. Below one workgroup per CU, a launch reserves
+// this much more (dynamic LDS, unused) so that the dispatcher gives each workgroup a CU of its own: packed
+// two to a CU, 256 workgroups (4096 rows) measured 4 % slower over the whole loop; with more workgroups than
+// CUs, two per CU save a round (11008 rows: 7.29 ms against 7.99 at one per CU).
+constexpr size_t PANEL_SPREAD_LDS = 8192;
+static int cu_count() {
+  static std::atomic<int> cached{0};
+  int n = cached.load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return 256;
+  cached.store(n, std::memory_order_relaxed);
+  return n;
+}
+
 template <bool ASYM>
 static hipError_t launch_panel(bool inpanel, dim3 grid, double* Wq, int out, int in, int b0, const double* U,
                                const int32_t* perm, double* scale_row, double* zero_row, double qmax, int group,
                                int n_groups, int8_t* codes, float* scales, int32_t* zeros, double* errp,
                                int ld_err, double* row_loss, hipStream_t stream) {
+  const size_t lds = ((int)grid.x <= cu_count()) ? PANEL_SPREAD_LDS : 0;
   if (inpanel)
-    k_panel<true, ASYM><<<grid, dim3(256), 0, stream>>>(Wq, out, in, b0, U, perm, scale_row, zero_row, qmax, group,
-                                                        n_groups, codes, scales, zeros, errp, ld_err, row_loss);
+    k_panel<true, ASYM><<<grid, dim3(256), lds, stream>>>(Wq, out, in, b0, U, perm, scale_row, zero_row, qmax,
+                                                          group, n_groups, codes, scales, zeros, errp, ld_err,
+                                                          row_loss);
   else
-    k_panel<false, ASYM><<<grid, dim3(256), 0, stream>>>(Wq, out, in, b0, U, perm, scale_row, zero_row, qmax, group,
-                                                         n_groups, codes, scales, zeros, errp, ld_err, row_loss);
+    k_panel<false, ASYM><<<grid, dim3(256), lds, stream>>>(Wq, out, in, b0, U, perm, scale_row, zero_row, qmax,
+                                                           group, n_groups, codes, scales, zeros, errp, ld_err,
+                                                           row_loss);
   return hipGetLastError();
 }
 
