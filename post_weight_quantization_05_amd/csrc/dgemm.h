@@ -59,7 +59,8 @@ struct InvFill {
 int inv_fill_tiles(const InvFill& f);
 // One block-column step of the blocked Cholesky factorization (see k_colstep in dgemm.hip): C -= A B^T
 // on the lower tiles of the M x N region C, the diagonal block at its origin factored and inverted, and
-// the column-0 tiles below it solved against that factor. The same launch also computes lower tiles
+// the column-0 tiles below it solved against that factor; K is 0, 64 or 256. The same launch also
+// computes lower tiles
 // x_first .. x_first + x_count - 1 (in tile order) of x, an independent A B^T update of a square region
 // (x may be null when x_count is 0), and, when f is not null, the tiles of launch f->k of the inverse.
 hipError_t colstep_launch(const DgemmArgs& a, const DgemmArgs* x, int x_first, int x_count, const InvFill* f,

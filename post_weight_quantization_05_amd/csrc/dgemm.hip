@@ -251,8 +251,9 @@ __global__ __launch_bounds__(256) void k_dgemm(DgemmArgs a) {
 // twice). k64_stage loads and stores them (rows i0.. of A to As, rows j0.. of B to Bs) and ends with a
 // barrier; the products read them.
 constexpr int K64S = 68;
-__device__ __forceinline__ void k64_stage(const double* A, const double* B, int64_t lda, int64_t ldb, int M, int N,
-                                          int i0, int j0, double* As, double* Bs) {
+// thread element e = tid + 256 v of a 64 x 64 operand block: row e / 32, column pair 2 (e % 32)
+__device__ __forceinline__ void k64_load(const double* A, const double* B, int64_t lda, int64_t ldb, int M, int N,
+                                         int i0, int j0, double2 (&ra)[8], double2 (&rb)[8]) {
   const int tid = threadIdx.x;
   const bool a_vec = ((lda & 1) == 0) && ((reinterpret_cast<uintptr_t>(A) & 15) == 0);
   const bool b_vec = ((ldb & 1) == 0) && ((reinterpret_cast<uintptr_t>(B) & 15) == 0);
@@ -269,13 +270,16 @@ __device__ __forceinline__ void k64_stage(const double* A, const double* B, int6
     }
     return v;
   };
-  double2 ra[8], rb[8];
 #pragma unroll
   for (int v = 0; v < 8; ++v) {
     const int e = tid + 256 * v, r = e >> 5, c2 = (e & 31) * 2;
     ra[v] = ld2(A, lda, i0 + r, M, c2, a_vec);
     rb[v] = ld2(B, ldb, j0 + r, N, c2, b_vec);
   }
+}
+// stores a loaded pair of operand blocks (A to As, B to Bs) and ends with a barrier
+__device__ __forceinline__ void k64_store(const double2 (&ra)[8], const double2 (&rb)[8], double* As, double* Bs) {
+  const int tid = threadIdx.x;
 #pragma unroll
   for (int v = 0; v < 8; ++v) {
     const int e = tid + 256 * v, r = e >> 5, c2 = (e & 31) * 2;
@@ -284,39 +288,52 @@ __device__ __forceinline__ void k64_stage(const double* A, const double* B, int6
   }
   __syncthreads();
 }
+__device__ __forceinline__ void k64_stage(const double* A, const double* B, int64_t lda, int64_t ldb, int M, int N,
+                                          int i0, int j0, double* As, double* Bs) {
+  double2 ra[8], rb[8];
+  k64_load(A, B, lda, ldb, M, N, i0, j0, ra, rb);
+  k64_store(ra, rb, As, Bs);
+}
 
-// acc = the T x T tile of A B^T from the staged operands; 4 waves in 2 x 2, each 32 x 32. Ends with a
-// barrier.
+// acc = the T x T tile of A B^T over K = 64 nk (nk >= 1), staged 64 of K at a time; 4 waves in 2 x 2, each
+// 32 x 32. Ends with a barrier.
 __device__ __forceinline__ void tile_product_k64(const double* A, const double* B, int64_t lda, int64_t ldb, int M,
                                                  int N, int i0, int j0, double* As, double* Bs,
-                                                 f64x4 (&acc)[2][2]) {
+                                                 f64x4 (&acc)[2][2], const int nk = 1) {
   constexpr int T = 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int lk = lane >> 4, lc = lane & 15;
-  k64_stage(A, B, lda, ldb, M, N, i0, j0, As, Bs);
 #pragma unroll
   for (int p = 0; p < 2; ++p)
 #pragma unroll
     for (int q = 0; q < 2; ++q) acc[p][q] = f64x4{0.0, 0.0, 0.0, 0.0};
+  // the next 64 of K is loaded into registers while the matrix cores work on the staged chunk
+  double2 ra[8], rb[8];
+  k64_load(A, B, lda, ldb, M, N, i0, j0, ra, rb);
+  for (int kc = 0; kc < nk; ++kc) {
+    k64_store(ra, rb, As, Bs);
+    if (kc + 1 < nk) k64_load(A + T * (kc + 1), B + T * (kc + 1), lda, ldb, M, N, i0, j0, ra, rb);
 #pragma unroll
-  for (int k4 = 0; k4 < T; k4 += 4) {
-    const int kr = k4 + lk;
-    double fa[2], fb[2];
+    for (int k4 = 0; k4 < T; k4 += 4) {
+      const int kr = k4 + lk;
+      double fa[2], fb[2];
 #pragma unroll
-    for (int r = 0; r < 2; ++r) fa[r] = As[(wm * (T / 2) + r * 16 + lc) * K64S + kr];
+      for (int r = 0; r < 2; ++r) fa[r] = As[(wm * (T / 2) + r * 16 + lc) * K64S + kr];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) fb[q] = Bs[(wn * (T / 2) + q * 16 + lc) * K64S + kr];
+      for (int q = 0; q < 2; ++q) fb[q] = Bs[(wn * (T / 2) + q * 16 + lc) * K64S + kr];
 #pragma unroll
-    for (int r = 0; r < 2; ++r)
+      for (int r = 0; r < 2; ++r)
 #pragma unroll
-      for (int q = 0; q < 2; ++q) acc[r][q] = __builtin_amdgcn_mfma_f64_16x16x4f64(fa[r], fb[q], acc[r][q], 0, 0, 0);
+        for (int q = 0; q < 2; ++q)
+          acc[r][q] = __builtin_amdgcn_mfma_f64_16x16x4f64(fa[r], fb[q], acc[r][q], 0, 0, 0);
+    }
+    __syncthreads();
   }
-  __syncthreads();
 }
 
-// The two products of a panel workgroup of the block-column step, from one staging of the previous
-// panel's rows (this tile's rows i0.. as A, the diagonal block's rows 0.. as B):
+// The two products of a panel workgroup of the block-column step, over K = 64 nk (nk >= 1), from stagings of
+// the previous panel's rows 64 of K at a time (this tile's rows i0.. as A, the diagonal block's rows 0.. as B):
 //   dacc: the diagonal block's update B B^T, 2 x 2 waves of 32 x 32 as in tile_product_k64;
 //   xt:   this tile's update A B^T, transposed: wave w forms the 64 x 16 strip (B A^T)[:, 16w .. 16w + 15],
 //         so entry r of xt[jb] in lane l is (A B^T)[16w + l % 16][16 jb + 4 r + l / 16], exactly the A-operand
@@ -324,34 +341,38 @@ __device__ __forceinline__ void tile_product_k64(const double* A, const double* 
 // Ends with a barrier.
 __device__ __forceinline__ void panel_products_k64(const double* A, const double* B, int64_t lda, int64_t ldb,
                                                    int M, int N, int i0, double* As, double* Bs,
-                                                   f64x4 (&dacc)[2][2], f64x4 (&xt)[4]) {
+                                                   f64x4 (&dacc)[2][2], f64x4 (&xt)[4], int nk = 1) {
   constexpr int T = 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int lk = lane >> 4, lc = lane & 15;
-  k64_stage(A, B, lda, ldb, M, N, i0, 0, As, Bs);
 #pragma unroll
   for (int p = 0; p < 2; ++p)
 #pragma unroll
     for (int q = 0; q < 2; ++q) dacc[p][q] = f64x4{0.0, 0.0, 0.0, 0.0};
 #pragma unroll
   for (int jb = 0; jb < 4; ++jb) xt[jb] = f64x4{0.0, 0.0, 0.0, 0.0};
+  // (no register prefetch of the next chunk here: the panel workgroup already holds its tile X and the
+  // diagonal block's old values, and the extra 64 registers would spill)
+  for (int kc = 0; kc < nk; ++kc) {
+    k64_stage(A + T * kc, B + T * kc, lda, ldb, M, N, i0, 0, As, Bs);
 #pragma unroll
-  for (int k4 = 0; k4 < T; k4 += 4) {
-    const int kr = k4 + lk;
-    double fb[4], fo;
+    for (int k4 = 0; k4 < T; k4 += 4) {
+      const int kr = k4 + lk;
+      double fb[4], fo;
 #pragma unroll
-    for (int jb = 0; jb < 4; ++jb) fb[jb] = Bs[(jb * 16 + lc) * K64S + kr];
-    fo = As[(wave * 16 + lc) * K64S + kr];
+      for (int jb = 0; jb < 4; ++jb) fb[jb] = Bs[(jb * 16 + lc) * K64S + kr];
+      fo = As[(wave * 16 + lc) * K64S + kr];
 #pragma unroll
-    for (int r = 0; r < 2; ++r)
+      for (int r = 0; r < 2; ++r)
 #pragma unroll
-      for (int q = 0; q < 2; ++q)
-        dacc[r][q] = __builtin_amdgcn_mfma_f64_16x16x4f64(fb[2 * wm + r], fb[2 * wn + q], dacc[r][q], 0, 0, 0);
+        for (int q = 0; q < 2; ++q)
+          dacc[r][q] = __builtin_amdgcn_mfma_f64_16x16x4f64(fb[2 * wm + r], fb[2 * wn + q], dacc[r][q], 0, 0, 0);
 #pragma unroll
-    for (int jb = 0; jb < 4; ++jb) xt[jb] = __builtin_amdgcn_mfma_f64_16x16x4f64(fb[jb], fo, xt[jb], 0, 0, 0);
+      for (int jb = 0; jb < 4; ++jb) xt[jb] = __builtin_amdgcn_mfma_f64_16x16x4f64(fb[jb], fo, xt[jb], 0, 0, 0);
+    }
+    __syncthreads();
   }
-  __syncthreads();
 }
 
 // C = alpha A B + beta C for one 64 x 64 tile with K = 64, A (64 x 64) and B (64 x 64) row-major: rows of A
@@ -496,9 +517,12 @@ __global__ __launch_bounds__(256, 2) void k_inv_fill(InvFill f) {
 //    workgroups gets the same factor as tile (0, 0) without waiting for it); X is then solved,
 //    X (L^-1)^T on the matrix cores from X held in registers, and written in place: the panel of the
 //    next step.
-// K is 64, or 0 for the first step of an outer block (no update: the launch only factors the block and
+// K is 64 (the previous step's panel), 256 (the first step of an outer block: the previous outer block's
+// whole panel, staged 64 of K at a time), or 0 (the very first step: the launch only factors the block and
 // solves the panel). Further workgroups past the step's own tiles take tiles of a deferred update xa.
-template <int T>
+// NK: K / 64 when K > 0 (1 or 4), a compile-time count so that the K = 64 launches keep the register budget
+// of a single staged product.
+template <int T, int NK>
 __global__ __launch_bounds__(256, 2) void k_colstep(DgemmArgs a, DgemmArgs xa, int x_first, int n_own,
                                                    int x_count, InvFill fl) {
   static_assert(T == diagblock::NB, "the diagonal block is one tile");
@@ -552,7 +576,7 @@ __global__ __launch_bounds__(256, 2) void k_colstep(DgemmArgs a, DgemmArgs xa, i
   const int ntn = (a.N + T - 1) / T;
   const int I = blockIdx.x / ntn, J = blockIdx.x - I * ntn;
   if (I < J) return;
-  const int M = a.M, N = a.N, K = a.K;  // K is 0 or 64
+  const int M = a.M, N = a.N, K = a.K;  // K is 0, 64 or 256
   const int i0 = I * T, j0 = J * T;
   if (i0 >= M || j0 >= N) return;
   const double* A = a.A;
@@ -572,7 +596,7 @@ __global__ __launch_bounds__(256, 2) void k_colstep(DgemmArgs a, DgemmArgs xa, i
     // the update C -= A B^T of a tile to the right of the panel
     if (K == 0) return;
     f64x4 acc[FR][FC];
-    tile_product_k64(A, B, a.lda, a.ldb, M, N, i0, j0, ABs, ABs + T * K64S, acc);
+    tile_product_k64(A, B, a.lda, a.ldb, M, N, i0, j0, ABs, ABs + T * K64S, acc, NK);
     const bool diag_tile = (I == J);
 #pragma unroll
     for (int r = 0; r < FR; ++r)
@@ -617,8 +641,8 @@ __global__ __launch_bounds__(256, 2) void k_colstep(DgemmArgs a, DgemmArgs xa, i
   };
   if (I == 0) {
     f64x4 acc[FR][FC];
-    if (K == T) {
-      tile_product_k64(A, B, a.lda, a.ldb, M, N, 0, 0, ABs, ABs + T * K64S, acc);
+    if (K > 0) {
+      tile_product_k64(A, B, a.lda, a.ldb, M, N, 0, 0, ABs, ABs + T * K64S, acc, NK);
     } else {
 #pragma unroll
       for (int r = 0; r < FR; ++r)
@@ -650,9 +674,9 @@ __global__ __launch_bounds__(256, 2) void k_colstep(DgemmArgs a, DgemmArgs xa, i
       x[jb][r] = (xrow < M && j < m) ? C[(int64_t)xrow * a.ldc + j] : 0.0;
     }
   f64x4 dacc[FR][FC];
-  if (K == T) {
+  if (K > 0) {
     f64x4 xt[4];
-    panel_products_k64(A, B, a.lda, a.ldb, M, N, i0, ABs, ABs + T * K64S, dacc, xt);
+    panel_products_k64(A, B, a.lda, a.ldb, M, N, i0, ABs, ABs + T * K64S, dacc, xt, NK);
 #pragma unroll
     for (int jb = 0; jb < 4; ++jb)
 #pragma unroll
@@ -1093,8 +1117,8 @@ hipError_t dgemm_launch(const DgemmArgs& a, bool ta, bool tb, int batches, hipSt
 
 hipError_t colstep_launch(const DgemmArgs& a, const DgemmArgs* x, int x_first, int x_count, const InvFill* f,
                           hipStream_t stream) {
-  if (a.M <= 0 || a.N <= 0 || a.N > a.M || (a.K != 0 && a.K != 64) || !a.diag_Lstage || !a.diag_Dinv ||
-      !a.diag_status)
+  if (a.M <= 0 || a.N <= 0 || a.N > a.M || (a.K != 0 && a.K != 64 && a.K != 256) || !a.diag_Lstage ||
+      !a.diag_Dinv || !a.diag_status)
     return hipErrorInvalidValue;
   const int tiles = ((a.M + 63) / 64) * ((a.N + 63) / 64);
   DgemmArgs none{};
@@ -1102,8 +1126,11 @@ hipError_t colstep_launch(const DgemmArgs& a, const DgemmArgs* x, int x_first, i
   if (x_count > 0 && (x->M != x->N || x->kmode != KMODE_FULL)) return hipErrorInvalidValue;
   const InvFill nof{};
   const int f_count = f ? inv_fill_tiles(*f) : 0;
-  k_colstep<64><<<dim3(tiles + x_count + f_count), dim3(256), 0, stream>>>(a, x_count > 0 ? *x : none, x_first, tiles,
-                                                                           x_count, f ? *f : nof);
+  const dim3 grid(tiles + x_count + f_count);
+  if (a.K == 256)
+    k_colstep<64, 4><<<grid, dim3(256), 0, stream>>>(a, x_count > 0 ? *x : none, x_first, tiles, x_count, f ? *f : nof);
+  else
+    k_colstep<64, 1><<<grid, dim3(256), 0, stream>>>(a, x_count > 0 ? *x : none, x_first, tiles, x_count, f ? *f : nof);
   return hipGetLastError();
 }
 

@@ -219,13 +219,16 @@ __global__ __launch_bounds__(256) void k_reverse_to_upper(const double* __restri
 // Blocked right-looking Cholesky in two levels. Inside an outer block column of NBO columns, each
 // 64-column step is one launch (k_colstep): the outer block's remaining columns get the previous
 // panel's update (K = 64), the next diagonal block is factored and inverted, and the next panel is
-// solved against it. After the outer block, products with K = NBO update the trailing matrix: the next
-// outer block's columns at once, the rest inside the next outer block's steps. The factors of the diagonal blocks are staged in Lst and copied into A at the end (A's
-// diagonal block is read by several workgroups of the launch that factors it).
+// solved against it. The outer block's whole panel (K = NBO) updates the trailing matrix: the next outer
+// block's columns in that block's first step launch (its own tiles, before its diagonal block is
+// factored), the rest as deferred tiles inside the next outer block's steps. The factors of the diagonal
+// blocks are staged in Lst and copied into A at the end (A's diagonal block is read by several workgroups
+// of the launch that factors it).
 #ifndef GPTQ_FACTOR_NBO
 #define GPTQ_FACTOR_NBO 256
 #endif
 constexpr int NBO = GPTQ_FACTOR_NBO;  // outer block width (a multiple of 64)
+static_assert(NBO == 256, "an outer block's panel is the K of its successor's first step launch (64 or 256)");
 // Deferred trailing tiles per block-column step: with L^-1 in the steps (two workgroups per CU carrying
 // it) 640 (prepare at in = 4096: 2.92 ms against 3.00 with 160); without, 160 (in = 8192 / 11008: 13.7 /
 // 29.0 ms against 14.0 / 29.9 with 640).
@@ -284,8 +287,10 @@ hipError_t potrf_lower(double* A, int d, double* Dinv, double* Lst, unsigned* st
       const int left = pend_tiles - pend_done, rem = steps - step++;
       return (left + rem - 1) / rem;
     };
-    // first block of the outer block column: its diagonal block and panel, no update
-    e = colstep(b0, min(NB, d - b0), b0, 0, share());
+    // first block of the outer block column: the update of the whole outer block by the previous outer
+    // panel (K = NBO; none for the first outer block), its diagonal block and its panel
+    if (b0 == 0) e = colstep(b0, min(NB, d - b0), b0, 0, share());
+    else e = colstep(b0, b1 - b0, b0 - NBO, NBO, share());
     if (e != hipSuccess) return e;
     for (int o = b0; o + NB < b1; o += NB) {
       // the outer block's remaining columns get panel o; the next block is factored and its panel solved
@@ -295,19 +300,9 @@ hipError_t potrf_lower(double* A, int d, double* Dinv, double* Lst, unsigned* st
     }
     pend_tiles = pend_done = 0;
     if (b1 < d) {
-      // trailing update with the whole outer panel Q = A[b1:, b0:b1]: A22 -= Q Q^T (lower part)
+      // trailing update with the whole outer panel Q = A[b1:, b0:b1]: A22 -= Q Q^T (lower part). The next
+      // outer block's columns get it in that block's first step launch; the rest is deferred.
       const int b2 = min(d, b1 + NBO);
-      const double* Q = A + (int64_t)b1 * d + b0;
-      DgemmArgs s{};  // the next outer block's columns, now
-      s.A = Q; s.lda = d;
-      s.B = Q; s.ldb = d;
-      s.C = A + (int64_t)b1 * d + b1; s.ldc = d;
-      s.M = d - b1; s.N = b2 - b1; s.K = b1 - b0;
-      s.alpha = -1.0; s.beta = 1.0;
-      s.lower_only = 1;
-      s.kmode = KMODE_FULL;
-      e = dgemm_launch(s, false, true, 1, stream);
-      if (e != hipSuccess) return e;
       if (b2 < d) {  // the rest, deferred
         pend = DgemmArgs{};
         const double* Q2 = A + (int64_t)b2 * d + b0;
