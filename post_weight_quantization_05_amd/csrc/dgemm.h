@@ -35,10 +35,11 @@ struct DgemmArgs {
   unsigned* diag_status;
 };
 
-// C = alpha op(A) op(B) + beta C on 64 x 64 tiles. Single plain products with small K and at most 1024
-// tiles take kernels that keep a whole tile's operands in flight: op(B) = B with K <= 128 (no lower_only),
-// and op(B) = B^T with K <= 256 and no tile list. Everything else (batches, triangular K ranges, tile lists, op(A) = A^T, larger
-// K) takes the chunked-ring GEMM.
+// C = alpha op(A) op(B) + beta C on 64 x 64 tiles. Single plain products op(B) = B take kernels of their own:
+// K <= 128 with at most 1024 tiles (no lower_only) a kernel that keeps a whole tile's operands in flight,
+// K >= 256 (a multiple of 16, even N) with at least 512 tiles of 128 x 128 the 128 x 128 kernel. Everything
+// else (batches, triangular K ranges, tile lists, op(A) = A^T, op(B) = B^T, other sizes) takes the
+// chunked-ring GEMM.
 hipError_t dgemm_launch(const DgemmArgs& a, bool ta, bool tb, int batches, hipStream_t stream);
 // The inverse Z = L^-1 of the factor, formed by the block-column steps as work that fills the CUs their
 // chain leaves idle (see inv_fill_tile in dgemm.hip). Row block t of L Z = I is eliminated right-looking:

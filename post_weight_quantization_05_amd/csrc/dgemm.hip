@@ -941,129 +941,6 @@ __global__ __launch_bounds__(256) void k_dgemm_nn_smallk(DgemmArgs a) {
       }
 }
 
-// Products C = alpha A B^T + beta C with K at most 256, A row-major M x K, B row-major N x K: the
-// factorization's update of the next outer block's columns (K = 256, lower tiles only). K is taken 64 at a
-// time from a ring of two register sets, so 128 of K is in flight while the matrix cores run, and the old
-// C values are loaded up front; per 64 of K one LDS store, one barrier and the MFMA sequence. Both operands
-// are staged as [row][k] with rows of 68 doubles (a 16 x 4 fragment read touches each bank pair twice).
-constexpr int SKT_MAX = 256;
-template <bool TB>
-__global__ __launch_bounds__(256) void k_dgemm_smallk(DgemmArgs a) {
-  static_assert(TB, "B^T operand");
-  constexpr int SK_BS = SK_AS;
-  constexpr int T = 64;
-  __shared__ __attribute__((aligned(16))) double As[T * SK_AS];
-  __shared__ __attribute__((aligned(16))) double Bs[T * SK_BS];
-  const int M = a.M, N = a.N, K = a.K;
-  const int ntn = (N + T - 1) / T;
-  const int I = blockIdx.x / ntn, J = blockIdx.x - I * ntn;
-  if (a.lower_only && I < J) return;
-  const int i0 = I * T, j0 = J * T;
-  if (i0 >= M || j0 >= N) return;
-  const double* A = a.A;
-  const double* B = a.B;
-  double* C = a.C;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int lk = lane >> 4, lc = lane & 15;
-  const bool a_vec = ((a.lda & 1) == 0) && ((reinterpret_cast<uintptr_t>(A) & 15) == 0);
-  const bool b_vec = ((a.ldb & 1) == 0) && ((reinterpret_cast<uintptr_t>(B) & 15) == 0);
-  // element pair (r, c..c+1) of a row-major P, zero outside [0, rlim) x [0, clim)
-  auto ld2 = [](const double* P, int64_t ld, int r, int rlim, int c, int clim, bool vec) {
-    double2 v = make_double2(0.0, 0.0);
-    if (r < rlim) {
-      const double* q = P + (int64_t)r * ld + c;
-      if (vec && c + 1 < clim) {
-        v = *reinterpret_cast<const double2*>(q);
-      } else {
-        if (c < clim) v.x = q[0];
-        if (c + 1 < clim) v.y = q[1];
-      }
-    }
-    return v;
-  };
-  // thread element e = tid + 256 v of a 64 x 64 block: row e / 32, column pair 2 (e % 32)
-  double2 ra[2][8], rb[2][8];
-  auto load = [&](auto slot_c, int h) {
-    constexpr int slot = decltype(slot_c)::value;
-    const int kh = K - h * T;  // columns of K left from this 64
-#pragma unroll
-    for (int v = 0; v < 8; ++v) {
-      const int e = tid + 256 * v, r = e >> 5, c2 = (e & 31) * 2;
-      ra[slot][v] = ld2(A + h * T, a.lda, i0 + r, M, c2, kh, a_vec);                          // A[i0 + r][hT + c2]
-      rb[slot][v] = TB ? ld2(B + h * T, a.ldb, j0 + r, N, c2, kh, b_vec)                      // B[j0 + r][hT + c2]
-                       : ld2(B + (int64_t)h * T * a.ldb, a.ldb, r, kh, j0 + c2, N, b_vec);     // B[hT + r][j0 + c2]
-    }
-  };
-  const int nh = (K + T - 1) / T;
-  if (nh > 0) load(std::integral_constant<int, 0>{}, 0);
-  if (nh > 1) load(std::integral_constant<int, 1>{}, 1);
-  // the old values of the thread's C entries (entry (r, q, e) is row 4e + lk of 16 x 16 block (r, q))
-  double cold[2][2][4];
-#pragma unroll
-  for (int r = 0; r < 2; ++r)
-#pragma unroll
-    for (int q = 0; q < 2; ++q)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int gi = i0 + wm * (T / 2) + r * 16 + 4 * e + lk;
-        const int gj = j0 + wn * (T / 2) + q * 16 + lc;
-        cold[r][q][e] = (a.beta != 0.0 && gi < M && gj < N) ? C[(int64_t)gi * a.ldc + gj] : 0.0;
-      }
-  f64x4 acc[2][2];
-#pragma unroll
-  for (int r = 0; r < 2; ++r)
-#pragma unroll
-    for (int q = 0; q < 2; ++q) acc[r][q] = f64x4{0.0, 0.0, 0.0, 0.0};
-  // one 64 of K from ring slot `slot`; the slot is refilled with the 64 two steps on (K is the same for
-  // the whole workgroup, so every thread takes the same barriers)
-  auto step = [&](auto slot_c, int h) {
-    constexpr int slot = decltype(slot_c)::value;
-    if (h > 0) __syncthreads();  // the previous 64 is read
-#pragma unroll
-    for (int v = 0; v < 8; ++v) {
-      const int e = tid + 256 * v, r = e >> 5, c2 = (e & 31) * 2;
-      *reinterpret_cast<double2*>(&As[r * SK_AS + c2]) = ra[slot][v];
-      *reinterpret_cast<double2*>(&Bs[r * (TB ? SK_AS : SK_BS) + c2]) = rb[slot][v];
-    }
-    __syncthreads();
-    if (h + 2 < nh) load(slot_c, h + 2);
-#pragma unroll
-    for (int k4 = 0; k4 < T; k4 += 4) {
-      const int kr = k4 + lk;
-      double fa[2], fb[2];
-#pragma unroll
-      for (int r = 0; r < 2; ++r) fa[r] = As[(wm * (T / 2) + r * 16 + lc) * SK_AS + kr];
-#pragma unroll
-      for (int q = 0; q < 2; ++q)
-        fb[q] = TB ? Bs[(wn * (T / 2) + q * 16 + lc) * SK_AS + kr] : Bs[kr * SK_BS + wn * (T / 2) + q * 16 + lc];
-#pragma unroll
-      for (int r = 0; r < 2; ++r)
-#pragma unroll
-        for (int q = 0; q < 2; ++q) acc[r][q] = __builtin_amdgcn_mfma_f64_16x16x4f64(fa[r], fb[q], acc[r][q], 0, 0, 0);
-    }
-  };
-  for (int h = 0; h < nh; h += 2) {
-    step(std::integral_constant<int, 0>{}, h);
-    if (h + 1 < nh) step(std::integral_constant<int, 1>{}, h + 1);
-  }
-  const bool diag_tile = a.lower_only && I == J;
-#pragma unroll
-  for (int r = 0; r < 2; ++r)
-#pragma unroll
-    for (int q = 0; q < 2; ++q)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int gi = i0 + wm * (T / 2) + r * 16 + 4 * e + lk;
-        const int gj = j0 + wn * (T / 2) + q * 16 + lc;
-        // a diagonal tile of a lower-only update writes its lower triangle only
-        if (gi < M && gj < N && (!diag_tile || gj - j0 <= gi - i0)) {
-          const double v = a.alpha * acc[r][q][e];
-          C[(int64_t)gi * a.ldc + gj] = (a.beta == 0.0) ? v : fma(a.beta, cold[r][q][e], v);
-        }
-      }
-}
-
 template <int T>
 static hipError_t dgemm_launch_t(const DgemmArgs& a, bool ta, bool tb, int batches, hipStream_t stream) {
   int tiles;
@@ -1077,15 +954,11 @@ static hipError_t dgemm_launch_t(const DgemmArgs& a, bool ta, bool tb, int batch
   dim3 grid(tiles, batches);
   const bool plain = T == 64 && !ta && !a.tri_tiles && a.kmode == KMODE_FULL && batches == 1 && a.m_step == 0 &&
                      !a.k_by_m;
-#ifndef GPTQ_DGEMM_SMALLK_TB
-#define GPTQ_DGEMM_SMALLK_TB 1
-#endif
-  // the small-K kernels run two workgroups per CU (one for B^T); past about two rounds of tiles the chunked
-  // ring's four per CU wins (measured: 11008-row quantize updates 1.2 % slower on the small-K kernel,
-  // 4096-row ones 2-3 % faster)
+  // the small-K kernel runs two workgroups per CU; past about two rounds of tiles the chunked ring's four
+  // per CU wins (measured: 11008-row quantize updates 1.2 % slower on the small-K kernel, 4096-row ones
+  // 2-3 % faster)
   const bool few = tiles <= SK_TILES;
   const bool smallk = GPTQ_DGEMM_SMALLK && plain && few && !tb && a.K <= SK_MAX && !a.lower_only;
-  const bool smallk_t = GPTQ_DGEMM_SMALLK_TB && plain && few && tb && a.K <= SKT_MAX;
 #ifndef GPTQ_DGEMM_BIG
 #define GPTQ_DGEMM_BIG 1
 #endif
@@ -1100,7 +973,6 @@ static hipError_t dgemm_launch_t(const DgemmArgs& a, bool ta, bool tb, int batch
     k_dgemm_nn_big<<<dim3(big_tiles), dim3(256), 0, stream>>>(a.A, (int)a.lda, a.B, (int)a.ldb, a.C, (int)a.ldc,
                                                             a.M, a.N, a.K, a.alpha, a.beta);
   else if (smallk) k_dgemm_nn_smallk<<<grid, dim3(256), 0, stream>>>(a);
-  else if (smallk_t) k_dgemm_smallk<true><<<grid, dim3(256), 0, stream>>>(a);
   else if (!ta && !tb) k_dgemm<false, false, T><<<grid, dim3(256), 0, stream>>>(a);
   else if (!ta && tb) k_dgemm<false, true, T><<<grid, dim3(256), 0, stream>>>(a);
   else if (ta && !tb) k_dgemm<true, false, T><<<grid, dim3(256), 0, stream>>>(a);
