@@ -211,6 +211,24 @@ def upper_factor_of_inverse(H_p: np.ndarray) -> np.ndarray:
     return np.ascontiguousarray(L.T)
 
 
+def r_form(H_p: np.ndarray, panel: int = 128) -> np.ndarray:
+    """The factor in the form the second quantize route of the library reads (a layout, not a step of the
+    pages): R = U^-1, upper-triangular with R R^T = H (so J R J is the lower Cholesky factor of J H J, J the
+    index reversal), in the upper triangle, diagonal included; and for each run of `panel` columns
+    [b, b + p) the strictly lower part of that diagonal block holding J U_bb J, U_bb = R_bb^-1 being U's
+    diagonal block. Written from the definitions with numpy's Cholesky factor and inverse.
+    """
+    d = H_p.shape[0]
+    rev = np.arange(d)[::-1]
+    R = np.linalg.cholesky(H_p[np.ix_(rev, rev)])[np.ix_(rev, rev)]
+    M = np.triu(R)
+    for b in range(0, d, panel):
+        p = min(panel, d - b)
+        U_bb = np.linalg.inv(R[b:b + p, b:b + p])
+        M[b:b + p, b:b + p] += np.tril(U_bb[::-1, ::-1], -1)
+    return M
+
+
 # ---------------------------------------------------------------------------------------------
 # Grids: fitting a grid to a run of weights, snapping a weight to it, and the snapped value
 # ---------------------------------------------------------------------------------------------
