@@ -3,7 +3,10 @@
 
 A step is one pass of the whole path on the q_proj workload (W 4096 x 4096 bf16, X 262144 x 4096 bf16 =
 128 segments x 2048 tokens, 4-bit per-row scales, damp 0.01): accumulate X^T X over all rows (the first
-accumulate call writes S, so no zeroing pass is needed), prepare U, run the compensation loop. Inputs are resident in HBM before timing starts.
+accumulate call writes S, so no zeroing pass is needed), prepare the factor, run the compensation loop. By
+default the factor is in its R form (R = U^-1, the Cholesky factor of the reversed H, with U's 128 x 128
+diagonal blocks) and the loop runs from it (gptq_quantize_layer_r); --factor reversed times the route through
+U itself. Inputs are resident in HBM before timing starts.
 Prints ONE JSON line (see the fields below). `--gpus N` with N > 1 exits: this path runs on one GPU.
 """
 from __future__ import annotations
@@ -31,7 +34,11 @@ def parse():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", default="q_proj", help="workload name (q_proj, up_gate, down, tiny, teacher)")
-    ap.add_argument("--factor", choices=["rechol", "reversed"], default="reversed")
+    ap.add_argument("--factor", choices=["rechol", "reversed", "rform"], default="rform",
+                    help="rform (default): prepare writes R = U^-1 with U's 128 x 128 diagonal blocks and the loop "
+                         "runs from it (inputs a multiple of 64, group 0 or dividing 128; other workloads take "
+                         "reversed); reversed: U by one Cholesky and one triangular inverse; rechol: U as the "
+                         "Cholesky factor of the explicit inverse")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-rows", type=int, default=65536)
     ap.add_argument("--cpu-loop-rows", type=int, default=64)
@@ -163,7 +170,12 @@ def main():
         print(json.dumps({"mode": "copy", "bytes_per_copy": n, "copies": max(1, args.steps)}), flush=True)
         return
     cfg = syn.config_by_name(args.config)
-    flags = G.GPTQ_FACTOR_REVERSED if args.factor == "reversed" else G.GPTQ_FACTOR_INVERSE_RECHOL
+    if args.factor == "rform" and (cfg.d_in % 64 or (cfg.group and 128 % cfg.group)):
+        print(f"bench: the R form does not take in = {cfg.d_in}, group = {cfg.group}; running the reversed route",
+              file=sys.stderr, flush=True)
+        args.factor = "reversed"
+    flags = {"reversed": G.GPTQ_FACTOR_REVERSED, "rechol": G.GPTQ_FACTOR_INVERSE_RECHOL,
+             "rform": G.GPTQ_FACTOR_R_FORM}[args.factor]
     t0 = time.perf_counter()
     W = syn.gen_w(cfg)
     X = syn.gen_x(cfg)
@@ -200,7 +212,8 @@ def main():
         G.prepare_chol(st.S, st.colsq, st.n_total, cfg.damp, cfg.act_order, flags, out=(U, perm, dead))
         if record:
             marks[3].record(stream)
-        res = G.quantize_layer(Wd, U, perm, dead, cfg.bits, cfg.group, ws=qws)
+        res = G.quantize_layer(Wd, U, perm, dead, cfg.bits, cfg.group, ws=qws,
+                               r_form=(flags == G.GPTQ_FACTOR_R_FORM))
         if record:
             marks[4].record(stream)
             for i, k in enumerate(("zero", "hessian", "prepare", "quantize")):
@@ -252,7 +265,10 @@ def main():
     # algorithmic work (lower triangle of X^T X, the two-step factor, the loop's multiply-adds)
     n = cfg.n
     hess_flops = n * d * (d + 1)
-    factor_flops = (2.0 / 3.0 if flags == G.GPTQ_FACTOR_REVERSED else 4.0 / 3.0) * d ** 3
+    # the factor's algorithmic work: Cholesky and triangular inverse (2/3 d^3) on the reversed route, twice that
+    # with the inverse and its re-factorization; the R form needs the Cholesky factor only (1/3 d^3)
+    factor_flops = {G.GPTQ_FACTOR_REVERSED: 2.0 / 3.0, G.GPTQ_FACTOR_INVERSE_RECHOL: 4.0 / 3.0,
+                    G.GPTQ_FACTOR_R_FORM: 1.0 / 3.0}[flags] * d ** 3
     loop_flops = out * d * (d - 1)
     x_bytes = n * d * (2 if cfg.dtype == "bf16" else 4)
     hess_ms = stage_ms["hessian"]

@@ -56,6 +56,14 @@ typedef enum { GPTQ_F32 = 0, GPTQ_BF16 = 1 } gptq_dtype;
  *    guide's _hessian_inverse_chol takes ("The code, line by line"), at twice the flops. */
 #define GPTQ_FACTOR_REVERSED 0u
 #define GPTQ_FACTOR_INVERSE_RECHOL 1u
+/* GPTQ_FACTOR_R_FORM (2): instead of U, the factor form that gptq_quantize_layer_r reads (the same route
+ *    without the triangular inverse). R = U^-1 = J chol(J H J) J is upper triangular with R R^T = H (P^T H P
+ *    with act_order): its upper triangle, diagonal included, holds R. The loop also needs U's 128 x 128
+ *    diagonal blocks, which are the inverses of R's: for the block of columns [b, b + p) (b a multiple of
+ *    128, p = min(128, in - b)) the strictly lower part of that diagonal block holds J U_bb J, i.e.
+ *    element (b + r, b + c), r > c, is U[b + p - 1 - r][b + p - 1 - c]. Everything else is 0. Requires
+ *    in % 64 == 0 (UNSUPPORTED otherwise); not combined with GPTQ_FACTOR_INVERSE_RECHOL. */
+#define GPTQ_FACTOR_R_FORM 2u
 
 /* ---------------------------------------------------------------------------------------------------
  * 1. Hessian accumulation. GPTQ guide, "The idea": H = 2 X^T X / n is the curvature of the layer's
@@ -98,10 +106,12 @@ int gptq_hessian_accumulate(const void* X, int x_dtype, int64_t n_rows, int64_t 
  *             quantization order; the strictly lower triangle is set to 0.
  *  perm       out: int32[in], perm[j] = original input index quantized at position j.
  *  dead       out: uint8[in], 1 for dead inputs (original order).
- *  flags      GPTQ_FACTOR_REVERSED (0) or GPTQ_FACTOR_INVERSE_RECHOL; other bits -> INVALID_ARG.
+ *  flags      GPTQ_FACTOR_REVERSED (0), GPTQ_FACTOR_INVERSE_RECHOL or GPTQ_FACTOR_R_FORM (then U receives
+ *             the R form described with that flag); other values -> INVALID_ARG.
  *  ws         at least gptq_prepare_workspace_bytes(in) bytes.
  *  Synchronises `stream` once. Errors: INVALID_ARG (in < 1, n_total < 1, damp < 0 or not finite, NULL
- *  pointer, unknown flags), WORKSPACE, NOT_SPD (a Cholesky pivot below 2^-1000, in particular <= 0, e.g.
+ *  pointer, unknown flags), UNSUPPORTED (GPTQ_FACTOR_R_FORM with in % 64 != 0), WORKSPACE, NOT_SPD (a
+ *  Cholesky pivot below 2^-1000, in particular <= 0, e.g.
  *  damp = 0 with a rank-deficient X),
  *  NONFINITE (NaN/Inf in S or colsq, or met in a pivot), HIP. On NOT_SPD/NONFINITE, U is unspecified.
  * ------------------------------------------------------------------------------------------------- */
@@ -174,6 +184,30 @@ int gptq_quantize_layer_ex(const void* W, int w_dtype, int64_t out, int64_t in, 
                            int bits, int group, int grid,
                            int8_t* codes, float* scales, int32_t* zeros, int32_t* g_idx, double* row_loss,
                            void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------------------------
+ * 3''. The same loop from the R form of the factor (gptq_prepare_chol with GPTQ_FACTOR_R_FORM), which
+ *    prepare forms without the triangular inverse. Lesson "GPTQ's error-compensation loop": after the
+ *    loop, every row's start minus its quantized values is its errors times U, W0 - Q = E U, so E = D R with
+ *    D = W0 - Q and R = U^-1. The columns of a 128-column panel P, when P's turn comes, therefore hold
+ *    W0_P + (D_A R_AP) U_PP, A the columns before P: the loop keeps T = D R up to date with the same
+ *    lazy products as the U route (T += D R instead of W -= E U), and each panel starts from
+ *    W0_P + T_P U_PP, U_PP being U's diagonal block (with one grid per row, T_P enters the loop's steps
+ *    instead), its columns then quantized exactly as in gptq_quantize_layer_ex.
+ *
+ *  R          the R form written by gptq_prepare_chol with GPTQ_FACTOR_R_FORM (in x in, in quantization
+ *             order), or the same layout built by the caller.
+ *  Requires in % 64 == 0 and group == 0 or 128 % group == 0 (a wider group takes its scale from columns
+ *  beyond the current panel, whose updated values the R form does not give): UNSUPPORTED otherwise.
+ *  Everything else (arguments, grids, outputs, layouts, workspace, errors) is as for gptq_quantize_layer_ex;
+ *  the results agree with it up to rounding (codes may differ only where a weight lies within rounding of
+ *  a grid midpoint).
+ * ------------------------------------------------------------------------------------------------- */
+int gptq_quantize_layer_r(const void* W, int w_dtype, int64_t out, int64_t in, int64_t ld_w,
+                          const double* R, const int32_t* perm, const uint8_t* dead,
+                          int bits, int group, int grid,
+                          int8_t* codes, float* scales, int32_t* zeros, int32_t* g_idx, double* row_loss,
+                          void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------------------------
  * 4. Packed codes and a consumer of the outputs. GPTQ guide, "When it breaks": the layer is stored as

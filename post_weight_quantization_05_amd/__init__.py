@@ -3,7 +3,7 @@
 The Python layer only marshals arguments; see include/gptq_mi355x.h for the ABI.
 """
 from ._lib import (  # noqa: F401
-    GPTQ_BF16, GPTQ_F32, GPTQ_FACTOR_INVERSE_RECHOL, GPTQ_FACTOR_REVERSED, GPTQ_GRID_ASYMMETRIC,
+    GPTQ_BF16, GPTQ_F32, GPTQ_FACTOR_INVERSE_RECHOL, GPTQ_FACTOR_R_FORM, GPTQ_FACTOR_REVERSED, GPTQ_GRID_ASYMMETRIC,
     GPTQ_GRID_SYMMETRIC, GPTQError, LIB_PATH, load,
     status_string,
 )

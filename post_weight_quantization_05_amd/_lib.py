@@ -20,6 +20,7 @@ GPTQ_BF16 = 1
 
 GPTQ_FACTOR_REVERSED = 0  # the default route
 GPTQ_FACTOR_INVERSE_RECHOL = 1
+GPTQ_FACTOR_R_FORM = 2  # R = U^-1 and U's 128 x 128 diagonal blocks, for gptq_quantize_layer_r
 
 GPTQ_GRID_SYMMETRIC = 0
 GPTQ_GRID_ASYMMETRIC = 1
@@ -43,6 +44,9 @@ SIGNATURES = {
     "gptq_quantize_layer_ex": (ctypes.c_int, [_vp, ctypes.c_int, _c_int64, _c_int64, _c_int64, _vp, _vp, _vp,
                                               ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _vp, _vp,
                                               _vp, ctypes.c_size_t, _vp]),
+    "gptq_quantize_layer_r": (ctypes.c_int, [_vp, ctypes.c_int, _c_int64, _c_int64, _c_int64, _vp, _vp, _vp,
+                                             ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _vp, _vp,
+                                             _vp, ctypes.c_size_t, _vp]),
     "gptq_hessian_accumulate_noalloc": (ctypes.c_int, [_vp, ctypes.c_int, _c_int64, _c_int64, _c_int64, _vp, _vp,
                                                        ctypes.POINTER(_c_int64), _vp]),
     "gptq_packed_words_per_row": (_c_int64, [_c_int64, ctypes.c_int]),

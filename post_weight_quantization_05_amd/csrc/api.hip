@@ -66,7 +66,9 @@ int gptq_prepare_chol(const double* S, const double* colsq, int64_t n_total, int
   if (!S || !colsq || !U || !perm || !dead) return GPTQ_ERR_INVALID_ARG;
   if (in < 1 || in > MAX_IN || n_total < 1) return GPTQ_ERR_INVALID_ARG;
   if (!(damp >= 0.0) || !std::isfinite(damp)) return GPTQ_ERR_INVALID_ARG;
-  if ((flags & ~GPTQ_FACTOR_INVERSE_RECHOL) != 0u) return GPTQ_ERR_INVALID_ARG;
+  if (flags != GPTQ_FACTOR_REVERSED && flags != GPTQ_FACTOR_INVERSE_RECHOL && flags != GPTQ_FACTOR_R_FORM)
+    return GPTQ_ERR_INVALID_ARG;
+  if (flags == GPTQ_FACTOR_R_FORM && in % 64 != 0) return GPTQ_ERR_UNSUPPORTED;
   if (!ws || ws_bytes < prepare_ws_bytes(in)) return GPTQ_ERR_WORKSPACE;
   unsigned dev_status = 0;
   hipError_t e = prepare_launch(S, colsq, n_total, in, damp, act_order ? 1 : 0, flags, U, perm, dead, ws,
@@ -97,6 +99,26 @@ int gptq_quantize_layer_ex(const void* W, int w_dtype, int64_t out, int64_t in, 
   unsigned dev_status = 0;
   const hipError_t e = quantize_launch(W, w_dtype, out, in, ld_w, U, perm, dead, bits, group, grid, codes, scales,
                                        zeros, g_idx, row_loss, ws, reinterpret_cast<hipStream_t>(stream), &dev_status);
+  if (e != hipSuccess) return GPTQ_ERR_HIP;
+  return (dev_status & DEV_STATUS_NONFINITE) ? GPTQ_ERR_NONFINITE : GPTQ_OK;
+}
+
+int gptq_quantize_layer_r(const void* W, int w_dtype, int64_t out, int64_t in, int64_t ld_w, const double* R,
+                          const int32_t* perm, const uint8_t* dead, int bits, int group, int grid, int8_t* codes,
+                          float* scales, int32_t* zeros, int32_t* g_idx, double* row_loss, void* ws,
+                          size_t ws_bytes, void* stream) {
+  if (!W || !R || !perm || !dead || !codes || !scales) return GPTQ_ERR_INVALID_ARG;
+  if (grid != GPTQ_GRID_SYMMETRIC && grid != GPTQ_GRID_ASYMMETRIC) return GPTQ_ERR_INVALID_ARG;
+  if (grid == GPTQ_GRID_ASYMMETRIC && !zeros) return GPTQ_ERR_INVALID_ARG;
+  if (out < 1 || in < 1 || in > MAX_IN || out > MAX_OUT || ld_w < in || !valid_dtype(w_dtype))
+    return GPTQ_ERR_INVALID_ARG;
+  if (bits < 2 || bits > 8 || group < 0) return GPTQ_ERR_INVALID_ARG;
+  if (in % 64 != 0 || (group != 0 && 128 % group != 0)) return GPTQ_ERR_UNSUPPORTED;
+  if (!ws || ws_bytes < quantize_ws_bytes(out, in)) return GPTQ_ERR_WORKSPACE;
+  unsigned dev_status = 0;
+  const hipError_t e = quantize_launch(W, w_dtype, out, in, ld_w, R, perm, dead, bits, group, grid, codes, scales,
+                                       zeros, g_idx, row_loss, ws, reinterpret_cast<hipStream_t>(stream), &dev_status,
+                                       true);
   if (e != hipSuccess) return GPTQ_ERR_HIP;
   return (dev_status & DEV_STATUS_NONFINITE) ? GPTQ_ERR_NONFINITE : GPTQ_OK;
 }

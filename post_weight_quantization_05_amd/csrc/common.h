@@ -57,7 +57,7 @@ size_t quantize_ws_bytes(int64_t out, int64_t in);
 hipError_t quantize_launch(const void* W, int w_dtype, int64_t out, int64_t in, int64_t ld_w, const double* U,
                            const int32_t* perm, const uint8_t* dead, int bits, int group, int grid, int8_t* codes,
                            float* scales, int32_t* zeros, int32_t* g_idx, double* row_loss, void* ws,
-                           hipStream_t stream, unsigned* host_status);
+                           hipStream_t stream, unsigned* host_status, bool rform = false);
 
 // Packed codes and the dequantizing matmul (pack.hip)
 int64_t packed_words_per_row(int64_t in, int bits);

@@ -235,6 +235,9 @@ static_assert(NBO == 256, "an outer block's panel is the K of its successor's fi
 #ifndef GPTQ_FACTOR_DEFER
 #define GPTQ_FACTOR_DEFER 160
 #endif
+#ifndef GPTQ_FACTOR_DEFER_RFORM
+#define GPTQ_FACTOR_DEFER_RFORM 640
+#endif
 #ifndef GPTQ_FACTOR_DEFER_FILL
 #define GPTQ_FACTOR_DEFER_FILL 640
 #endif
@@ -243,7 +246,7 @@ static_assert(NBO == 256, "an outer block's panel is the K of its successor's fi
 // Z, G (both null, or Z d x d and G two buffers of 64 rows per block x 64): also form Z = L^-1 (lower part)
 // with the steps' idle CUs (InvFill in dgemm.h), finished by three launches after the last step.
 hipError_t potrf_lower(double* A, int d, double* Dinv, double* Lst, unsigned* status, bool place_l, double* Z,
-                       double* G, hipStream_t stream) {
+                       double* G, hipStream_t stream, int defer = -1) {
   const int S = (d + NB - 1) / NB;
   InvFill inv{};
   inv.L = A;
@@ -253,7 +256,7 @@ hipError_t potrf_lower(double* A, int d, double* Dinv, double* Lst, unsigned* st
   inv.G[1] = G ? G + (int64_t)S * NB * NB : nullptr;
   inv.d = d;
   inv.S = S;
-  const int defer_per_step = Z ? GPTQ_FACTOR_DEFER_FILL : GPTQ_FACTOR_DEFER;
+  const int defer_per_step = defer >= 0 ? defer : Z ? GPTQ_FACTOR_DEFER_FILL : GPTQ_FACTOR_DEFER;
   // The trailing update of an outer block is split in two: the next outer block's columns right away
   // (its first step needs them), the rest (columns from the block after that on) deferred and spread over
   // the next outer block's steps as extra workgroups. Per tile the arithmetic is unchanged.
@@ -399,6 +402,73 @@ size_t prepare_ws_bytes(int64_t in) {
   return b;
 }
 
+// The R form's diagonal blocks (see GPTQ_FACTOR_R_FORM): for the quantization panel [b0, b0 + pw) the inverse
+// of L's diagonal block over the reversed rows [s, s + pw), s = in - b0 - pw, goes into the strictly lower part
+// of the output's diagonal block, unreversed (output (b0 + r, b0 + c) = (L_ss^-1)[r][c], r > c): that is
+// J U_PP J. With in % 64 == 0, s is a multiple of 64 and the block is one or two of the factorization's
+// 64 x 64 diagonal blocks, whose inverses the steps left in Dinv; for two,
+//   [A 0; B C]^-1 = [A^-1 0; -C^-1 B A^-1  C^-1],
+// the off-diagonal part formed here in fp64 on the matrix cores (one workgroup per panel, B A^-1 and then
+// C^-1 (B A^-1), the k-steps above C^-1's diagonal skipped).
+__global__ __launch_bounds__(256) void k_rform_diag(const double* __restrict__ L, const double* __restrict__ Dinv,
+                                                    int d, double* __restrict__ M) {
+  __shared__ double Ai[NB][NB + 1], Ci[NB][NB + 1], Bb[NB][NB + 1], Y[NB][NB + 1];
+  const int b0 = blockIdx.x * 128;
+  const int pw = min(128, d - b0);
+  const int s = d - b0 - pw;
+  const int kb = s / NB;
+  const int tid = threadIdx.x;
+  double* out = M + (int64_t)b0 * d + b0;
+  auto put = [&](int r, int c, double v) { out[(int64_t)r * d + c] = v; };
+  // the diagonal 64 x 64 inverses, strictly lower parts (the blocks are lower; zeros are staged above)
+  for (int e = tid; e < NB * NB; e += 256) {
+    const int r = e / NB, c = e % NB;
+    const double a = Dinv[(int64_t)kb * NB * NB + e];
+    if (r > c) put(r, c, a);
+    Ai[r][c] = (r >= c) ? a : 0.0;
+    if (pw == 128) {
+      const double cc = Dinv[(int64_t)(kb + 1) * NB * NB + e];
+      if (r > c) put(NB + r, NB + c, cc);
+      Ci[r][c] = (r >= c) ? cc : 0.0;
+      Bb[r][c] = L[(int64_t)(s + NB + r) * d + s + c];
+    }
+  }
+  if (pw < 128) return;
+  __syncthreads();
+  // both 64 x 64 x 64 products on the matrix cores: wave wv forms the 16 rows 16 wv .. 16 wv + 15 of the
+  // result in four 16 x 16 blocks (v_mfma_f64_16x16x4f64: lane l supplies the left operand's
+  // [l % 16][k0 + l / 16] and the right operand's [k0 + l / 16][l % 16]; accumulator entry e of lane l is
+  // row 4e + l / 16, column l % 16 of the block)
+  const int lane = tid & 63, wv = tid >> 6;
+  const int lr = lane & 15, lk = lane >> 4;
+  f64x4 acc[4];
+  // Y = B A^-1
+#pragma unroll
+  for (int q = 0; q < 4; ++q) acc[q] = f64x4{0.0, 0.0, 0.0, 0.0};
+  for (int k0 = 0; k0 < NB; k0 += 4) {
+    const double av = Bb[16 * wv + lr][k0 + lk];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[q] = diagblock::mfma16(av, Ai[k0 + lk][16 * q + lr], acc[q]);
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) Y[16 * wv + 4 * e + lk][16 * q + lr] = acc[q][e];
+  __syncthreads();
+  // X21 = -C^-1 Y (C^-1 lower: the wave's rows need k < 16 wv + 16)
+#pragma unroll
+  for (int q = 0; q < 4; ++q) acc[q] = f64x4{0.0, 0.0, 0.0, 0.0};
+  for (int k0 = 0; k0 < 16 * wv + 16; k0 += 4) {
+    const double av = Ci[16 * wv + lr][k0 + lk];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[q] = diagblock::mfma16(av, Y[k0 + lk][16 * q + lr], acc[q]);
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) put(NB + 16 * wv + 4 * e + lk, 16 * q + lr, -acc[q][e]);
+}
+
 hipError_t prepare_launch(const double* S, const double* colsq, int64_t n_total, int64_t in, double damp,
                           int act_order, unsigned flags, double* U, int32_t* perm, uint8_t* dead, void* ws,
                           hipStream_t stream, unsigned* host_status) {
@@ -437,6 +507,18 @@ hipError_t prepare_launch(const double* S, const double* colsq, int64_t n_total,
                      d, reversed ? 1 : 0, A);
   GPTQ_TRY(hipGetLastError());
 
+  if (flags == GPTQ_FACTOR_R_FORM) {
+    // R = J L J (L placed in A), then the inverses of its 128 x 128 diagonal blocks in their lower parts
+    GPTQ_TRY(potrf_lower(A, d, Dinv, Lst, status, true, nullptr, G, stream, GPTQ_FACTOR_DEFER_RFORM));
+    hipLaunchKernelGGL(k_reverse_to_upper, dim3((unsigned)ceil_div(d, 256), (unsigned)std::min(d, 4096)), dim3(256),
+                       0, stream, A, d, U);
+    GPTQ_TRY(hipGetLastError());
+    hipLaunchKernelGGL(k_rform_diag, dim3((unsigned)ceil_div(d, 128)), dim3(256), 0, stream, A, Dinv, d, U);
+    GPTQ_TRY(hipGetLastError());
+    GPTQ_TRY(hipMemcpyAsync(host_status, status, sizeof(unsigned), hipMemcpyDeviceToHost, stream));
+    GPTQ_TRY(hipStreamSynchronize(stream));
+    return hipSuccess;
+  }
   const bool fill = d <= FILL_MAX;
   GPTQ_TRY(potrf_lower(A, d, Dinv, Lst, status, false, fill ? Z : nullptr, G, stream));
   double* Li = Z;  // L^-1 (lower part)

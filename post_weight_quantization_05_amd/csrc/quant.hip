@@ -192,13 +192,18 @@ __global__ __launch_bounds__(256) void k_rowprep(const T* __restrict__ W, int64_
 // INPANEL = false: one scale per row, or groups that are multiples of 128 (the scale is recomputed at
 // panels where b0 % group == 0 and carried across panels in scale_row); INPANEL = true: groups dividing
 // 128 (boundaries inside the panel at j % group == 0).
-template <bool INPANEL, bool ASYM>
+// RF: the factor comes in the R form (GPTQ_FACTOR_R_FORM): the block's U is read from the reversed lower part of
+// R's diagonal block, 1 / U[j][j] is R[j][j], Wq holds the starting weights W0 and T the accumulated D R of
+// the earlier panels; the workgroup first forms its rows' W0_P + T_P U_PP (on the matrix cores, 16 rows x
+// 128 x 128), and stores D = W0 - Q instead of the errors for the products that follow.
+template <bool INPANEL, bool ASYM, bool RF>
 __global__ __launch_bounds__(256) void k_panel(double* __restrict__ Wq, int out, int in, int b0,
                                                const double* __restrict__ U, const int32_t* __restrict__ perm,
                                                double* __restrict__ scale_row, double* __restrict__ zero_row,
                                                double qmax, int group, int n_groups, int8_t* __restrict__ codes,
                                                float* __restrict__ scales, int32_t* __restrict__ zeros,
-                                               double* __restrict__ Err, int ld_err, double* __restrict__ row_loss) {
+                                               double* __restrict__ Err, int ld_err, double* __restrict__ row_loss,
+                                               const double* __restrict__ T, int t_valid) {
   // U panel block, upper part only: row a holds columns 16 (a / 16) .. 127 (the 16-column blocks that reach
   // the diagonal, zeros left of it), 72 KB instead of 128, so two panel workgroups fit in a CU (see
   // launch_panel)
@@ -207,6 +212,32 @@ __global__ __launch_bounds__(256) void k_panel(double* __restrict__ Wq, int out,
   __shared__ int pidx[PW];
   const int tid = threadIdx.x;
   const int pw = min(PW, in - b0);
+  const int c = tid & 15;
+  const int r = blockIdx.x * 16 + (tid >> 4);
+  const bool rok = r < out;
+  // the global loads that do not depend on the U block are issued first, so their latency overlaps its
+  // loads: the row's weights (16 lanes per row, lane c holding columns c + 16 m), RF: the row's T_P, and
+  // the pivot and permutation entry of column tid
+  double* wrow = Wq + (int64_t)(rok ? r : 0) * in;
+  double w[8];
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+    const int col = c + 16 * m;
+    w[m] = (rok && col < pw) ? wrow[b0 + col] : 0.0;
+  }
+  double t[8];
+  if constexpr (RF) {
+    const double* trow = T + (int64_t)(rok ? r : 0) * in + b0;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const int col = c + 16 * m;
+      t[m] = (t_valid && rok && col < pw) ? trow[col] : 0.0;
+    }
+  }
+  static_assert(PW <= 256, "one thread per panel column");
+  const bool dcol = tid < pw;
+  const double udiag = dcol ? U[(int64_t)(b0 + tid) * in + b0 + tid] : 0.0;  // RF: R[j][j] = 1 / U[j][j]
+  const int pcol = dcol ? perm[b0 + tid] : 0;
   // loaded one 16-row block at a time (block k: 16 rows of 128 - 16k stored columns, 8 - k elements per
   // thread), all of a block's loads in flight before its stores
   static_for<0, 8>([&](auto kc) {
@@ -218,26 +249,54 @@ __global__ __launch_bounds__(256) void k_panel(double* __restrict__ Wq, int out,
     for (int q = 0; q < NE; ++q) {
       const int i = tid + 256 * q;
       const int a = 16 * k + i / RL, b = 16 * k + i % RL;
-      v[q] = (a < pw && b < pw && b >= a) ? U[(int64_t)(b0 + a) * in + b0 + b] : 0.0;
+      if (RF)  // U[a][b] = R form (b0 + pw - 1 - a, b0 + pw - 1 - b) for a < b (the diagonal comes below)
+        v[q] = (a < pw && b < pw && b > a) ? U[(int64_t)(b0 + pw - 1 - a) * in + b0 + pw - 1 - b] : 0.0;
+      else
+        v[q] = (a < pw && b < pw && b >= a) ? U[(int64_t)(b0 + a) * in + b0 + b] : 0.0;
     }
 #pragma unroll
     for (int q = 0; q < NE; ++q) Us[urow(16 * k) + tid + 256 * q] = v[q];
   });
-  for (int a = tid; a < PW; a += 256) {
-    rdiag[a] = (a < pw) ? 1.0 / U[(int64_t)(b0 + a) * in + b0 + a] : 0.0;
-    pidx[a] = (a < pw) ? min(max(perm[b0 + a], 0), in - 1) : 0;
+  if (RF) __syncthreads();  // the block's stores above are done before the diagonal is written
+  if (tid < PW) {
+    if (RF) {
+      rdiag[tid] = udiag;
+      if (dcol) Us[urow(tid) + tid - 16 * (tid >> 4)] = 1.0 / udiag;  // U[j][j], for the first product below
+    } else {
+      rdiag[tid] = dcol ? 1.0 / udiag : 0.0;
+    }
+    pidx[tid] = dcol ? min(max(pcol, 0), in - 1) : 0;
   }
   __syncthreads();
 
-  const int c = tid & 15;
-  const int r = blockIdx.x * 16 + (tid >> 4);
-  const bool rok = r < out;
-  double* wrow = Wq + (int64_t)(rok ? r : 0) * in;
-  double w[8];
+  double w0[8];  // RF: the starting weights of the lane's columns, for D = W0 - Q
+  if constexpr (RF) {
 #pragma unroll
-  for (int m = 0; m < 8; ++m) {
-    const int col = c + 16 * m;
-    w[m] = (rok && col < pw) ? wrow[b0 + col] : 0.0;
+    for (int m = 0; m < 8; ++m) w0[m] = w[m];
+    if constexpr (!INPANEL) {
+      if (t_valid) {
+        // one grid per row (group 0, the only case without in-panel groups that the R form takes): only
+        // the column being decided needs its current value, so the panel starts from W0_k + T_k U_kk and
+        // the rest of T_P U_PP enters the loop, where step j takes off (e_j - T_j) U_jk, not e_j U_jk
+#pragma unroll
+        for (int m = 0; m < 8; ++m) w[m] = fma(t[m], Us[urow(c + 16 * m) + c], w[m]);
+      }
+    } else if (t_valid) {
+      // groups inside the panel: a group's grid is set from the current values of all its columns, so the
+      // whole T_P U_PP is added first, by the lanes that own the columns (T_j broadcast from lane j % 16 of
+      // the row, U_PP's row j read from LDS as in the loop below; no step depends on another)
+#pragma unroll
+      for (int jm = 0; jm < 8; ++jm) {
+        static_for<0, 16>([&](auto jlc) {
+          constexpr int jl = decltype(jlc)::value;
+          const int j = jm * 16 + jl;
+          const double tj = bcast16<jl>(t[jm]);
+#pragma unroll
+          for (int m = 0; m < 8; ++m)
+            if (m >= jm) w[m] = fma(tj, Us[urow(j) + c + 16 * (m - jm)], w[m]);
+        });
+      }
+    }
   }
 
   double s = 1.0;
@@ -284,11 +343,12 @@ __global__ __launch_bounds__(256) void k_panel(double* __restrict__ Wq, int out,
   }
 
   int code_m[8];
-  double err_m[8];
+  double err_m[8], d_m[8];  // d_m: RF, W0 - Q of the lane's columns
 #pragma unroll
   for (int m = 0; m < 8; ++m) {
     code_m[m] = 0;
     err_m[m] = 0.0;
+    d_m[m] = 0.0;
   }
 
   // row j of the U block and 1/U[j][j] are read from LDS one step ahead, so the LDS latency stays off
@@ -340,13 +400,23 @@ __global__ __launch_bounds__(256) void k_panel(double* __restrict__ Wq, int out,
           qv = cq * s;
         }
         asm volatile("" : "+v"(qv));  // q is rounded before the subtraction (no contraction into an FMA)
-        const double e = (wj - qv) * dcur;
+        const double dq = wj - qv;
+        const double e = dq * dcur;
+        double f = e;  // what the later columns k take off, times U[j][k]
+        if constexpr (RF && !INPANEL) f = fma(dq, dcur, -bcast16<jl>(t[jm]));  // e_j - T_j, rounded once
         code_m[jm] = (c == jl) ? (int)cq : code_m[jm];
         err_m[jm] = (c == jl) ? e : err_m[jm];
-        asm volatile("" : "+v"(code_m[jm]), "+v"(err_m[jm]));
+        if constexpr (RF && INPANEL) {
+          // the scale changes at group boundaries inside the panel, so D is formed here (and here, so that q
+          // is not kept for all 128 steps); with one scale per row it is formed after the loop
+          d_m[jm] = (c == jl) ? w0[jm] - qv : d_m[jm];
+          asm volatile("" : "+v"(code_m[jm]), "+v"(err_m[jm]), "+v"(d_m[jm]));
+        } else {
+          asm volatile("" : "+v"(code_m[jm]), "+v"(err_m[jm]));
+        }
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
-          if (m >= jm) w[m] = fma(-e, ucur[m], w[m]);
+          if (m >= jm) w[m] = fma(-f, ucur[m], w[m]);
         }
         if (j + 1 < PW) {
 #pragma unroll
@@ -367,7 +437,15 @@ __global__ __launch_bounds__(256) void k_panel(double* __restrict__ Wq, int out,
       const int col = c + 16 * m;
       if (col < pw) {
         crow[pidx[col]] = (int8_t)code_m[m];
-        erow[col] = err_m[m];
+        if constexpr (RF && !INPANEL) {
+          // group 0 (the only one without in-panel groups that the R form takes): the row's one grid gives
+          // back the loop's q from the code, rounded as there before the subtraction
+          const double cq = (double)code_m[m];
+          double qv = ASYM ? s * (cq - z) : cq * s;
+          asm volatile("" : "+v"(qv));
+          d_m[m] = w0[m] - qv;
+        }
+        erow[col] = RF ? d_m[m] : err_m[m];
         lsum = fma(err_m[m], err_m[m], lsum);
       }
     }
@@ -392,7 +470,8 @@ __global__ void k_gidx(const int32_t* __restrict__ perm, int in, int group, int3
 size_t quantize_ws_bytes(int64_t out, int64_t in) {
   size_t b = 0;
   b += align_up((size_t)out * in * sizeof(double), 256);  // working copy
-  b += align_up((size_t)out * OB * sizeof(double), 256);  // errors of one outer block
+  b += align_up((size_t)out * OB * sizeof(double), 256);  // errors (or, R form, D = W0 - Q) of one outer block
+  b += align_up((size_t)out * in * sizeof(double), 256);  // R form: T, the accumulated D R
   b += align_up((size_t)out * sizeof(double), 256);       // current fp64 scale per row
   b += align_up((size_t)out * sizeof(double), 256);       // current zero point per row (asymmetric grid)
   b += 256;                                                // status word
@@ -430,27 +509,27 @@ static int cu_count() {
   return n;
 }
 
-template <bool ASYM>
+template <bool ASYM, bool RF>
 static hipError_t launch_panel(bool inpanel, dim3 grid, double* Wq, int out, int in, int b0, const double* U,
                                const int32_t* perm, double* scale_row, double* zero_row, double qmax, int group,
                                int n_groups, int8_t* codes, float* scales, int32_t* zeros, double* errp,
-                               int ld_err, double* row_loss, hipStream_t stream) {
+                               int ld_err, double* row_loss, const double* T, int t_valid, hipStream_t stream) {
   const size_t lds = ((int)grid.x <= cu_count()) ? PANEL_SPREAD_LDS : 0;
   if (inpanel)
-    k_panel<true, ASYM><<<grid, dim3(256), lds, stream>>>(Wq, out, in, b0, U, perm, scale_row, zero_row, qmax,
-                                                          group, n_groups, codes, scales, zeros, errp, ld_err,
-                                                          row_loss);
+    k_panel<true, ASYM, RF><<<grid, dim3(256), lds, stream>>>(Wq, out, in, b0, U, perm, scale_row, zero_row, qmax,
+                                                              group, n_groups, codes, scales, zeros, errp, ld_err,
+                                                              row_loss, T, t_valid);
   else
-    k_panel<false, ASYM><<<grid, dim3(256), lds, stream>>>(Wq, out, in, b0, U, perm, scale_row, zero_row, qmax,
-                                                           group, n_groups, codes, scales, zeros, errp, ld_err,
-                                                           row_loss);
+    k_panel<false, ASYM, RF><<<grid, dim3(256), lds, stream>>>(Wq, out, in, b0, U, perm, scale_row, zero_row, qmax,
+                                                               group, n_groups, codes, scales, zeros, errp, ld_err,
+                                                               row_loss, T, t_valid);
   return hipGetLastError();
 }
 
 hipError_t quantize_launch(const void* W, int w_dtype, int64_t out64, int64_t in64, int64_t ld_w, const double* U,
                            const int32_t* perm, const uint8_t* dead, int bits, int group, int grid, int8_t* codes,
                            float* scales, int32_t* zeros, int32_t* g_idx, double* row_loss, void* ws,
-                           hipStream_t stream, unsigned* host_status) {
+                           hipStream_t stream, unsigned* host_status, bool rform) {
   const int out = (int)out64, in = (int)in64;
   const bool asym = (grid == GPTQ_GRID_ASYMMETRIC);
   char* w = reinterpret_cast<char*>(ws);
@@ -458,6 +537,8 @@ hipError_t quantize_launch(const void* W, int w_dtype, int64_t out64, int64_t in
   w += align_up((size_t)out * in * sizeof(double), 256);
   double* Err = reinterpret_cast<double*>(w);
   w += align_up((size_t)out * OB * sizeof(double), 256);
+  double* Tacc = reinterpret_cast<double*>(w);  // R form only
+  w += align_up((size_t)out * in * sizeof(double), 256);
   double* scale_row = reinterpret_cast<double*>(w);
   w += align_up((size_t)out * sizeof(double), 256);
   double* zero_row = reinterpret_cast<double*>(w);
@@ -480,25 +561,41 @@ hipError_t quantize_launch(const void* W, int w_dtype, int64_t out64, int64_t in
                                    scales, zeros, row_loss, status, stream);
   if (e != hipSuccess) return e;
 
+  // R form: the products accumulate T += D R (alpha +1) instead of W -= E U; T is written before it is read
+  // (beta 0 for the first panel's update inside the first outer block and for the first block update, the
+  // first products to reach each column; the first panel has no T)
+  const double alpha = rform ? 1.0 : -1.0;
+  double* Cw = rform ? Tacc : Wq;
   const dim3 pgrid((unsigned)ceil_div(out, 16));
   for (int ob0 = 0; ob0 < in; ob0 += ob) {
     const int ob1 = min(in, ob0 + ob);
     for (int b0 = ob0; b0 < ob1; b0 += PW) {
       double* errp = Err + (b0 - ob0);  // this panel's columns of the outer block's error matrix
       const bool inpanel = group != 0 && PW % group == 0;
-      e = asym ? launch_panel<true>(inpanel, pgrid, Wq, out, in, b0, U, perm, scale_row, zero_row, qmax, group,
-                                    n_groups, codes, scales, zeros, errp, OB, row_loss, stream)
-               : launch_panel<false>(inpanel, pgrid, Wq, out, in, b0, U, perm, scale_row, zero_row, qmax, group,
-                                     n_groups, codes, scales, zeros, errp, OB, row_loss, stream);
+      const int t_valid = b0 > 0 ? 1 : 0;
+      if (rform)
+        e = asym ? launch_panel<true, true>(inpanel, pgrid, Wq, out, in, b0, U, perm, scale_row, zero_row, qmax,
+                                            group, n_groups, codes, scales, zeros, errp, OB, row_loss, Tacc,
+                                            t_valid, stream)
+                 : launch_panel<false, true>(inpanel, pgrid, Wq, out, in, b0, U, perm, scale_row, zero_row, qmax,
+                                             group, n_groups, codes, scales, zeros, errp, OB, row_loss, Tacc,
+                                             t_valid, stream);
+      else
+        e = asym ? launch_panel<true, false>(inpanel, pgrid, Wq, out, in, b0, U, perm, scale_row, zero_row, qmax,
+                                             group, n_groups, codes, scales, zeros, errp, OB, row_loss, nullptr, 0,
+                                             stream)
+                 : launch_panel<false, false>(inpanel, pgrid, Wq, out, in, b0, U, perm, scale_row, zero_row, qmax,
+                                              group, n_groups, codes, scales, zeros, errp, OB, row_loss, nullptr,
+                                              0, stream);
       if (e != hipSuccess) return e;
       const int b1 = b0 + PW;
       if (b1 < ob1) {  // the rest of the outer block: W[:, b1:ob1] -= Err[:, panel] U[b0:b1, b1:ob1]
         DgemmArgs t{};
         t.A = errp; t.lda = OB;
         t.B = U + (int64_t)b0 * in + b1; t.ldb = in;
-        t.C = Wq + b1; t.ldc = in;
+        t.C = Cw + b1; t.ldc = in;
         t.M = out; t.N = ob1 - b1; t.K = PW;
-        t.alpha = -1.0; t.beta = 1.0;
+        t.alpha = alpha; t.beta = (rform && b0 == 0) ? 0.0 : 1.0;
         t.kmode = KMODE_FULL;
         e = dgemm_launch(t, false, false, 1, stream);
         if (e != hipSuccess) return e;
@@ -508,9 +605,9 @@ hipError_t quantize_launch(const void* W, int w_dtype, int64_t out64, int64_t in
       DgemmArgs t{};
       t.A = Err; t.lda = OB;
       t.B = U + (int64_t)ob0 * in + ob1; t.ldb = in;
-      t.C = Wq + ob1; t.ldc = in;
+      t.C = Cw + ob1; t.ldc = in;
       t.M = out; t.N = in - ob1; t.K = ob1 - ob0;
-      t.alpha = -1.0; t.beta = 1.0;
+      t.alpha = alpha; t.beta = (rform && ob0 == 0) ? 0.0 : 1.0;
       t.kmode = KMODE_FULL;
       e = dgemm_launch(t, false, false, 1, stream);
       if (e != hipSuccess) return e;

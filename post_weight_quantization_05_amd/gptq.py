@@ -13,12 +13,12 @@ from dataclasses import dataclass
 import torch
 
 from . import _lib
-from ._lib import GPTQ_BF16, GPTQ_F32, GPTQ_FACTOR_INVERSE_RECHOL, GPTQ_FACTOR_REVERSED, check
+from ._lib import GPTQ_BF16, GPTQ_F32, GPTQ_FACTOR_INVERSE_RECHOL, GPTQ_FACTOR_R_FORM, GPTQ_FACTOR_REVERSED, check
 
 __all__ = [
     "HessianState", "hessian_accumulate", "prepare_chol", "quantize_layer", "gptq_quantize", "QuantResult",
     "pack_codes", "dequant_matmul", "apply_layerwise", "QuantizedLayer",
-    "GPTQ_FACTOR_INVERSE_RECHOL", "GPTQ_FACTOR_REVERSED",
+    "GPTQ_FACTOR_INVERSE_RECHOL", "GPTQ_FACTOR_REVERSED", "GPTQ_FACTOR_R_FORM",
 ]
 
 
@@ -146,9 +146,11 @@ class QuantResult:
 
 def quantize_layer(W: torch.Tensor, U: torch.Tensor, perm: torch.Tensor, dead: torch.Tensor, bits: int = 4,
                    group: int | None = None, stream=None, ws: torch.Tensor | None = None,
-                   asymmetric: bool = False) -> QuantResult:
+                   asymmetric: bool = False, r_form: bool = False) -> QuantResult:
     """The column-by-column error-compensation loop; W (out x in) bf16 or fp32 is only read.
-    asymmetric=True uses the min/max grid with a zero point (gptq_quantize_layer_ex)."""
+    asymmetric=True uses the min/max grid with a zero point (gptq_quantize_layer_ex). r_form=True: U is the
+    R form of the factor (prepare_chol with GPTQ_FACTOR_R_FORM) and the loop runs from it
+    (gptq_quantize_layer_r)."""
     _req_cuda(W, "W")
     ld = _ld(W, "W")
     out, d = W.shape
@@ -169,11 +171,12 @@ def quantize_layer(W: torch.Tensor, U: torch.Tensor, perm: torch.Tensor, dead: t
             ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
         zeros = torch.empty((out, n_groups), dtype=torch.int32, device=dev) if asymmetric else None
     grid = _lib.GPTQ_GRID_ASYMMETRIC if asymmetric else _lib.GPTQ_GRID_SYMMETRIC
-    st = lib.gptq_quantize_layer_ex(W.data_ptr(), _dtype_code(W), out, d, ld, U.data_ptr(), perm.data_ptr(),
-                                    dead.data_ptr(), int(bits), group, grid, codes.data_ptr(), scales.data_ptr(),
-                                    zeros.data_ptr() if zeros is not None else None, g_idx.data_ptr(),
-                                    row_loss.data_ptr(), ws.data_ptr(), ws.numel(), _stream(stream))
-    check(st, "gptq_quantize_layer_ex")
+    name = "gptq_quantize_layer_r" if r_form else "gptq_quantize_layer_ex"
+    st = getattr(lib, name)(W.data_ptr(), _dtype_code(W), out, d, ld, U.data_ptr(), perm.data_ptr(),
+                            dead.data_ptr(), int(bits), group, grid, codes.data_ptr(), scales.data_ptr(),
+                            zeros.data_ptr() if zeros is not None else None, g_idx.data_ptr(),
+                            row_loss.data_ptr(), ws.data_ptr(), ws.numel(), _stream(stream))
+    check(st, name)
     if asymmetric:
         codes = codes.view(torch.uint8)
     return QuantResult(codes, scales, g_idx, row_loss, perm, dead, U, zeros)
@@ -234,12 +237,14 @@ def dequant_matmul(X: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, 
 def gptq_quantize(W: torch.Tensor, X: torch.Tensor, bits: int = 4, group: int | None = None, damp: float = 0.01,
                   act_order: bool = False, flags: int = GPTQ_FACTOR_REVERSED, stream=None,
                   asymmetric: bool = False) -> QuantResult:
-    """The whole per-layer path: accumulate the Hessian over X, prepare U, quantize W. Every kernel and
-    every allocation is on `stream` (None = the current stream)."""
+    """The whole per-layer path: accumulate the Hessian over X, prepare U (or its R form, with
+    flags=GPTQ_FACTOR_R_FORM), quantize W. Every kernel and every allocation is on `stream` (None = the
+    current stream)."""
     state = HessianState(W.shape[1], device=W.device, stream=stream)
     hessian_accumulate(X, state, stream)
     U, perm, dead = prepare_chol(state.S, state.colsq, state.n_total, damp, act_order, flags, stream)
-    return quantize_layer(W, U, perm, dead, bits, group, stream, asymmetric=asymmetric)
+    return quantize_layer(W, U, perm, dead, bits, group, stream, asymmetric=asymmetric,
+                          r_form=(flags == GPTQ_FACTOR_R_FORM))
 
 
 @dataclass

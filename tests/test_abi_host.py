@@ -23,7 +23,7 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     lib = _lib.load()
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     for n in names:
         assert hasattr(lib, n), n
         assert n in _lib.SIGNATURES, n
@@ -94,7 +94,10 @@ def test_prepare_argument_errors():
     assert call(damp=-1.0) == bad
     assert call(damp=float("nan")) == bad
     assert call(damp=float("inf")) == bad
-    assert call(flags=2) == bad
+    assert call(flags=3) == bad
+    assert call(flags=4) == bad
+    # the R form needs in % 64 == 0
+    assert call(flags=_lib.GPTQ_FACTOR_R_FORM, d=100) == _lib.GPTQ_ERR_UNSUPPORTED
     assert call(ws=None) == _lib.GPTQ_ERR_WORKSPACE
     assert call(wsb=8) == _lib.GPTQ_ERR_WORKSPACE
 
@@ -142,6 +145,29 @@ def test_quantize_ex_argument_errors():
     assert call(group=48) == _lib.GPTQ_ERR_UNSUPPORTED
     assert call(ws=None) == _lib.GPTQ_ERR_WORKSPACE
     assert call(grid=_lib.GPTQ_GRID_SYMMETRIC, zeros=None, ws=None) == _lib.GPTQ_ERR_WORKSPACE
+
+
+def test_quantize_r_argument_errors():
+    """The R-form loop: the checks of gptq_quantize_layer_ex, plus in % 64 == 0 and groups that divide 128
+    (UNSUPPORTED otherwise)."""
+    lib = _lib.load()
+    bad = _lib.GPTQ_ERR_INVALID_ARG
+
+    def call(W=FAKE, dt=1, out=8, d=256, ld=256, R=FAKE, perm=FAKE, dead=FAKE, bits=4, group=0, grid=0,
+             codes=FAKE, scales=FAKE, zeros=None, ws=FAKE, wsb=1 << 30):
+        return lib.gptq_quantize_layer_r(W, dt, out, d, ld, R, perm, dead, bits, group, grid, codes, scales, zeros,
+                                         None, None, ws, wsb, None)
+
+    assert call(R=None) == bad
+    assert call(W=None) == bad
+    assert call(grid=2) == bad
+    assert call(grid=1) == bad  # asymmetric without zeros
+    assert call(bits=9) == bad
+    for g in (3, 48, 256, 1024):
+        assert call(group=g) == _lib.GPTQ_ERR_UNSUPPORTED
+    assert call(d=200, ld=200) == _lib.GPTQ_ERR_UNSUPPORTED
+    assert call(ws=None) == _lib.GPTQ_ERR_WORKSPACE
+    assert call(group=64, wsb=4) == _lib.GPTQ_ERR_WORKSPACE
 
 
 def test_pack_and_dequant_argument_errors():

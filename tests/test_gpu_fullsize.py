@@ -9,6 +9,8 @@ Full-size outputs are checked where the CPU oracle can compute them one by one:
   * end to end (all three): the oracle's fp64 Hessian over all rows, its U, and its loop on sampled rows,
     against the GPU's own full path; gates C-1..C-4 on those rows, C-4 beside the oracle's noise floor
     where a file under tests/golden/ holds one.
+The second quantize route (the R form of the factor, gptq_quantize_layer_r) is checked the same way on
+q_proj and down, stage by stage and end to end.
 """
 import json
 import os
@@ -112,6 +114,12 @@ def test_fullsize_prepare_and_quantize_given_oracle_s(name, rows, flags):
     r = G.quantize_layer(to_device(W, cfg.dtype), dev64(U_ref), dev64(perm.astype(np.int32)),
                          dev64(dead.astype(np.uint8)), cfg.bits, cfg.group)
     torch.cuda.synchronize()
+    _check_sampled_rows(cfg, W, r, perm, dead, U_ref)
+
+
+def _check_sampled_rows(cfg, W, r, perm, dead, U_ref):
+    """Codes (C-1, C-3 where they differ), g_idx, scales and the row loss of sampled rows against the
+    oracle loop run with U_ref."""
     rows_s = np.random.default_rng(3).choice(cfg.out, 12, replace=False)
     rows_s = np.unique(np.concatenate([rows_s, [0, cfg.out - 1]]))
     W64 = O.to_f64(W[rows_s], cfg.dtype)
@@ -127,6 +135,33 @@ def test_fullsize_prepare_and_quantize_given_oracle_s(name, rows, flags):
     assert np.array_equal(r.g_idx.cpu().numpy(), g_idx)
     np.testing.assert_allclose(r.scales.cpu().numpy()[rows_s], scales.astype(np.float32), rtol=2e-7)
     np.testing.assert_allclose(r.row_loss.cpu().numpy()[rows_s], loss, rtol=1e-8)
+
+
+@pytest.mark.parametrize("name,rows", [("q_proj", 8192), ("down", 16384)])
+def test_fullsize_r_form_prepare_and_quantize_given_oracle_s(name, rows):
+    """The R route at full size, stage by stage: prepare's R form (R = U^-1 in the upper triangle, U's
+    128 x 128 diagonal blocks reversed below it) against the oracle's, then gptq_quantize_layer_r given
+    the oracle's R form, on sampled rows against the oracle loop run with the oracle's U."""
+    cfg = syn.config_by_name(name)
+    print(f"[fullsize] R route prepare+quantize {name} rows={rows}", flush=True)
+    S, colsq, n, H_p, perm, dead, U_ref = _oracle_u_from_rows(cfg, rows, cfg.act_order)
+    M_ref = O.r_form(H_p)
+    M, p, dd = G.prepare_chol(dev64(S), dev64(colsq), n, cfg.damp, cfg.act_order, G.GPTQ_FACTOR_R_FORM)
+    assert np.array_equal(p.cpu().numpy(), perm)
+    assert np.array_equal(dd.cpu().numpy().astype(bool), dead)
+    Mg = M.cpu().numpy()
+    tol = 1e-10 if cfg.d_in <= 4096 else 1e-9
+    up, lo = np.triu(M_ref), np.tril(M_ref, -1)
+    rel_up = np.linalg.norm(np.triu(Mg) - up) / np.linalg.norm(up)
+    rel_lo = np.linalg.norm(np.tril(Mg, -1) - lo) / np.linalg.norm(lo)
+    print(f"[fullsize] {name}: R part rel {rel_up:.2e}, U blocks rel {rel_lo:.2e}", flush=True)
+    assert rel_up <= tol and rel_lo <= tol
+    del M
+    W = syn.gen_w(cfg)
+    r = G.quantize_layer(to_device(W, cfg.dtype), dev64(M_ref), dev64(perm.astype(np.int32)),
+                         dev64(dead.astype(np.uint8)), cfg.bits, cfg.group, r_form=True)
+    torch.cuda.synchronize()
+    _check_sampled_rows(cfg, W, r, perm, dead, U_ref)
 
 
 def _oracle_s64(cfg):
@@ -155,19 +190,22 @@ def _floor(name):
 
 
 @pytest.mark.timeout(1200)
-@pytest.mark.parametrize("name", ["q_proj", "up_gate", "down"])
-def test_fullsize_end_to_end_sampled_rows(name):
+@pytest.mark.parametrize("name,flags", [("q_proj", G.GPTQ_FACTOR_REVERSED), ("q_proj", G.GPTQ_FACTOR_R_FORM),
+                                        ("up_gate", G.GPTQ_FACTOR_REVERSED), ("down", G.GPTQ_FACTOR_REVERSED),
+                                        ("down", G.GPTQ_FACTOR_R_FORM)],
+                         ids=["q_proj", "q_proj-rform", "up_gate", "down", "down-rform"])
+def test_fullsize_end_to_end_sampled_rows(name, flags):
     """The GPU's whole path at full size against the oracle's whole path (fp64 Hessian over all rows)
     on sampled rows: C-1 code agreement, C-3 forced replay, C-4 dequantized Q, C-2 output error, and for
     act_order + groups (down) perm and g_idx identical. Where a noise-floor file exists (the oracle's own
     drift under an fp32-accumulated Hessian, tests/golden/make_noise_floor.py), its rows are the ones
     checked and its floor is printed beside C-4."""
     cfg = syn.config_by_name(name)
-    print(f"[fullsize] end-to-end {name}", flush=True)
+    print(f"[fullsize] end-to-end {name} flags={flags}", flush=True)
     X = _x(name)
     W = syn.gen_w(cfg)
     r = G.gptq_quantize(to_device(W, cfg.dtype), to_device(X, cfg.dtype), cfg.bits, cfg.group, cfg.damp,
-                        cfg.act_order, G.GPTQ_FACTOR_REVERSED)
+                        cfg.act_order, flags)
     torch.cuda.synchronize()
     gperm = r.perm.cpu().numpy()
     gg = r.g_idx.cpu().numpy()
