@@ -284,18 +284,31 @@ __global__ __launch_bounds__(256) void k_panel(double* __restrict__ Wq, int out,
     } else if (t_valid) {
       // groups inside the panel: a group's grid is set from the current values of all its columns, so the
       // whole T_P U_PP is added first, by the lanes that own the columns (T_j broadcast from lane j % 16 of
-      // the row, U_PP's row j read from LDS as in the loop below; no step depends on another)
+      // the row, U_PP's row j read from LDS as in the loop below). No product depends on another, so the
+      // rows go four at a time with the next four rows' LDS reads in flight (a scheduling barrier keeps
+      // the compiler from sinking them next to their uses, which left two or three reads in flight)
+      double ub[2][4][8];
+      auto load4 = [&](auto gc, double(&u)[4][8]) {
+        constexpr int g = decltype(gc)::value, jm = g / 4;
 #pragma unroll
-      for (int jm = 0; jm < 8; ++jm) {
-        static_for<0, 16>([&](auto jlc) {
-          constexpr int jl = decltype(jlc)::value;
-          const int j = jm * 16 + jl;
-          const double tj = bcast16<jl>(t[jm]);
+        for (int q = 0; q < 4; ++q)
 #pragma unroll
           for (int m = 0; m < 8; ++m)
-            if (m >= jm) w[m] = fma(tj, Us[urow(j) + c + 16 * (m - jm)], w[m]);
+            if (m >= jm) u[q][m] = Us[urow(4 * g + q) + c + 16 * (m - jm)];
+      };
+      load4(std::integral_constant<int, 0>{}, ub[0]);
+      static_for<0, PW / 4>([&](auto gc) {
+        constexpr int g = decltype(gc)::value, jm = g / 4;
+        if constexpr (g + 1 < PW / 4) load4(std::integral_constant<int, g + 1>{}, ub[(g + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        static_for<0, 4>([&](auto qc) {
+          constexpr int q = decltype(qc)::value;
+          const double tj = bcast16<(4 * g + q) % 16>(t[jm]);
+#pragma unroll
+          for (int m = 0; m < 8; ++m)
+            if (m >= jm) w[m] = fma(tj, ub[g & 1][q][m], w[m]);
         });
-      }
+      });
     }
   }
 

@@ -84,6 +84,10 @@ RQ_CASES = [
     (R1344, 4, 0, True, False),
     (R1344, 3, 128, True, False),
     (R1344, 4, 32, False, True),
+    (MID, 4, 0, True, True),      # one asymmetric grid per row: T folded into the steps, D from the codes
+    (R1344, 3, 0, False, True),
+    (MID, 8, 0, False, False),
+    (R1344, 2, 16, True, False),
 ]
 
 
@@ -151,6 +155,7 @@ E2E_R_CASES = [
     (MID, 4, 128, False, False),
     (R1344, 3, 128, True, False),
     (MID, 4, 128, False, True),
+    (MID, 4, 0, True, True),
 ]
 
 
