@@ -194,7 +194,10 @@ def main():
     U = torch.empty((d, d), dtype=torch.float64, device="cuda")
     perm = torch.empty(d, dtype=torch.int32, device="cuda")
     dead = torch.empty(d, dtype=torch.uint8, device="cuda")
-    qws = torch.empty(G.load().gptq_quantize_workspace_bytes(out, d), dtype=torch.uint8, device="cuda")
+    lib = G.load()
+    qws_bytes = (lib.gptq_quantize_r_workspace_bytes if flags == G.GPTQ_FACTOR_R_FORM
+                 else lib.gptq_quantize_workspace_bytes)(out, d)
+    qws = torch.empty(qws_bytes, dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
 
     ev = {k: [] for k in ("zero", "hessian", "prepare", "quantize")}

@@ -199,10 +199,14 @@ int gptq_quantize_layer_ex(const void* W, int w_dtype, int64_t out, int64_t in, 
  *             order), or the same layout built by the caller.
  *  Requires in % 64 == 0 and group == 0 or 128 % group == 0 (a wider group takes its scale from columns
  *  beyond the current panel, whose updated values the R form does not give): UNSUPPORTED otherwise.
- *  Everything else (arguments, grids, outputs, layouts, workspace, errors) is as for gptq_quantize_layer_ex;
- *  the results agree with it up to rounding (codes may differ only where a weight lies within rounding of
- *  a grid midpoint).
+ *  ws         at least gptq_quantize_r_workspace_bytes(out, in) bytes: gptq_quantize_workspace_bytes(out,
+ *             in) plus out x in doubles for T (rounded up to 256 bytes). It returns 0 for out/in outside
+ *             the accepted range.
+ *  Everything else (arguments, grids, outputs, layouts, errors) is as for gptq_quantize_layer_ex; the results
+ *  agree with it up to rounding (codes may differ only where a weight lies within rounding of a grid
+ *  midpoint).
  * ------------------------------------------------------------------------------------------------- */
+size_t gptq_quantize_r_workspace_bytes(int64_t out, int64_t in);
 int gptq_quantize_layer_r(const void* W, int w_dtype, int64_t out, int64_t in, int64_t ld_w,
                           const double* R, const int32_t* perm, const uint8_t* dead,
                           int bits, int group, int grid,

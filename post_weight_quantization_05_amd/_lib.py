@@ -38,6 +38,7 @@ SIGNATURES = {
     "gptq_prepare_chol": (ctypes.c_int, [_vp, _vp, _c_int64, _c_int64, ctypes.c_double, ctypes.c_int,
                                          ctypes.c_uint, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
     "gptq_quantize_workspace_bytes": (ctypes.c_size_t, [_c_int64, _c_int64]),
+    "gptq_quantize_r_workspace_bytes": (ctypes.c_size_t, [_c_int64, _c_int64]),
     "gptq_quantize_layer": (ctypes.c_int, [_vp, ctypes.c_int, _c_int64, _c_int64, _c_int64, _vp, _vp, _vp,
                                            ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
                                            _vp]),

@@ -81,7 +81,12 @@ int gptq_prepare_chol(const double* S, const double* colsq, int64_t n_total, int
 
 size_t gptq_quantize_workspace_bytes(int64_t out, int64_t in) {
   if (out < 1 || in < 1 || in > MAX_IN || out > MAX_OUT) return 0;
-  return quantize_ws_bytes(out, in);
+  return quantize_ws_bytes(out, in, false);
+}
+
+size_t gptq_quantize_r_workspace_bytes(int64_t out, int64_t in) {
+  if (out < 1 || in < 1 || in > MAX_IN || out > MAX_OUT) return 0;
+  return quantize_ws_bytes(out, in, true);
 }
 
 int gptq_quantize_layer_ex(const void* W, int w_dtype, int64_t out, int64_t in, int64_t ld_w, const double* U,
@@ -95,7 +100,7 @@ int gptq_quantize_layer_ex(const void* W, int w_dtype, int64_t out, int64_t in, 
     return GPTQ_ERR_INVALID_ARG;
   if (bits < 2 || bits > 8 || group < 0) return GPTQ_ERR_INVALID_ARG;
   if (group != 0 && !(128 % group == 0 || group % 128 == 0)) return GPTQ_ERR_UNSUPPORTED;
-  if (!ws || ws_bytes < quantize_ws_bytes(out, in)) return GPTQ_ERR_WORKSPACE;
+  if (!ws || ws_bytes < quantize_ws_bytes(out, in, false)) return GPTQ_ERR_WORKSPACE;
   unsigned dev_status = 0;
   const hipError_t e = quantize_launch(W, w_dtype, out, in, ld_w, U, perm, dead, bits, group, grid, codes, scales,
                                        zeros, g_idx, row_loss, ws, reinterpret_cast<hipStream_t>(stream), &dev_status);
@@ -114,7 +119,7 @@ int gptq_quantize_layer_r(const void* W, int w_dtype, int64_t out, int64_t in, i
     return GPTQ_ERR_INVALID_ARG;
   if (bits < 2 || bits > 8 || group < 0) return GPTQ_ERR_INVALID_ARG;
   if (in % 64 != 0 || (group != 0 && 128 % group != 0)) return GPTQ_ERR_UNSUPPORTED;
-  if (!ws || ws_bytes < quantize_ws_bytes(out, in)) return GPTQ_ERR_WORKSPACE;
+  if (!ws || ws_bytes < quantize_ws_bytes(out, in, true)) return GPTQ_ERR_WORKSPACE;
   unsigned dev_status = 0;
   const hipError_t e = quantize_launch(W, w_dtype, out, in, ld_w, R, perm, dead, bits, group, grid, codes, scales,
                                        zeros, g_idx, row_loss, ws, reinterpret_cast<hipStream_t>(stream), &dev_status,

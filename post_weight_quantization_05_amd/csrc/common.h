@@ -53,7 +53,7 @@ hipError_t prepare_launch(const double* S, const double* colsq, int64_t n_total,
                           hipStream_t stream, unsigned* host_status);
 
 // Quantize (quant.hip)
-size_t quantize_ws_bytes(int64_t out, int64_t in);
+size_t quantize_ws_bytes(int64_t out, int64_t in, bool rform);
 hipError_t quantize_launch(const void* W, int w_dtype, int64_t out, int64_t in, int64_t ld_w, const double* U,
                            const int32_t* perm, const uint8_t* dead, int bits, int group, int grid, int8_t* codes,
                            float* scales, int32_t* zeros, int32_t* g_idx, double* row_loss, void* ws,

@@ -480,14 +480,14 @@ __global__ void k_gidx(const int32_t* __restrict__ perm, int in, int group, int3
 
 }  // namespace
 
-size_t quantize_ws_bytes(int64_t out, int64_t in) {
+size_t quantize_ws_bytes(int64_t out, int64_t in, bool rform) {
   size_t b = 0;
   b += align_up((size_t)out * in * sizeof(double), 256);  // working copy
   b += align_up((size_t)out * OB * sizeof(double), 256);  // errors (or, R form, D = W0 - Q) of one outer block
-  b += align_up((size_t)out * in * sizeof(double), 256);  // R form: T, the accumulated D R
   b += align_up((size_t)out * sizeof(double), 256);       // current fp64 scale per row
   b += align_up((size_t)out * sizeof(double), 256);       // current zero point per row (asymmetric grid)
   b += 256;                                                // status word
+  if (rform) b += align_up((size_t)out * in * sizeof(double), 256);  // T, the accumulated D R
   return b;
 }
 
@@ -550,13 +550,13 @@ hipError_t quantize_launch(const void* W, int w_dtype, int64_t out64, int64_t in
   w += align_up((size_t)out * in * sizeof(double), 256);
   double* Err = reinterpret_cast<double*>(w);
   w += align_up((size_t)out * OB * sizeof(double), 256);
-  double* Tacc = reinterpret_cast<double*>(w);  // R form only
-  w += align_up((size_t)out * in * sizeof(double), 256);
   double* scale_row = reinterpret_cast<double*>(w);
   w += align_up((size_t)out * sizeof(double), 256);
   double* zero_row = reinterpret_cast<double*>(w);
   w += align_up((size_t)out * sizeof(double), 256);
   unsigned* status = reinterpret_cast<unsigned*>(w);
+  w += 256;
+  double* Tacc = rform ? reinterpret_cast<double*>(w) : nullptr;  // R form only (see quantize_ws_bytes)
   // largest code: qmax of the symmetric grid, or the top level 2^b - 1 of the asymmetric one
   const double qmax = asym ? (double)((1 << bits) - 1) : (double)((1 << (bits - 1)) - 1);
   const int n_groups = group ? (int)ceil_div(in, group) : 1;

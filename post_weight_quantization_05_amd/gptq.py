@@ -161,7 +161,7 @@ def quantize_layer(W: torch.Tensor, U: torch.Tensor, perm: torch.Tensor, dead: t
     n_groups = -(-d // group) if group else 1
     dev = W.device
     lib = _lib.load()
-    need = lib.gptq_quantize_workspace_bytes(out, d)
+    need = (lib.gptq_quantize_r_workspace_bytes if r_form else lib.gptq_quantize_workspace_bytes)(out, d)
     with _on(stream):
         codes = torch.empty((out, d), dtype=torch.int8, device=dev)
         scales = torch.empty((out, n_groups), dtype=torch.float32, device=dev)

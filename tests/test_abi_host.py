@@ -23,7 +23,7 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     lib = _lib.load()
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 15, names
     for n in names:
         assert hasattr(lib, n), n
         assert n in _lib.SIGNATURES, n
@@ -51,6 +51,9 @@ def test_workspace_queries():
     assert lib.gptq_quantize_workspace_bytes(4096, 4096) >= 4096 * 4096 * 8 + 4096 * 128 * 8
     assert lib.gptq_prepare_workspace_bytes(0) == 0
     assert lib.gptq_quantize_workspace_bytes(5, 0) == 0
+    # the R route adds T (out x in doubles) to the same layout
+    assert lib.gptq_quantize_r_workspace_bytes(4096, 4096) == lib.gptq_quantize_workspace_bytes(4096, 4096) + 4096 * 4096 * 8
+    assert lib.gptq_quantize_r_workspace_bytes(5, 0) == 0
 
 
 FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
@@ -168,6 +171,8 @@ def test_quantize_r_argument_errors():
     assert call(d=200, ld=200) == _lib.GPTQ_ERR_UNSUPPORTED
     assert call(ws=None) == _lib.GPTQ_ERR_WORKSPACE
     assert call(group=64, wsb=4) == _lib.GPTQ_ERR_WORKSPACE
+    # the route through U's workspace lacks T
+    assert call(wsb=lib.gptq_quantize_workspace_bytes(8, 256)) == _lib.GPTQ_ERR_WORKSPACE
 
 
 def test_pack_and_dequant_argument_errors():
