@@ -68,6 +68,14 @@ __device__ __forceinline__ double bcast16(double v) {
   return __builtin_amdgcn_mov_dpp(v, 0x150 + K, 0xF, 0xF, false);
 }
 
+// the value of v in lane addr / 4 (ds_bpermute on both halves)
+__device__ __forceinline__ double bpermute_f64(int addr, double v) {
+  const long long x = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_ds_bpermute(addr, (int)x);
+  const int hi = __builtin_amdgcn_ds_bpermute(addr, (int)(x >> 32));
+  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+
 // value of lane (i - R) mod 16 of this lane's 16-lane row (DPP row_ror; 64-bit DPP takes only row_newbcast,
 // so the two halves move separately)
 template <int R>
@@ -283,31 +291,20 @@ __global__ __launch_bounds__(256) void k_panel(double* __restrict__ Wq, int out,
       }
     } else if (t_valid) {
       // groups inside the panel: a group's grid is set from the current values of all its columns, so the
-      // whole T_P U_PP is added first, by the lanes that own the columns (T_j broadcast from lane j % 16 of
-      // the row, U_PP's row j read from LDS as in the loop below). No product depends on another, so the
-      // rows go four at a time with the next four rows' LDS reads in flight (a scheduling barrier keeps
-      // the compiler from sinking them next to their uses, which left two or three reads in flight)
-      double ub[2][4][8];
-      auto load4 = [&](auto gc, double(&u)[4][8]) {
-        constexpr int g = decltype(gc)::value, jm = g / 4;
+      // whole T_P U_PP is added first, on the matrix cores with w as the accumulator.
+      // v_mfma_f64_4x4x4f64 forms four 4 x 4 x 4 block products at once: lane l supplies A[l % 16][l / 16]
+      // and B[l / 16][l % 16], block g takes A's rows 4g .. 4g + 3 and B's columns 4g .. 4g + 3, and its
+      // entry (i, j) lands in lane 16 i + 4 g + j. With the wave's four rows of T_P as the A rows of every
+      // block and 16 columns of U_PP as B, lane 16 r + c receives row r, column c of the product, which is
+      // the layout in which the lanes hold w. U_PP's rows come from LDS; the A values come from the lanes
+      // that hold them (T_P[r][k] is in lane 16 r + k % 16, register k / 16), through ds_bpermute.
+      const int lane = tid & 63, lr = lane & 15, lk = lane >> 4;
+      static_for<0, PW / 4>([&](auto kc) {
+        constexpr int k0 = 4 * decltype(kc)::value, mb = k0 / 16;
+        const double a = bpermute_f64(4 * (16 * (lane & 3) + (k0 & 15) + lk), t[mb]);
+        const int rb = urow(k0 + lk) + lr - 16 * mb;  // row k0 + lk of U_PP, stored from column 16 mb on
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-          for (int m = 0; m < 8; ++m)
-            if (m >= jm) u[q][m] = Us[urow(4 * g + q) + c + 16 * (m - jm)];
-      };
-      load4(std::integral_constant<int, 0>{}, ub[0]);
-      static_for<0, PW / 4>([&](auto gc) {
-        constexpr int g = decltype(gc)::value, jm = g / 4;
-        if constexpr (g + 1 < PW / 4) load4(std::integral_constant<int, g + 1>{}, ub[(g + 1) & 1]);
-        __builtin_amdgcn_sched_barrier(0);
-        static_for<0, 4>([&](auto qc) {
-          constexpr int q = decltype(qc)::value;
-          const double tj = bcast16<(4 * g + q) % 16>(t[jm]);
-#pragma unroll
-          for (int m = 0; m < 8; ++m)
-            if (m >= jm) w[m] = fma(tj, ub[g & 1][q][m], w[m]);
-        });
+        for (int m = mb; m < 8; ++m) w[m] = __builtin_amdgcn_mfma_f64_4x4x4f64(a, Us[rb + 16 * m], w[m], 0, 0, 0);
       });
     }
   }
