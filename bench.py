@@ -6,7 +6,8 @@ A step is one pass of the whole path on the q_proj workload (W 4096 x 4096 bf16,
 accumulate call writes S, so no zeroing pass is needed), prepare the factor, run the compensation loop. By
 default the factor is in its R form (R = U^-1, the Cholesky factor of the reversed H, with U's 128 x 128
 diagonal blocks) and the loop runs from it (gptq_quantize_layer_r); --factor reversed times the route through
-U itself. Inputs are resident in HBM before timing starts.
+U itself; with the R route the line also carries the same layer timed through U (`route_through_u`, after
+the R route's steps; --single-route skips it). Inputs are resident in HBM before timing starts.
 Prints ONE JSON line (see the fields below). `--gpus N` with N > 1 exits: this path runs on one GPU.
 """
 from __future__ import annotations
@@ -39,6 +40,9 @@ def parse():
                          "runs from it (inputs a multiple of 64, group 0 or dividing 128; other workloads take "
                          "reversed); reversed: U by one Cholesky and one triangular inverse; rechol: U as the "
                          "Cholesky factor of the explicit inverse")
+    ap.add_argument("--single-route", action="store_true",
+                    help="skip the second timing of the layer through U that the R route's line carries "
+                         "(route_through_u), e.g. for kernel traces of one route")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-rows", type=int, default=65536)
     ap.add_argument("--cpu-loop-rows", type=int, default=64)
@@ -200,9 +204,7 @@ def main():
     qws = torch.empty(qws_bytes, dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
 
-    ev = {k: [] for k in ("zero", "hessian", "prepare", "quantize")}
-
-    def step(record):
+    def step(record, fl, ev):
         marks = [torch.cuda.Event(enable_timing=True) for _ in range(5)] if record else None
         if record:
             marks[0].record(stream)
@@ -212,16 +214,34 @@ def main():
         G.hessian_accumulate(Xd, st)
         if record:
             marks[2].record(stream)
-        G.prepare_chol(st.S, st.colsq, st.n_total, cfg.damp, cfg.act_order, flags, out=(U, perm, dead))
+        G.prepare_chol(st.S, st.colsq, st.n_total, cfg.damp, cfg.act_order, fl, out=(U, perm, dead))
         if record:
             marks[3].record(stream)
-        res = G.quantize_layer(Wd, U, perm, dead, cfg.bits, cfg.group, ws=qws,
-                               r_form=(flags == G.GPTQ_FACTOR_R_FORM))
+        res = G.quantize_layer(Wd, U, perm, dead, cfg.bits, cfg.group, ws=qws, r_form=(fl == G.GPTQ_FACTOR_R_FORM))
         if record:
             marks[4].record(stream)
             for i, k in enumerate(("zero", "hessian", "prepare", "quantize")):
                 ev[k].append((marks[i], marks[i + 1]))
         return res
+
+    def run_route(fl):
+        """W untimed steps, then K steps between two events on the stream; ms per step, mean stage times
+        (HIP events) and the host wall time of the timed steps."""
+        ev = {k: [] for k in ("zero", "hessian", "prepare", "quantize")}
+        for _ in range(args.warmup):
+            step(False, fl, ev)
+        torch.cuda.synchronize()
+        t_start = torch.cuda.Event(enable_timing=True)
+        t_end = torch.cuda.Event(enable_timing=True)
+        t_start.record(stream)
+        wall0 = time.perf_counter()
+        for _ in range(args.steps):
+            step(True, fl, ev)
+        t_end.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        stage_ms = {k: float(np.mean([a.elapsed_time(b) for a, b in v])) for k, v in ev.items()}
+        return t_start.elapsed_time(t_end) / args.steps, stage_ms, wall
 
     def streamed_hessian_ms(reps=3):
         """The same accumulation as 2048-row calls (the workload's segments), on the same stream: the
@@ -249,21 +269,7 @@ def main():
         print(json.dumps({"mode": "hessian", "config": cfg.name, "launches": max(1, args.steps)}), flush=True)
         return
 
-    for _ in range(args.warmup):
-        step(False)
-    torch.cuda.synchronize()
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    t_start.record(stream)
-    wall0 = time.perf_counter()
-    for _ in range(args.steps):
-        res = step(True)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    total_ms = t_start.elapsed_time(t_end)
-    ms_per_step = total_ms / args.steps
-    stage_ms = {k: float(np.mean([a.elapsed_time(b) for a, b in v])) for k, v in ev.items()}
+    ms_per_step, stage_ms, wall = run_route(flags)
 
     # algorithmic work (lower triangle of X^T X, the two-step factor, the loop's multiply-adds)
     n = cfg.n
@@ -325,6 +331,15 @@ def main():
         "wall_s_timed": round(wall, 3),
         "gen_s": round(gen_s, 2),
     }
+    if flags == G.GPTQ_FACTOR_R_FORM and not args.single_route:
+        # the same layer through U itself (one Cholesky and one triangular inverse, the loop subtracting
+        # Err U), timed the same way after the R route, for comparison
+        u_ms, u_stages, _ = run_route(G.GPTQ_FACTOR_REVERSED)
+        u_bound = bound_ms + (2.0 / 3.0 - 1.0 / 3.0) * d ** 3 / (PEAK_FP64_TFLOPS * 1e12) * 1e3
+        line["route_through_u"] = {"factor_route": "reversed", "ms_per_step": round(u_ms, 4),
+                                   "stages_ms": {k: round(v, 4) for k, v in u_stages.items()},
+                                   "combined_bound_ms": round(u_bound, 4),
+                                   "frac_of_combined_bound": round(u_bound / u_ms, 4)}
     if cfg.n >= 2048 and not args.no_streamed_hessian:
         s_ms, calls = streamed_hessian_ms()
         line["hessian_streamed"] = {"calls": calls, "rows_per_call": 2048, "ms": round(s_ms, 4),
