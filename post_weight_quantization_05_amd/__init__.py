@@ -8,6 +8,6 @@ from ._lib import (  # noqa: F401
     status_string,
 )
 from .gptq import (  # noqa: F401
-    HessianState, QuantizedLayer, QuantResult, apply_layerwise, dequant_matmul, gptq_quantize, hessian_accumulate,
-    pack_codes, prepare_chol, quantize_layer,
+    HessianState, QuantizedLayer, QuantResult, apply_layerwise, dequant_matmul, factor_route, gptq_quantize,
+    hessian_accumulate, pack_codes, prepare_chol, quantize_layer,
 )

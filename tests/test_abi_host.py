@@ -210,3 +210,17 @@ def test_pack_and_dequant_argument_errors():
 def test_missing_library_fails_loudly(tmp_path):
     with pytest.raises(RuntimeError, match="missing"):
         _lib.load(str(tmp_path / "nope.so"))
+
+
+def test_factor_route_choice():
+    """gptq_quantize's route when flags is None: the R form where the library takes it and it measured faster
+    (one grid per row, or in >= 8192), else the route through U."""
+    import post_weight_quantization_05_amd as G
+    assert G.factor_route(4096, 0) == G.GPTQ_FACTOR_R_FORM
+    assert G.factor_route(4096, None) == G.GPTQ_FACTOR_R_FORM
+    assert G.factor_route(4096, 128) == G.GPTQ_FACTOR_REVERSED
+    assert G.factor_route(11008, 128) == G.GPTQ_FACTOR_R_FORM
+    assert G.factor_route(11008, 32) == G.GPTQ_FACTOR_R_FORM
+    assert G.factor_route(11008, 256) == G.GPTQ_FACTOR_REVERSED  # wider than a panel: the R form does not take it
+    assert G.factor_route(100, 0) == G.GPTQ_FACTOR_REVERSED      # not a multiple of 64
+    assert G.factor_route(8200, 0) == G.GPTQ_FACTOR_REVERSED
