@@ -22,6 +22,12 @@
 //              U[block, ob1:] (K = OB). The products are the ones of the column-by-column loop; only
 //              their grouping (and so the floating-point summation order) changes, and the fp64 W is
 //              read and written a few times instead of once per panel.
+// The R route (gptq_quantize_layer_r) runs the same schedule from R = U^-1 and U's 128 x 128 diagonal
+// blocks: the loop gives W0 - Q = Err U, so Err = D R with D = W0 - Q, and a panel P starts from
+// W0_P + T_P U_PP with T = sum over earlier panels B of D_B R_BP. The lazy updates accumulate T += D R
+// (the same products, into T instead of W), the working copy keeps W0, and k_panel<.., RF = true> writes
+// D in place of Err and starts from W0 + T U_PP: with one grid per row T enters the loop's steps (step j
+// propagates e_j - T_j), with groups inside the panel T_P U_PP is formed first on the matrix cores.
 // Grids. Symmetric ([guide] "The code, line by line"): codes -qmax..qmax, qmax = 2^(b-1) - 1, scale =
 // max(max|w|, 1e-12) / qmax, code = clip(round(w / scale)), value = code * scale. Asymmetric ([handbook]
 // quantize_weight, dequantize_weight, gptq_quantize_row; the paper's default per the guide's
