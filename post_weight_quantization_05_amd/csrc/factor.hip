@@ -22,6 +22,8 @@
 //  trailing SYRK updates and H^-1 = L^-T L^-1 use the fp64 MFMA GEMM core (dgemm.hip).
 // Routes (flags): INVERSE_RECHOL = potrf with L^-1, lauum, potrf, transpose (the guide's order);
 // REVERSED = potrf with L^-1 of J H J, then U = J L^-1 J (same unique U, half the work).
+// R_FORM = potrf of J H J without L^-1, then R = J L J (= U^-1) and U's 128 x 128 diagonal blocks, the
+// inverses of R's, from the steps' 64 x 64 diagonal inverses (k_rform_diag), for the R route of the loop.
 #include <algorithm>
 #include <type_traits>
 
