@@ -237,8 +237,13 @@ static_assert(NBO == 256, "an outer block's panel is the K of its successor's fi
 #ifndef GPTQ_FACTOR_DEFER
 #define GPTQ_FACTOR_DEFER 160
 #endif
+// The R form's steps carry no L^-1: 640 deferred tiles per step up to in = 6144, 320 above (in = 4096:
+// 2.49 ms with 640, 2.52 with 320; in = 11008: 18.3 ms with 320, 18.7 with 640, 18.6 with 160).
 #ifndef GPTQ_FACTOR_DEFER_RFORM
 #define GPTQ_FACTOR_DEFER_RFORM 640
+#endif
+#ifndef GPTQ_FACTOR_DEFER_RFORM_LARGE
+#define GPTQ_FACTOR_DEFER_RFORM_LARGE 320
 #endif
 #ifndef GPTQ_FACTOR_DEFER_FILL
 #define GPTQ_FACTOR_DEFER_FILL 640
@@ -511,7 +516,8 @@ hipError_t prepare_launch(const double* S, const double* colsq, int64_t n_total,
 
   if (flags == GPTQ_FACTOR_R_FORM) {
     // R = J L J (L placed in A), then the inverses of its 128 x 128 diagonal blocks in their lower parts
-    GPTQ_TRY(potrf_lower(A, d, Dinv, Lst, status, true, nullptr, G, stream, GPTQ_FACTOR_DEFER_RFORM));
+    GPTQ_TRY(potrf_lower(A, d, Dinv, Lst, status, true, nullptr, G, stream,
+                         d <= FILL_MAX ? GPTQ_FACTOR_DEFER_RFORM : GPTQ_FACTOR_DEFER_RFORM_LARGE));
     hipLaunchKernelGGL(k_reverse_to_upper, dim3((unsigned)ceil_div(d, 256), (unsigned)std::min(d, 4096)), dim3(256),
                        0, stream, A, d, U);
     GPTQ_TRY(hipGetLastError());
