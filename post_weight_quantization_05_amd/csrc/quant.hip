@@ -208,8 +208,9 @@ __global__ __launch_bounds__(256) void k_rowprep(const T* __restrict__ W, int64_
 // 128 (boundaries inside the panel at j % group == 0).
 // RF: the factor comes in the R form (GPTQ_FACTOR_R_FORM): the block's U is read from the reversed lower part of
 // R's diagonal block, 1 / U[j][j] is R[j][j], Wq holds the starting weights W0 and T the accumulated D R of
-// the earlier panels; the workgroup first forms its rows' W0_P + T_P U_PP (on the matrix cores, 16 rows x
-// 128 x 128), and stores D = W0 - Q instead of the errors for the products that follow.
+// the earlier panels; the rows start from W0_P + T_P U_PP (with INPANEL formed first on the matrix cores,
+// otherwise folded into the steps), and D = W0 - Q is stored instead of the errors for the products that
+// follow.
 template <bool INPANEL, bool ASYM, bool RF>
 __global__ __launch_bounds__(256) void k_panel(double* __restrict__ Wq, int out, int in, int b0,
                                                const double* __restrict__ U, const int32_t* __restrict__ perm,
