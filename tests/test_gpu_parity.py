@@ -436,19 +436,21 @@ def test_quantize_reports_nonfinite_weights():
     assert torch.equal(r.row_loss, clean.row_loss)
 
 
-def test_whole_path_on_a_side_stream():
+@pytest.mark.parametrize("flags", [None, G.GPTQ_FACTOR_R_FORM], ids=["auto", "rform"])
+def test_whole_path_on_a_side_stream(flags):
     """Every kernel and every temporary of gptq_quantize lives on the stream it is given: the result on
-    a side stream, with the default stream busy meanwhile, is bitwise the default-stream result."""
+    a side stream, with the default stream busy meanwhile, is bitwise the default-stream result (the
+    automatic route, which takes the route through U here, and the R route with its T buffer)."""
     cfg = HESS_CASES[2]
     W, X, W64, X64 = layer_inputs(cfg)
     Wd, Xd = to_device(W, cfg.dtype), to_device(X, cfg.dtype)
-    a = G.gptq_quantize(Wd, Xd, 4, 128, 0.01, True)
+    a = G.gptq_quantize(Wd, Xd, 4, 128, 0.01, True, flags)
     torch.cuda.synchronize()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     busy = torch.randn(3072, 3072, device="cuda")
     for _ in range(3):
-        b = G.gptq_quantize(Wd, Xd, 4, 128, 0.01, True, stream=s)
+        b = G.gptq_quantize(Wd, Xd, 4, 128, 0.01, True, flags, stream=s)
         for _ in range(4):
             busy = torch.tanh(busy @ busy * 1e-3)  # default-stream work allocating and freeing memory
     torch.cuda.current_stream().wait_stream(s)
