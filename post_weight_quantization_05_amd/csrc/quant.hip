@@ -211,7 +211,12 @@ __global__ __launch_bounds__(256) void k_rowprep(const T* __restrict__ W, int64_
 // the earlier panels; the rows start from W0_P + T_P U_PP (with INPANEL formed first on the matrix cores,
 // otherwise folded into the steps), and D = W0 - Q is stored instead of the errors for the products that
 // follow.
-template <bool INPANEL, bool ASYM, bool RF>
+// GC: the group size when it is known at compile time (INPANEL with group 64 or 128); the column steps are
+// then expanded at compile time and only the steps that open a group carry the group's grid code, so the
+// kernel keeps the registers of the one-grid-per-row form (74 against 151). GC = 0: the group size comes
+// from `group` (one grid per row, or in-panel groups of 1 .. 32, whose steps stay a loop over the 16-column
+// blocks: expanded, groups of 32 take all 256 registers and groups of 16 spill).
+template <bool INPANEL, bool ASYM, bool RF, int GC>
 __global__ __launch_bounds__(256) void k_panel(double* __restrict__ Wq, int out, int in, int b0,
                                                const double* __restrict__ U, const int32_t* __restrict__ perm,
                                                double* __restrict__ scale_row, double* __restrict__ zero_row,
@@ -374,8 +379,8 @@ __global__ __launch_bounds__(256) void k_panel(double* __restrict__ Wq, int out,
   double dcur = rdiag[0], dnext = 0.0;
 #pragma unroll
   for (int m = 0; m < 8; ++m) ucur[m] = Us[c + 16 * m];
-#pragma unroll
-  for (int jm = 0; jm < 8; ++jm) {
+  // the 16 steps of column block jm
+  auto block_steps = [&](const int jm) __attribute__((always_inline)) {
     // steps past the panel edge (j >= pw) need no guard: there w = 0, U = 0 and 1/U = 0, so they
     // change nothing and their codes are never stored
     static_for<0, 16>([&](auto jlc) {
@@ -388,12 +393,14 @@ __global__ __launch_bounds__(256) void k_panel(double* __restrict__ Wq, int out,
         dnext = rdiag[j + 1];
       }
       {
-        if (INPANEL && (j % group) == 0) {
+        // a group opens at this step (with GC a constant once the steps are expanded)
+        const bool gstart = INPANEL && (GC > 0 ? (j % (GC > 0 ? GC : 1)) == 0 : (j % group) == 0);
+        if (gstart) {
           double hi = ASYM ? -INFINITY : 0.0, lo = INFINITY;
 #pragma unroll
           for (int m = 0; m < 8; ++m) {
             const int col = c + 16 * m;
-            const bool in_g = col >= j && col < j + group && col < pw;
+            const bool in_g = col >= j && col < j + (GC > 0 ? GC : group) && col < pw;
             hi = in_g ? (ASYM ? fmax(hi, w[m]) : fmax(hi, fabs(w[m]))) : hi;
             lo = in_g ? fmin(lo, w[m]) : lo;
           }
@@ -443,6 +450,12 @@ __global__ __launch_bounds__(256) void k_panel(double* __restrict__ Wq, int out,
         }
       }
     });
+  };
+  if constexpr (INPANEL && GC == 0) {
+#pragma unroll
+    for (int jm = 0; jm < 8; ++jm) block_steps(jm);
+  } else {
+    static_for<0, 8>([&](auto jmc) { block_steps(decltype(jmc)::value); });
   }
 
   double lsum = 0.0;
@@ -532,14 +545,16 @@ static hipError_t launch_panel(bool inpanel, dim3 grid, double* Wq, int out, int
                                int n_groups, int8_t* codes, float* scales, int32_t* zeros, double* errp,
                                int ld_err, double* row_loss, const double* T, int t_valid, hipStream_t stream) {
   const size_t lds = ((int)grid.x <= cu_count()) ? PANEL_SPREAD_LDS : 0;
-  if (inpanel)
-    k_panel<true, ASYM, RF><<<grid, dim3(256), lds, stream>>>(Wq, out, in, b0, U, perm, scale_row, zero_row, qmax,
-                                                              group, n_groups, codes, scales, zeros, errp, ld_err,
-                                                              row_loss, T, t_valid);
-  else
-    k_panel<false, ASYM, RF><<<grid, dim3(256), lds, stream>>>(Wq, out, in, b0, U, perm, scale_row, zero_row, qmax,
-                                                               group, n_groups, codes, scales, zeros, errp, ld_err,
-                                                               row_loss, T, t_valid);
+  auto go = [&](auto inp, auto gc) {
+    k_panel<decltype(inp)::value, ASYM, RF, decltype(gc)::value><<<grid, dim3(256), lds, stream>>>(
+        Wq, out, in, b0, U, perm, scale_row, zero_row, qmax, group, n_groups, codes, scales, zeros, errp, ld_err,
+        row_loss, T, t_valid);
+  };
+  using std::integral_constant;
+  if (!inpanel) go(integral_constant<bool, false>{}, integral_constant<int, 0>{});
+  else if (group == 128) go(integral_constant<bool, true>{}, integral_constant<int, 128>{});
+  else if (group == 64) go(integral_constant<bool, true>{}, integral_constant<int, 64>{});
+  else go(integral_constant<bool, true>{}, integral_constant<int, 0>{});
   return hipGetLastError();
 }
 
