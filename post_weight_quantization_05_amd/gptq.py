@@ -239,8 +239,8 @@ def factor_route(in_features: int, group: int | None) -> int:
     multiple of 64; group 0 or dividing 128) and it is the faster of the two on MI355X, i.e. with one grid per
     row (its panels fold T into their steps at almost no cost) or with in >= 8192 (where leaving out L^-1
     saves more in prepare than the in-panel T_P U_PP costs the loop); otherwise the route through U.
-    Measured per layer: q_proj (in 4096, group 0) 9.85 against 9.90 ms, down (in 11008, group 128) 51.1
-    against 60.9 ms, up_gate (in 4096, group 128) 15.1 against 14.7 ms."""
+    Measured per layer: q_proj (in 4096, group 0) 9.81 against 9.90 ms, down (in 11008, group 128) 48.2
+    against 58.2 ms, up_gate (in 4096, group 128) 13.30 against 13.34 ms (a tie: the route through U)."""
     group = int(group or 0)
     if in_features % 64 != 0 or (group != 0 and 128 % group != 0):
         return GPTQ_FACTOR_REVERSED
