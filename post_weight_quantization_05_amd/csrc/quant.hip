@@ -211,11 +211,12 @@ __global__ __launch_bounds__(256) void k_rowprep(const T* __restrict__ W, int64_
 // the earlier panels; the rows start from W0_P + T_P U_PP (with INPANEL formed first on the matrix cores,
 // otherwise folded into the steps), and D = W0 - Q is stored instead of the errors for the products that
 // follow.
-// GC: the group size when it is known at compile time (INPANEL with group 64 or 128); the column steps are
-// then expanded at compile time and only the steps that open a group carry the group's grid code, so the
-// kernel keeps the registers of the one-grid-per-row form (74 against 151). GC = 0: the group size comes
-// from `group` (one grid per row, or in-panel groups of 1 .. 32, whose steps stay a loop over the 16-column
-// blocks: expanded, groups of 32 take all 256 registers and groups of 16 spill).
+// GC: the group size when it is known at compile time (INPANEL with group 32, 64 or 128); the column steps
+// are then expanded at compile time and only the steps that open a group carry the group's grid code
+// (groups of 64 and 128 keep the 74 registers of the one-grid-per-row form, against 151; groups of 32 take
+// 256 without spilling, which two workgroups per CU still hold). GC = 0: the group size comes from `group`
+// (one grid per row, or in-panel groups of 1 .. 16, whose steps stay a loop over the 16-column blocks:
+// expanded, groups of 16 spill, faster at 4096 rows and slower at 11008).
 template <bool INPANEL, bool ASYM, bool RF, int GC>
 __global__ __launch_bounds__(256) void k_panel(double* __restrict__ Wq, int out, int in, int b0,
                                                const double* __restrict__ U, const int32_t* __restrict__ perm,
@@ -554,6 +555,7 @@ static hipError_t launch_panel(bool inpanel, dim3 grid, double* Wq, int out, int
   if (!inpanel) go(integral_constant<bool, false>{}, integral_constant<int, 0>{});
   else if (group == 128) go(integral_constant<bool, true>{}, integral_constant<int, 128>{});
   else if (group == 64) go(integral_constant<bool, true>{}, integral_constant<int, 64>{});
+  else if (group == 32) go(integral_constant<bool, true>{}, integral_constant<int, 32>{});
   else go(integral_constant<bool, true>{}, integral_constant<int, 0>{});
   return hipGetLastError();
 }
