@@ -236,47 +236,71 @@ __global__ __launch_bounds__(256) void k_panel(double* __restrict__ Wq, int out,
   const int c = tid & 15;
   const int r = blockIdx.x * 16 + (tid >> 4);
   const bool rok = r < out;
-  // the global loads that do not depend on the U block are issued first, so their latency overlaps its
-  // loads: the row's weights (16 lanes per row, lane c holding columns c + 16 m), RF: the row's T_P, and
-  // the pivot and permutation entry of column tid
-  double* wrow = Wq + (int64_t)(rok ? r : 0) * in;
-  double w[8];
+  // Every global load of the prologue is issued before the first wait: addresses are clamped into their
+  // operands and the values selected afterwards, so that no load sits behind a branch (with the loads
+  // guarded, the compiler kept each 16-row block's loads behind the previous block's LDS stores: eight
+  // round trips to memory instead of one). The row's weights (16 lanes per row, lane c holding columns
+  // c + 16 m), RF: the row's T_P, the pivot and permutation entry of column tid, then the U block.
+  const int64_t rbase = (int64_t)(rok ? r : 0) * in + b0;
+  double w[8], t[8];  // the raw loads first; the out-of-range ones are zeroed after the U block's loads
 #pragma unroll
   for (int m = 0; m < 8; ++m) {
     const int col = c + 16 * m;
-    w[m] = (rok && col < pw) ? wrow[b0 + col] : 0.0;
+    w[m] = Wq[rbase + (rok && col < pw ? col : 0)];
+    if constexpr (RF) t[m] = T[rbase + (t_valid && rok && col < pw ? col : 0)];
   }
-  double t[8];
-  if constexpr (RF) {
-    const double* trow = T + (int64_t)(rok ? r : 0) * in + b0;
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      const int col = c + 16 * m;
-      t[m] = (t_valid && rok && col < pw) ? trow[col] : 0.0;
-    }
-  }
+  // the row's grid from the row prep or the previous panel (one grid per row, or a group carried over)
+  const double s_row = scale_row[rok ? r : 0];
+  const double z_row = ASYM ? zero_row[rok ? r : 0] : 0.0;
   static_assert(PW <= 256, "one thread per panel column");
   const bool dcol = tid < pw;
-  const double udiag = dcol ? U[(int64_t)(b0 + tid) * in + b0 + tid] : 0.0;  // RF: R[j][j] = 1 / U[j][j]
-  const int pcol = dcol ? perm[b0 + tid] : 0;
-  // loaded one 16-row block at a time (block k: 16 rows of 128 - 16k stored columns, 8 - k elements per
-  // thread), all of a block's loads in flight before its stores
+  const int dc = dcol ? tid : 0;
+  const double udiag_x = U[(int64_t)(b0 + dc) * in + b0 + dc];  // RF: R[j][j] = 1 / U[j][j]
+  const int pcol_x = perm[b0 + dc];
+  const double udiag = dcol ? udiag_x : 0.0;
+  const int pcol = dcol ? pcol_x : 0;
+  // the U block, 16-row block k holding 16 rows of 128 - 16k stored columns (8 - k elements per thread):
+  // element (a, b) of the panel's U_PP, b >= a (RF: b > a, the diagonal comes below), read from
+  // U[b0 + a][b0 + b], or (RF) from the R form's reversed lower part at (b0 + pw - 1 - a, b0 + pw - 1 - b)
+  auto u_elem = [&](int k, int q, bool& valid) -> int64_t {
+    const int RL = PW - 16 * k;
+    const int i = tid + 256 * q;
+    const int a = 16 * k + i / RL, b = 16 * k + i % RL;
+    valid = a < pw && b < pw && (RF ? b > a : b >= a);
+    const int aa = valid ? a : 0, bb = valid ? b : 0;
+    return RF ? (int64_t)(b0 + pw - 1 - aa) * in + b0 + pw - 1 - bb : (int64_t)(b0 + aa) * in + b0 + bb;
+  };
+  double uv[36];  // 8 + 7 + ... + 1
   static_for<0, 8>([&](auto kc) {
     constexpr int k = decltype(kc)::value;
-    constexpr int RL = PW - 16 * k;  // stored length of the block's rows
-    constexpr int NE = RL / 16;      // elements per thread: 16 RL / 256
-    double v[NE];
+    constexpr int OFF = 8 * k - k * (k - 1) / 2;
 #pragma unroll
-    for (int q = 0; q < NE; ++q) {
-      const int i = tid + 256 * q;
-      const int a = 16 * k + i / RL, b = 16 * k + i % RL;
-      if (RF)  // U[a][b] = R form (b0 + pw - 1 - a, b0 + pw - 1 - b) for a < b (the diagonal comes below)
-        v[q] = (a < pw && b < pw && b > a) ? U[(int64_t)(b0 + pw - 1 - a) * in + b0 + pw - 1 - b] : 0.0;
-      else
-        v[q] = (a < pw && b < pw && b >= a) ? U[(int64_t)(b0 + a) * in + b0 + b] : 0.0;
+    for (int q = 0; q < 8 - k; ++q) {
+      bool valid;
+      uv[OFF + q] = U[u_elem(k, q, valid)];
     }
+  });
+  // empty uses here keep the compiler from sinking the loads above to their first real uses (past the
+  // barrier, or into the branch that stores the pivots), which cost a round trip each
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::"v"(udiag_x), "v"(pcol_x), "v"(s_row), "v"(z_row));
 #pragma unroll
-    for (int q = 0; q < NE; ++q) Us[urow(16 * k) + tid + 256 * q] = v[q];
+  for (int m = 0; m < 8; ++m) {
+    const int col = c + 16 * m;
+    w[m] = (rok && col < pw) ? w[m] : 0.0;
+    if constexpr (RF) t[m] = (t_valid && rok && col < pw) ? t[m] : 0.0;
+    asm volatile("" ::"v"(w[m]));
+    if constexpr (RF) asm volatile("" ::"v"(t[m]));
+  }
+  static_for<0, 8>([&](auto kc) {
+    constexpr int k = decltype(kc)::value;
+    constexpr int OFF = 8 * k - k * (k - 1) / 2;
+#pragma unroll
+    for (int q = 0; q < 8 - k; ++q) {
+      bool valid;
+      (void)u_elem(k, q, valid);
+      Us[urow(16 * k) + tid + 256 * q] = valid ? uv[OFF + q] : 0.0;
+    }
   });
   if (RF) __syncthreads();  // the block's stores above are done before the diagonal is written
   if (tid < PW) {
@@ -343,7 +367,7 @@ __global__ __launch_bounds__(256) void k_panel(double* __restrict__ Wq, int out,
       double hi = ASYM ? -INFINITY : 0.0, lo = INFINITY;
       if (rok)
         for (int col = c; col < glen; col += 16) {
-          const double v = wrow[b0 + col];
+          const double v = Wq[rbase + col];
           hi = ASYM ? fmax(hi, v) : fmax(hi, fabs(v));
           lo = fmin(lo, v);
         }
@@ -359,9 +383,9 @@ __global__ __launch_bounds__(256) void k_panel(double* __restrict__ Wq, int out,
         }
       }
     } else {
-      s = rok ? scale_row[r] : 1.0;
+      s = rok ? s_row : 1.0;
       sy = 1.0 / s;
-      if (ASYM) z = rok ? zero_row[r] : 0.0;
+      if (ASYM) z = rok ? z_row : 0.0;
     }
   }
 
