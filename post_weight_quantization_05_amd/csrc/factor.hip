@@ -115,22 +115,6 @@ __global__ __launch_bounds__(256) void k_gather(const double* __restrict__ S, co
   const int a0 = blockIdx.y * 64, b0 = blockIdx.x * 64;
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
   const double s2n = 2.0 / (double)n_total;
-  auto value = [&](int a, int b) {
-    double v = 0.0;
-    if (a < d && b < d && b <= a) {
-      const int x = reversed ? d - 1 - a : a;
-      const int y = reversed ? d - 1 - b : b;
-      const int pi = min(max(perm[x], 0), d - 1);
-      const int pj = min(max(perm[y], 0), d - 1);
-      if (pi == pj) {
-        v = diag_h[pi];
-      } else {
-        const int hi = max(pi, pj), lo = min(pi, pj);
-        v = s2n * S[(int64_t)hi * d + lo];
-      }
-    }
-    return v;
-  };
   if (b0 > a0) {  // strictly upper tile
     for (int aa = ty; aa < 64; aa += 4) {
       const int a = a0 + aa, b = b0 + tx;
@@ -138,11 +122,38 @@ __global__ __launch_bounds__(256) void k_gather(const double* __restrict__ S, co
     }
     return;
   }
-  if (reversed) {
-    // (a, b) reads S[d-1-b][d-1-a]: consecutive a are consecutive addresses
-    for (int bb = ty; bb < 64; bb += 4) t[bb][tx] = value(a0 + tx, b0 + bb);
-  } else {
-    for (int aa = ty; aa < 64; aa += 4) t[tx][aa] = value(a0 + aa, b0 + tx);
+  // the thread's 16 elements: (a0 + tx, b0 + ty + 4k) when reversed ((a, b) reads S[d-1-b][d-1-a], so
+  // consecutive a are consecutive addresses), else (a0 + ty + 4k, b0 + tx). Every load is issued before
+  // its values are needed (indices clamped into range, values selected afterwards): the permutation
+  // entries of all 16, then their S and diagonal entries, two round trips to memory instead of two per
+  // element.
+  constexpr int NE = 16;
+  int pi[NE], pj[NE];
+  bool ok[NE];
+#pragma unroll
+  for (int k = 0; k < NE; ++k) {
+    const int a = reversed ? a0 + tx : a0 + ty + 4 * k;
+    const int b = reversed ? b0 + ty + 4 * k : b0 + tx;
+    ok[k] = a < d && b < d && b <= a;
+    const int x = ok[k] ? (reversed ? d - 1 - a : a) : 0;
+    const int y = ok[k] ? (reversed ? d - 1 - b : b) : 0;
+    pi[k] = perm[x];
+    pj[k] = perm[y];
+  }
+  double sv[NE], dv[NE];
+#pragma unroll
+  for (int k = 0; k < NE; ++k) {
+    const int p = min(max(pi[k], 0), d - 1), q = min(max(pj[k], 0), d - 1);
+    pi[k] = p;
+    pj[k] = q;
+    sv[k] = S[(int64_t)max(p, q) * d + min(p, q)];
+    dv[k] = diag_h[p];
+  }
+#pragma unroll
+  for (int k = 0; k < NE; ++k) {
+    const double v = ok[k] ? (pi[k] == pj[k] ? dv[k] : s2n * sv[k]) : 0.0;
+    if (reversed) t[ty + 4 * k][tx] = v;
+    else t[tx][ty + 4 * k] = v;
   }
   __syncthreads();
   for (int aa = ty; aa < 64; aa += 4) {
