@@ -438,20 +438,30 @@ __global__ __launch_bounds__(256) void k_rform_diag(const double* __restrict__ L
   const int tid = threadIdx.x;
   double* out = M + (int64_t)b0 * d + b0;
   auto put = [&](int r, int c, double v) { out[(int64_t)r * d + c] = v; };
-  // the diagonal 64 x 64 inverses, strictly lower parts (the blocks are lower; zeros are staged above)
-  for (int e = tid; e < NB * NB; e += 256) {
-    const int r = e / NB, c = e % NB;
-    const double a = Dinv[(int64_t)kb * NB * NB + e];
-    if (r > c) put(r, c, a);
-    Ai[r][c] = (r >= c) ? a : 0.0;
-    if (pw == 128) {
-      const double cc = Dinv[(int64_t)(kb + 1) * NB * NB + e];
-      if (r > c) put(NB + r, NB + c, cc);
-      Ci[r][c] = (r >= c) ? cc : 0.0;
-      Bb[r][c] = L[(int64_t)(s + NB + r) * d + s + c];
+  // the diagonal 64 x 64 inverses, strictly lower parts (the blocks are lower; zeros are staged above).
+  // All of a thread's loads are issued first (the second block's with clamped addresses when pw < 128).
+  constexpr int NE = NB * NB / 256;
+  const bool two = pw == 128;
+  double av[NE], cv[NE], bv[NE];
+#pragma unroll
+  for (int q = 0; q < NE; ++q) {
+    const int e = tid + 256 * q, r = e / NB, c = e % NB;
+    av[q] = Dinv[(int64_t)kb * NB * NB + e];
+    cv[q] = Dinv[(int64_t)(two ? kb + 1 : kb) * NB * NB + e];
+    bv[q] = L[(int64_t)(two ? s + NB + r : s + r) * d + s + c];
+  }
+#pragma unroll
+  for (int q = 0; q < NE; ++q) {
+    const int e = tid + 256 * q, r = e / NB, c = e % NB;
+    if (r > c) put(r, c, av[q]);
+    Ai[r][c] = (r >= c) ? av[q] : 0.0;
+    if (two) {
+      if (r > c) put(NB + r, NB + c, cv[q]);
+      Ci[r][c] = (r >= c) ? cv[q] : 0.0;
+      Bb[r][c] = bv[q];
     }
   }
-  if (pw < 128) return;
+  if (!two) return;
   __syncthreads();
   // both 64 x 64 x 64 products on the matrix cores: wave wv forms the 16 rows 16 wv .. 16 wv + 15 of the
   // result in four 16 x 16 blocks (v_mfma_f64_16x16x4f64: lane l supplies the left operand's
