@@ -142,24 +142,25 @@ __global__ __launch_bounds__(256) void k_rowprep(const T* __restrict__ W, int64_
   double* q = Wq + (int64_t)r * in;
   double mx = ASYM ? -INFINITY : 0.0, mn = INFINITY;
   bool bad = false;  // a NaN or Inf among the row's live weights
-  // eight columns per thread per pass: the index loads, then the gathered loads, all in flight together
-  constexpr int U8 = 8;
-  for (int j0 = threadIdx.x; j0 < in; j0 += 256 * U8) {
-    int p[U8];
+  // sixteen columns per thread per pass (one pass at in = 4096): the index loads, then the gathered loads,
+  // all in flight together
+  constexpr int CPT = 16;
+  for (int j0 = threadIdx.x; j0 < in; j0 += 256 * CPT) {
+    int p[CPT];
 #pragma unroll
-    for (int u = 0; u < U8; ++u) {
+    for (int u = 0; u < CPT; ++u) {
       const int j = j0 + 256 * u;
       p[u] = (j < in) ? min(max(perm[j], 0), in - 1) : 0;
     }
-    double v[U8];
+    double v[CPT];
 #pragma unroll
-    for (int u = 0; u < U8; ++u) {
+    for (int u = 0; u < CPT; ++u) {
       const bool dd = dead[p[u]] != 0;
       const double x = to_f64<T>(wr[p[u]]);
       v[u] = dd ? 0.0 : x;
     }
 #pragma unroll
-    for (int u = 0; u < U8; ++u) {
+    for (int u = 0; u < CPT; ++u) {
       const int j = j0 + 256 * u;
       if (j < in) {
         q[j] = v[u];
