@@ -20,8 +20,8 @@ struct DgemmArgs {
   int64_t ldc, strideC;
   int M, N, K;
   double alpha, beta;
-  int tri_tiles;  // only tiles with I >= J (square C)
-  int tile_first; // tri_tiles: launch covers lower tiles tile_first, tile_first + 1, ... in tile order
+  int tri_tiles;  // only tiles with I >= J (square C): 1 counted in row order, 2 in column order
+  int tile_first; // tri_tiles: launch covers lower tiles tile_first, tile_first + 1, ... in that order
   int lower_only; // rectangular C whose origin lies on a diagonal: tiles with I < J are skipped
   int kmode;
   int m_lim, m_step;  // when m_step != 0: rows of batch b = min(M, m_lim - b * m_step)
@@ -61,9 +61,9 @@ int inv_fill_tiles(const InvFill& f);
 // One block-column step of the blocked Cholesky factorization (see k_colstep in dgemm.hip): C -= A B^T
 // on the lower tiles of the M x N region C, the diagonal block at its origin factored and inverted, and
 // the column-0 tiles below it solved against that factor; K is 0, 64 or 256. The same launch also
-// computes lower tiles
-// x_first .. x_first + x_count - 1 (in tile order) of x, an independent A B^T update of a square region
-// (x may be null when x_count is 0), and, when f is not null, the tiles of launch f->k of the inverse.
+// computes lower tiles x_first .. x_first + x_count - 1 (in column order if x->tri_tiles is 2, else in
+// row order) of x, an independent A B^T update of a square region (x may be null when x_count is 0),
+// and, when f is not null, the tiles of launch f->k of the inverse.
 hipError_t colstep_launch(const DgemmArgs& a, const DgemmArgs* x, int x_first, int x_count, const InvFill* f,
                           hipStream_t stream);
 // The inverse's tiles of a launch after the last step (f.k = S, S + 1, S + 2).

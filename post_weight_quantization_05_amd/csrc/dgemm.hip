@@ -165,6 +165,19 @@ __device__ __forceinline__ void tile_product(const DgemmArgs& a, const double* A
   }
 }
 
+// Tile t of the lower triangle of an nt x nt tile grid: in row order (row I holds t = I(I+1)/2 ..
+// I(I+1)/2 + I), or in column order (column J from row J down, then column J + 1), which is row order
+// on the grid turned half a revolution.
+__device__ __forceinline__ void tri_tile(int t, int nt, bool col_order, int& I, int& J) {
+  const int s = col_order ? nt * (nt + 1) / 2 - 1 - t : t;
+  int R = (int)((sqrt(8.0 * (double)s + 1.0) - 1.0) * 0.5);
+  while ((R + 1) * (R + 2) / 2 <= s) ++R;
+  while (R * (R + 1) / 2 > s) --R;
+  const int C = s - R * (R + 1) / 2;
+  I = col_order ? nt - 1 - C : R;
+  J = col_order ? nt - 1 - R : C;
+}
+
 // T x T tile of C = alpha opA(A) opB(B) + beta C (see the file comment for the options).
 template <bool TA, bool TB, int T>
 __global__ __launch_bounds__(256) void k_dgemm(DgemmArgs a) {
@@ -175,12 +188,7 @@ __global__ __launch_bounds__(256) void k_dgemm(DgemmArgs a) {
   const int batch = blockIdx.y;
   int I, J;
   if (a.tri_tiles) {
-    const int t = blockIdx.x + a.tile_first;
-    int I0 = (int)((sqrt(8.0 * (double)t + 1.0) - 1.0) * 0.5);
-    while ((I0 + 1) * (I0 + 2) / 2 <= t) ++I0;
-    while (I0 * (I0 + 1) / 2 > t) --I0;
-    I = I0;
-    J = t - I0 * (I0 + 1) / 2;
+    tri_tile((int)blockIdx.x + a.tile_first, (a.M + T - 1) / T, a.tri_tiles == 2, I, J);
   } else {
     const int ntn = (a.N + T - 1) / T;
     I = blockIdx.x / ntn;
@@ -545,13 +553,14 @@ __global__ __launch_bounds__(256, 2) void k_colstep(DgemmArgs a, DgemmArgs xa, i
     return;
   }
   if ((int)blockIdx.x >= n_own) {
-    // a tile of the deferred trailing update xa (lower tiles of a square region, in tile order from
-    // x_first): independent of this step's own work, it fills CUs the step leaves idle
+    // a tile of the deferred trailing update xa (lower tiles of a square region from x_first, in column
+    // order if xa.tri_tiles is 2, else in row order): independent of this step's own work, it fills CUs
+    // the step leaves idle
     const int t = x_first + ((int)blockIdx.x - n_own);
-    int XI = (int)((sqrt(8.0 * (double)t + 1.0) - 1.0) * 0.5);
-    while ((XI + 1) * (XI + 2) / 2 <= t) ++XI;
-    while (XI * (XI + 1) / 2 > t) --XI;
-    const int XJ = t - XI * (XI + 1) / 2;
+    const int xnt = (xa.M + T - 1) / T;
+    if (t >= xnt * (xnt + 1) / 2) return;
+    int XI, XJ;
+    tri_tile(t, xnt, xa.tri_tiles == 2, XI, XJ);
     const int xi0 = XI * T, xj0 = XJ * T;
     if (xi0 >= xa.M || xj0 >= xa.N) return;
     f64x4 xacc[T / 32][T / 32];

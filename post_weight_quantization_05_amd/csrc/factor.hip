@@ -234,9 +234,13 @@ __global__ __launch_bounds__(256) void k_reverse_to_upper(const double* __restri
 // panel's update (K = 64), the next diagonal block is factored and inverted, and the next panel is
 // solved against it. The outer block's whole panel (K = NBO) updates the trailing matrix: the next outer
 // block's columns in that block's first step launch (its own tiles, before its diagonal block is
-// factored), the rest as deferred tiles inside the next outer block's steps. The factors of the diagonal
-// blocks are staged in Lst and copied into A at the end (A's diagonal block is read by several workgroups
-// of the launch that factors it).
+// factored), the rest as deferred tiles inside the next outer block's steps. Near the end of the matrix
+// (GPTQ_FACTOR_LOOKAHEAD_ROWS) an outer block's steps also update the next block's columns with each
+// panel once it is solved, so that block's first step takes only the last 64 columns of the panel
+// before it (K = 64); those steps run only after the deferred tiles of the same columns are done (they
+// come first in column order and all go to the first step). The factors of the diagonal blocks are
+// staged in Lst and copied into A at the end (A's diagonal block is read by several workgroups of the
+// launch that factors it).
 #ifndef GPTQ_FACTOR_NBO
 #define GPTQ_FACTOR_NBO 256
 #endif
@@ -259,6 +263,16 @@ static_assert(NBO == 256, "an outer block's panel is the K of its successor's fi
 #ifndef GPTQ_FACTOR_DEFER_FILL
 #define GPTQ_FACTOR_DEFER_FILL 640
 #endif
+// An outer block's steps also update the next outer block's columns (one 64-column panel per step, so
+// that block's first step takes K = 64 instead of the whole panel before it) once at most this many
+// rows lie below the next block's start: there the steps are bound by their chain of diagonal blocks
+// and the extra K = 64 tiles fill idle CUs, while higher up the steps are bound by their tiles, which
+// then read and write the next block's columns four times instead of once.
+// Prepare (ms) at in = 4096 / 8192 / 11008, R form: 2.353 / 8.92 / 18.04 with 2048, 2.350 / 8.92 / 18.06
+// with 3072, 2.358 / 9.25 / 18.45 with every block looking ahead, 2.449 / 9.02 / 18.06 with none.
+#ifndef GPTQ_FACTOR_LOOKAHEAD_ROWS
+#define GPTQ_FACTOR_LOOKAHEAD_ROWS 2048
+#endif
 
 // place_l: copy the diagonal blocks' factors into A at the end.
 // Z, G (both null, or Z d x d and G two buffers of 64 rows per block x 64): also form Z = L^-1 (lower part)
@@ -275,10 +289,14 @@ hipError_t potrf_lower(double* A, int d, double* Dinv, double* Lst, unsigned* st
   inv.d = d;
   inv.S = S;
   const int defer_per_step = defer >= 0 ? defer : Z ? GPTQ_FACTOR_DEFER_FILL : GPTQ_FACTOR_DEFER;
-  // The trailing update of an outer block is split in two: the next outer block's columns right away
-  // (its first step needs them), the rest (columns from the block after that on) deferred and spread over
-  // the next outer block's steps as extra workgroups. Per tile the arithmetic is unchanged.
-  DgemmArgs pend{};  // deferred part of the previous outer block's trailing update
+  // The trailing update of an outer block is split in two: the next outer block's columns in that block's
+  // first step (or panel by panel in this block's steps, near the end), the rest (columns from the block
+  // after that on) as one K = NBO product deferred and spread over the next outer block's steps as extra
+  // workgroups.
+  // deferred part of the previous outer block's trailing update: its tiles in column order (tri_tiles = 2)
+  // when the block that takes them looks ahead, else in row order (faster there: 18.06 against 18.20 ms
+  // for the R form's prepare at in = 11008)
+  DgemmArgs pend{};
   int pend_tiles = 0, pend_done = 0;
   // one block-column step: update C = A[c1:, c1:c1 + n] with the panel A[c1:, o:o + k] (k = 0: no
   // update), factor the diagonal block at (c1, c1), solve the panel below it; plus `share` deferred tiles
@@ -299,8 +317,11 @@ hipError_t potrf_lower(double* A, int d, double* Dinv, double* Lst, unsigned* st
     return e;
   };
   hipError_t e;
+  bool prev_look = false;
   for (int b0 = 0; b0 < d; b0 += NBO) {
     const int b1 = min(d, b0 + NBO);
+    const int b2 = min(d, b1 + NBO);  // end of the next outer block's columns
+    const bool look = b1 < d && d - b1 <= GPTQ_FACTOR_LOOKAHEAD_ROWS;  // steps update [b1, b2) too
     const int steps = (b1 - b0 + NB - 1) / NB;
     // the deferred tiles are shared out evenly over this outer block's steps (all of them by its end)
     int step = 0;
@@ -308,22 +329,32 @@ hipError_t potrf_lower(double* A, int d, double* Dinv, double* Lst, unsigned* st
       const int left = pend_tiles - pend_done, rem = steps - step++;
       return (left + rem - 1) / rem;
     };
-    // first block of the outer block column: the update of the whole outer block by the previous outer
-    // panel (K = NBO; none for the first outer block), its diagonal block and its panel
+    // with look, the deferred tiles of the next outer block's columns (the first tile columns in column
+    // order) all go to the first step, since the steps after it update those columns themselves
+    const int pend_nt = (pend.M + NB - 1) / NB, strip_cols = min(pend_nt, NBO / NB);
+    const int strip = look && pend_tiles > 0
+                          ? min(pend_tiles, strip_cols * pend_nt - strip_cols * (strip_cols - 1) / 2) : 0;
+    // first block of the outer block column: the update of the whole outer block by the last panel of
+    // the previous one (by the whole previous panel, K = NBO, if the previous block's steps did not look
+    // ahead; none for the first outer block), its diagonal block and its panel
     if (b0 == 0) e = colstep(b0, min(NB, d - b0), b0, 0, share());
-    else e = colstep(b0, b1 - b0, b0 - NBO, NBO, share());
+    else if (prev_look) e = colstep(b0, b1 - b0, b0 - NB, NB, max(share(), strip));
+    else e = colstep(b0, b1 - b0, b0 - NBO, NBO, max(share(), strip));
     if (e != hipSuccess) return e;
+    const int cend = look ? b2 : b1;
     for (int o = b0; o + NB < b1; o += NB) {
-      // the outer block's remaining columns get panel o; the next block is factored and its panel solved
+      // the outer block's remaining columns (and with look the next block's) get panel o; the next block
+      // is factored and its panel solved
       const int c1 = o + NB;
-      e = colstep(c1, b1 - c1, o, NB, share());
+      e = colstep(c1, cend - c1, o, NB, share());
       if (e != hipSuccess) return e;
     }
+    prev_look = look;
     pend_tiles = pend_done = 0;
+    pend = DgemmArgs{};
     if (b1 < d) {
       // trailing update with the whole outer panel Q = A[b1:, b0:b1]: A22 -= Q Q^T (lower part). The next
-      // outer block's columns get it in that block's first step launch; the rest is deferred.
-      const int b2 = min(d, b1 + NBO);
+      // outer block's columns have it by the end of that block's first step; the rest is deferred.
       if (b2 < d) {  // the rest, deferred
         pend = DgemmArgs{};
         const double* Q2 = A + (int64_t)b2 * d + b0;
@@ -333,6 +364,7 @@ hipError_t potrf_lower(double* A, int d, double* Dinv, double* Lst, unsigned* st
         pend.M = d - b2; pend.N = d - b2; pend.K = b1 - b0;
         pend.alpha = -1.0; pend.beta = 1.0;
         pend.kmode = KMODE_FULL;
+        pend.tri_tiles = d - b2 <= GPTQ_FACTOR_LOOKAHEAD_ROWS ? 2 : 1;  // the look of the block [b1, b2)
         const int nt = (pend.M + NB - 1) / NB;
         const int all = nt * (nt + 1) / 2;
         // the next outer block's steps take as many as they can hide (about one tile per CU that a
@@ -341,7 +373,6 @@ hipError_t potrf_lower(double* A, int d, double* Dinv, double* Lst, unsigned* st
         pend_tiles = min(all, next_steps * defer_per_step);
         if (pend_tiles < all) {
           DgemmArgs r = pend;
-          r.tri_tiles = 1;
           r.tile_first = pend_tiles;
           e = dgemm_launch(r, false, true, 1, stream);
           if (e != hipSuccess) return e;
