@@ -180,8 +180,9 @@ def test_prepare_matches_oracle(cfg, act, flags):
 
 
 # sizes around the 64-column steps, the 256-column outer blocks, and the first size whose trailing
-# updates are partly deferred into later steps (more than two outer blocks)
-@pytest.mark.parametrize("d", [1, 2, 63, 64, 65, 129, 255, 257, 320, 513, 577, 1000])
+# updates are partly deferred into later steps (more than two outer blocks); at 2500 the outer blocks from
+# the second on also update the next outer block's columns (at most 2048 rows below it), the first does not
+@pytest.mark.parametrize("d", [1, 2, 63, 64, 65, 129, 255, 257, 320, 513, 577, 1000, 2500])
 def test_prepare_small_and_edge_sizes(d):
     rng = np.random.default_rng(d)
     X = rng.standard_normal((3 * d + 2, d)) @ (np.eye(d) + 0.2 * rng.standard_normal((d, d)))

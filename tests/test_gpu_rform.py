@@ -62,7 +62,9 @@ def test_prepare_r_form_matches_oracle(cfg, act):
     _check_form(Mg.cpu().numpy(), M)
 
 
-@pytest.mark.parametrize("d", [64, 128, 192, 576, 1024, 1088])
+# 2560 and 3136: the outer blocks switch partway to updating the next outer block's columns in their own
+# steps (at most 2048 rows below it); 3136 ends on a 64-column outer block
+@pytest.mark.parametrize("d", [64, 128, 192, 576, 1024, 1088, 2560, 3136])
 def test_prepare_r_form_sizes(d):
     rng = np.random.default_rng(900 + d)
     X = rng.standard_normal((3 * d + 2, d)) @ (np.eye(d) + 0.2 * rng.standard_normal((d, d)))
